@@ -1,0 +1,436 @@
+/*
+ * pa_oracle.c -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+ *
+ * A plain, slow, obviously-correct CPU statement, in float64, of what the paged-attention hot path
+ * computes. Only the tests, the smoke check and the CPU-baseline leg of the benchmark may load it.
+ * It shares no code, header, table or helper with the HIP library; the two agree only on the
+ * interface facts (argument meaning and the cache layout below), each written out independently.
+ *
+ * Sources (a reader has the pages, so each function names the passage it follows):
+ *   [MEM]  openeuler.csdn.net, "高并发 AI 服务的内存瓶颈" (memory bottleneck of high-concurrency
+ *          AI serving): sections "vLLM - PagedAttention" (机制1 按需分配, 机制 2 写时复制) and
+ *          "PagedAttention 在 vLLM 中的实现细节" (Block Table 数据结构; Attention 计算时的 Block 映射).
+ *   [PD]   lilinji.mintlify.site lecture 32, "LLM 在线推理两阶段（Prefill vs Decode）…":
+ *          §1.1 (causal factorisation), §3.1 (attention formula; decode appends k_t, v_t then
+ *          attends K_{1:t}, V_{1:t}), §3.4 (GQA grouping figure), §5.4 (chunked prefill).
+ *   [OV]   devpress.csdn.net/amd vLLM overview: §3 PagedAttention (3) pseudo-code (per-block
+ *          accumulation over the block table), §9 FlashAttention (4) online softmax (running max
+ *          and running sum of exponentials, rescaled at the end).
+ *
+ * Cache layout (an interface fact, fixed by the library's header, restated here on its own):
+ *   k_cache, v_cache: 16-bit words, [num_blocks][num_kv_heads][16][head_dim].
+ *   The token in slot s lives in physical block s/16 at in-block offset s%16 ([MEM] Block Table
+ *   数据结构: position -> physical_block*block_size + offset). The pages leave the arrangement of
+ *   heads inside a block open; this layout keeps each (block, kv-head) tile contiguous.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   - seq_lens counts the token being decoded, so the decode query attends positions 0..L-1
+ *     inclusive of itself ([PD] §3.1).
+ *   - a prefill row at absolute position p attends keys 0..p inclusive ([PD] §1.1 causal law).
+ *   - query head h reads kv head h / (H_q/H_kv): contiguous groups ([PD] §3.4 figure).
+ *   - L = 0 gives a zero output row; slot < 0 means "skip this token"; copy_blocks copies the
+ *     whole 16-slot block in both caches.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F16 = 0, OR_BF16 = 1 };
+enum { OR_OK = 0, OR_BAD_INDEX = 1, OR_DUP_SLOT = 2, OR_BAD_MAPPING = 3, OR_BAD_ARG = 4,
+       OR_NO_MEM = 5 };
+
+#define OR_BLOCK 16
+
+/* ---------------------------------------------------------------- O1: 16-bit -> float64 */
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. bfloat16: the top 16 bits of an
+ * IEEE binary32. Both decode exactly into a double. */
+double oracle_to_double(uint16_t bits, int dtype)
+{
+    if (dtype == OR_BF16) {
+        uint32_t u = (uint32_t)bits << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1f;
+    int m = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static size_t cache_at(int blk, int kvh, int off, int d, int H_kv, int D)
+{
+    return (((size_t)blk * H_kv + kvh) * OR_BLOCK + off) * D + d;
+}
+
+/* ---------------------------------------------------------------- O2: scatter ([PD] §3.1; [MEM])
+ * For every token t with slot_mapping[t] >= 0, copy its H_kv*D key and value words into slot
+ * slot_mapping[t]. A bit copy: no arithmetic on the values. Slots in one call must be distinct and
+ * inside the pool, else nothing is written and an error is returned. */
+int oracle_reshape_and_cache(const uint16_t *key, const uint16_t *value, uint16_t *k_cache,
+                             uint16_t *v_cache, const int32_t *slot_mapping, int T,
+                             int num_blocks, int H_kv, int D)
+{
+    if (T < 0 || num_blocks < 0 || H_kv <= 0 || D <= 0)
+        return OR_BAD_ARG;
+    for (int t = 0; t < T; ++t) {
+        int32_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        if ((int64_t)s >= (int64_t)num_blocks * OR_BLOCK)
+            return OR_BAD_INDEX;
+        for (int u = 0; u < t; ++u)
+            if (slot_mapping[u] == s)
+                return OR_DUP_SLOT;
+    }
+    for (int t = 0; t < T; ++t) {
+        int32_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        int blk = s / OR_BLOCK, off = s % OR_BLOCK;
+        for (int g = 0; g < H_kv; ++g)
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)t * H_kv + g) * D + d;
+                k_cache[cache_at(blk, g, off, d, H_kv, D)] = key[src];
+                v_cache[cache_at(blk, g, off, d, H_kv, D)] = value[src];
+            }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- O3: copy-on-write ([MEM] 机制 2)
+ * For each (src, dst) pair copy the whole physical block -- all 16 slots, all kv heads -- in both
+ * caches. Destinations must be distinct and no destination may also be a source, so the result does
+ * not depend on the order of the pairs. */
+int oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int32_t *mapping, int n,
+                       int num_blocks, int H_kv, int D)
+{
+    if (n < 0 || num_blocks < 0 || H_kv <= 0 || D <= 0)
+        return OR_BAD_ARG;
+    for (int i = 0; i < n; ++i) {
+        int32_t s = mapping[2 * i], d = mapping[2 * i + 1];
+        if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+            return OR_BAD_INDEX;
+        for (int j = 0; j < n; ++j) {
+            if (j != i && mapping[2 * j + 1] == d)
+                return OR_BAD_MAPPING;
+            if (mapping[2 * j] == d)
+                return OR_BAD_MAPPING;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        int32_t s = mapping[2 * i], d = mapping[2 * i + 1];
+        for (int g = 0; g < H_kv; ++g)
+            for (int off = 0; off < OR_BLOCK; ++off)
+                for (int e = 0; e < D; ++e) {
+                    k_cache[cache_at(d, g, off, e, H_kv, D)] = k_cache[cache_at(s, g, off, e, H_kv, D)];
+                    v_cache[cache_at(d, g, off, e, H_kv, D)] = v_cache[cache_at(s, g, off, e, H_kv, D)];
+                }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- O4: gather ([MEM] Block 映射)
+ * Rebuild the logically contiguous rows 0..L-1 of kv head `kvh` of one sequence: position i sits in
+ * logical block i/16 at offset i%16, and the table maps the logical block to a physical one. */
+int oracle_gather(const uint16_t *cache, const int32_t *table_row, int L, int kvh, int num_blocks,
+                  int H_kv, int D, int dtype, double *out)
+{
+    for (int i = 0; i < L; ++i) {
+        int32_t blk = table_row[i / OR_BLOCK];
+        if (blk < 0 || blk >= num_blocks)
+            return OR_BAD_INDEX;
+        for (int d = 0; d < D; ++d)
+            out[(size_t)i * D + d] = oracle_to_double(cache[cache_at(blk, kvh, i % OR_BLOCK, d, H_kv, D)], dtype);
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- O5: attention ([PD] §3.1)
+ * out = softmax(scale * q K^T) V over the L rows of K and V, written out as its definition in two
+ * passes: scores, their maximum, the exponentials, their sum, the weighted sum of rows. The maximum
+ * is subtracted only to keep exp() finite; it cancels exactly in the ratio. L = 0 gives zeros. */
+int oracle_attention(const double *q, const double *K, const double *V, int L, int D,
+                     double scale, double *out)
+{
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (L <= 0)
+        return OR_OK;
+    double *w = (double *)malloc(sizeof(double) * (size_t)L);
+    if (!w)
+        return OR_NO_MEM;
+    double m = -INFINITY;
+    for (int j = 0; j < L; ++j) {
+        double s = 0.0;
+        for (int d = 0; d < D; ++d)
+            s += q[d] * K[(size_t)j * D + d];
+        w[j] = scale * s;
+        if (w[j] > m)
+            m = w[j];
+    }
+    double Z = 0.0;
+    for (int j = 0; j < L; ++j) {
+        w[j] = exp(w[j] - m);
+        Z += w[j];
+    }
+    for (int j = 0; j < L; ++j)
+        for (int d = 0; d < D; ++d)
+            out[d] += w[j] * V[(size_t)j * D + d];
+    for (int d = 0; d < D; ++d)
+        out[d] /= Z;
+    free(w);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- O6: paged decode
+ * For sequence s and query head h: gather rows 0..seq_lens[s]-1 of kv head h/(H_q/H_kv) through the
+ * block table ([MEM] Block 映射, [PD] §3.4) and apply O5 to query row q[s][h] ([PD] §3.1).
+ * `pairs` lists the (s, h) pairs to evaluate ([n_pairs][2]); NULL means every pair in order.
+ * out is [n_pairs][D] (or [B][H_q][D] when pairs is NULL). */
+int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *block_tables, int max_blocks, const int32_t *seq_lens, int B,
+                  int H_q, int H_kv, int D, int num_blocks, int dtype, double scale,
+                  const int32_t *pairs, int n_pairs, int nthreads, double *out)
+{
+    if (B < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
+        return OR_BAD_ARG;
+    int n = pairs ? n_pairs : B * H_q;
+    int group = H_q / H_kv;
+    int status = OR_OK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int i = 0; i < n; ++i) {
+        int s = pairs ? pairs[2 * i] : i / H_q;
+        int h = pairs ? pairs[2 * i + 1] : i % H_q;
+        int rc = OR_OK;
+        if (s < 0 || s >= B || h < 0 || h >= H_q) {
+            rc = OR_BAD_ARG;
+        } else {
+            int L = seq_lens[s];
+            if (L < 0 || L > max_blocks * OR_BLOCK) {
+                rc = OR_BAD_INDEX;
+            } else {
+                double *K = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
+                double *V = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
+                double *q = (double *)malloc(sizeof(double) * (size_t)D);
+                if (!K || !V || !q) {
+                    rc = OR_NO_MEM;
+                } else {
+                    const int32_t *row = block_tables + (size_t)s * max_blocks;
+                    rc = oracle_gather(k_cache, row, L, h / group, num_blocks, H_kv, D, dtype, K);
+                    if (rc == OR_OK)
+                        rc = oracle_gather(v_cache, row, L, h / group, num_blocks, H_kv, D, dtype, V);
+                    for (int d = 0; d < D; ++d)
+                        q[d] = oracle_to_double(query[((size_t)s * H_q + h) * D + d], dtype);
+                    if (rc == OR_OK)
+                        rc = oracle_attention(q, K, V, L, D, scale, out + (size_t)i * D);
+                }
+                free(K);
+                free(V);
+                free(q);
+            }
+        }
+        if (rc != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/* ---------------------------------------------------------------- O7: paged causal prefill chunk
+ * Sequence s owns query rows cu_q_lens[s] .. cu_q_lens[s+1]-1: the last q_len tokens of its
+ * seq_lens[s] tokens ([PD] §5.4: a chunk attends the cached context plus the earlier part of
+ * itself). Row i of the chunk sits at absolute position p = seq_lens[s] - q_len + i and attends
+ * keys 0..p ([PD] §1.1). `rows` lists (row, head) pairs ([n_rows][2]); NULL means every
+ * (row, head) in order. out is [n_rows][D] (or [total_q][H_q][D]). */
+int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
+                   const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                   const int32_t *cu_q_lens, int S, int H_q, int H_kv, int D, int num_blocks,
+                   int dtype, double scale, const int32_t *rows, int n_rows, int nthreads,
+                   double *out)
+{
+    if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
+        return OR_BAD_ARG;
+    int total_q = cu_q_lens[S];
+    int n = rows ? n_rows : total_q * H_q;
+    int group = H_q / H_kv;
+    int status = OR_OK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int i = 0; i < n; ++i) {
+        int r = rows ? rows[2 * i] : i / H_q;
+        int h = rows ? rows[2 * i + 1] : i % H_q;
+        int rc = OR_OK;
+        int s = -1;
+        for (int j = 0; j < S; ++j)
+            if (cu_q_lens[j] <= r && r < cu_q_lens[j + 1])
+                s = j;
+        if (s < 0 || h < 0 || h >= H_q) {
+            rc = OR_BAD_ARG;
+        } else {
+            int q_len = cu_q_lens[s + 1] - cu_q_lens[s];
+            int p = seq_lens[s] - q_len + (r - cu_q_lens[s]);
+            if (p < 0 || seq_lens[s] > max_blocks * OR_BLOCK) {
+                rc = OR_BAD_INDEX;
+            } else {
+                int L = p + 1;
+                double *K = (double *)malloc(sizeof(double) * (size_t)L * D);
+                double *V = (double *)malloc(sizeof(double) * (size_t)L * D);
+                double *q = (double *)malloc(sizeof(double) * (size_t)D);
+                if (!K || !V || !q) {
+                    rc = OR_NO_MEM;
+                } else {
+                    const int32_t *row = block_tables + (size_t)s * max_blocks;
+                    rc = oracle_gather(k_cache, row, L, h / group, num_blocks, H_kv, D, dtype, K);
+                    if (rc == OR_OK)
+                        rc = oracle_gather(v_cache, row, L, h / group, num_blocks, H_kv, D, dtype, V);
+                    for (int d = 0; d < D; ++d)
+                        q[d] = oracle_to_double(query[((size_t)r * H_q + h) * D + d], dtype);
+                    if (rc == OR_OK)
+                        rc = oracle_attention(q, K, V, L, D, scale, out + (size_t)i * D);
+                }
+                free(K);
+                free(V);
+                free(q);
+            }
+        }
+        if (rc != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/* ---------------------------------------------------------------- O8: split-and-merge ([OV] §9 (4))
+ * Cut the L rows into consecutive parts of `part` rows. Each part keeps its own running maximum m_p,
+ * its sum of exponentials Z_p = sum exp(s_j - m_p) and its normalised output o_p; the parts are then
+ * combined by rescaling every part to the global maximum M:
+ *   out = sum_p exp(m_p - M) Z_p o_p / sum_p exp(m_p - M) Z_p.
+ * This is the merge the split-K decode uses; it equals O5 up to rounding. */
+int oracle_split_merge(const double *q, const double *K, const double *V, int L, int D,
+                       double scale, int part, double *out)
+{
+    if (part <= 0 || L < 0 || D <= 0)
+        return OR_BAD_ARG;
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (L == 0)
+        return OR_OK;
+    int np = (L + part - 1) / part;
+    double *m = (double *)malloc(sizeof(double) * np);
+    double *Z = (double *)malloc(sizeof(double) * np);
+    double *o = (double *)malloc(sizeof(double) * (size_t)np * D);
+    double *w = (double *)malloc(sizeof(double) * part);
+    if (!m || !Z || !o || !w) {
+        free(m); free(Z); free(o); free(w);
+        return OR_NO_MEM;
+    }
+    for (int p = 0; p < np; ++p) {
+        int a = p * part, b = a + part < L ? a + part : L;
+        m[p] = -INFINITY;
+        for (int j = a; j < b; ++j) {
+            double s = 0.0;
+            for (int d = 0; d < D; ++d)
+                s += q[d] * K[(size_t)j * D + d];
+            w[j - a] = scale * s;
+            if (w[j - a] > m[p])
+                m[p] = w[j - a];
+        }
+        Z[p] = 0.0;
+        for (int d = 0; d < D; ++d)
+            o[(size_t)p * D + d] = 0.0;
+        for (int j = a; j < b; ++j) {
+            double e = exp(w[j - a] - m[p]);
+            Z[p] += e;
+            for (int d = 0; d < D; ++d)
+                o[(size_t)p * D + d] += e * V[(size_t)j * D + d];
+        }
+        for (int d = 0; d < D; ++d)
+            o[(size_t)p * D + d] /= Z[p];
+    }
+    double M = -INFINITY;
+    for (int p = 0; p < np; ++p)
+        if (m[p] > M)
+            M = m[p];
+    double W = 0.0;
+    for (int p = 0; p < np; ++p) {
+        double wp = exp(m[p] - M) * Z[p];
+        W += wp;
+        for (int d = 0; d < D; ++d)
+            out[d] += wp * o[(size_t)p * D + d];
+    }
+    for (int d = 0; d < D; ++d)
+        out[d] /= W;
+    free(m); free(Z); free(o); free(w);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- test helper: poison free slots
+ * Overwrite every slot of both caches that holds no valid token -- no sequence s has a position
+ * i < seq_lens[s] mapped to it by its table -- with the 16-bit word `pattern` (a NaN code for the
+ * caller's dtype). Attention must never read such a slot, so a kernel that does turns a finite
+ * result into NaN. Returns the number of poisoned slots, or -1 on a bad table entry. */
+long oracle_poison_free_slots(uint16_t *k_cache, uint16_t *v_cache, const int32_t *block_tables,
+                              int max_blocks, const int32_t *seq_lens, int S, int num_blocks,
+                              int H_kv, int D, uint16_t pattern)
+{
+    unsigned char *used = (unsigned char *)calloc((size_t)num_blocks * OR_BLOCK, 1);
+    if (!used)
+        return -1;
+    for (int s = 0; s < S; ++s)
+        for (int i = 0; i < seq_lens[s]; ++i) {
+            int32_t blk = block_tables[(size_t)s * max_blocks + i / OR_BLOCK];
+            if (blk < 0 || blk >= num_blocks) {
+                free(used);
+                return -1;
+            }
+            used[(size_t)blk * OR_BLOCK + i % OR_BLOCK] = 1;
+        }
+    long count = 0;
+    for (int blk = 0; blk < num_blocks; ++blk)
+        for (int off = 0; off < OR_BLOCK; ++off) {
+            if (used[(size_t)blk * OR_BLOCK + off])
+                continue;
+            ++count;
+            for (int g = 0; g < H_kv; ++g)
+                for (int d = 0; d < D; ++d) {
+                    k_cache[cache_at(blk, g, off, d, H_kv, D)] = pattern;
+                    v_cache[cache_at(blk, g, off, d, H_kv, D)] = pattern;
+                }
+        }
+    free(used);
+    return count;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

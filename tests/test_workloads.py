@@ -1,0 +1,126 @@
+"""Host-side input construction: block accounting and reference counts (CPU only).
+
+Pins the block-manager bookkeeping in pa_workloads to the pages' worked examples and to the
+invariants the method fixes: ceil(L/16) blocks per sequence, one reference per table that holds a
+block, copy-on-write only where samples diverge, and the token-budget split of a mixed step.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import pa_workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def examples():
+    with open(os.path.join(GOLDEN, "page_worked_examples.json")) as f:
+        return json.load(f)
+
+
+def test_page_on_demand_allocation_example():
+    g = examples()["on_demand_allocation"]
+    assert W.blocks_needed(g["tokens"]) == g["blocks"]
+    assert W.blocks_needed(g["tokens"]) * W.BLOCK == g["slots"]
+    w = W.build([g["tokens"]], 1, 1, 64, "f16", seed=1)
+    assert (w.block_tables[0] >= 0).sum() == g["blocks"]
+    # the new (100th) token lands in the 7th block at offset 3
+    assert w.slot_mapping[0] == w.block_tables[0, 6] * 16 + 3
+
+
+def test_page_copy_on_write_sampling_example():
+    g = examples()["copy_on_write_sampling"]
+    # a prompt of 5 full blocks shared by 3 samples, each diverging into one private block
+    w = W.build_prefix_sharing(1, g["samples"], 5 * 16, 16, 2, 64, "f16", seed=3)
+    tables = [set(t[t >= 0].tolist()) for t in w.block_tables]
+    shared = set.intersection(*tables)
+    assert len(shared) == g["shared_blocks"]
+    assert len(set.union(*tables)) == g["total_with_sharing"]
+    assert sum(len(t) for t in tables) == g["total_without_sharing"]
+    assert all(w.ref_cnt[b] == g["ref_cnt"] for b in shared)
+    assert len(w.copy_pairs) == 0          # the prompt ends on a block boundary: nothing to copy
+
+
+def test_tiny_decode_slots_by_hand():
+    """seq_lens {1,7,16,33} count the new token, so it sits at positions 0, 6, 15 and 32: logical
+    blocks 0, 0, 0 and 2 at offsets 0, 6, 15 and 0; 1+1+1+3 = 6 of the 16 blocks are used."""
+    w = W.tiny_decode()
+    bt = w.block_tables
+    assert w.num_blocks == 16
+    assert list(w.slot_mapping) == [bt[0, 0] * 16, bt[1, 0] * 16 + 6, bt[2, 0] * 16 + 15, bt[3, 2] * 16]
+    used = bt[bt >= 0]
+    assert len(used) == 6 and len(set(used.tolist())) == 6
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "llama2_7b_decode", "chunked_prefill_mixed"])
+def test_independent_sequences_hold_ceil_blocks_each(name):
+    w = W.named(name)
+    need = 0
+    seen = set()
+    for s, L in enumerate(w.seq_lens):
+        row = w.block_tables[s]
+        n = W.blocks_needed(int(L))
+        need += n
+        assert (row[:n] >= 0).all() and (row[n:] == -1).all()
+        assert not seen & set(row[:n].tolist())
+        seen |= set(row[:n].tolist())
+    assert max(seen) < w.num_blocks
+    if name != "tiny_decode":
+        assert w.num_blocks == need + -(-need // 10)
+    assert len(set(w.slot_mapping.tolist())) == len(w.slot_mapping)
+    assert np.array_equal(w.ref_cnt[sorted(seen)], np.ones(len(seen)))
+
+
+@pytest.mark.parametrize("prefix,pairs", [(2040, 224), (2048, 0)])
+def test_prefix_sharing_reference_counts_and_copies(prefix, pairs):
+    w = W.prefix_sharing_sampling(prefix)
+    assert len(w.seq_lens) == 256 and len(w.copy_pairs) == pairs
+    counts = np.zeros(w.num_blocks, np.int64)
+    for s, L in enumerate(w.seq_lens):
+        n = W.blocks_needed(int(L))
+        row = w.block_tables[s]
+        assert (row[:n] >= 0).all() and (row[n:] == -1).all()
+        counts[row[:n]] += 1
+        assert prefix < L <= prefix + 512
+    # I4: a block's reference count is the number of tables that hold it
+    assert np.array_equal(counts, w.ref_cnt)
+    for g in range(32):
+        first = w.block_tables[8 * g]
+        assert all(counts[b] == 8 for b in first[:127])
+        if pairs:
+            srcs = w.copy_pairs[7 * g:7 * g + 7, 0]
+            assert (srcs == srcs[0]).all() and counts[srcs[0]] == 1
+            assert w.block_tables[8 * g + 7, 127] == srcs[0]        # the last holder writes in place
+            dsts = w.copy_pairs[7 * g:7 * g + 7, 1]
+            assert list(dsts) == [w.block_tables[8 * g + j, 127] for j in range(7)]
+        else:
+            assert counts[first[127]] == 8
+    dst = w.copy_pairs[:, 1]
+    assert len(set(dst.tolist())) == len(dst) and not set(dst.tolist()) & set(w.copy_pairs[:, 0].tolist())
+
+
+def test_mixed_step_token_budget_split():
+    g = examples()["token_budget"]
+    w = W.chunked_prefill_mixed()
+    assert w.n_decode == g["decodes"]
+    chunk = int(w.cu_q_lens[-1])
+    assert chunk == min(g["prefill_remaining"], g["budget"] - g["decodes"]) == g["chunk"]
+    assert len(w.slot_mapping) == g["budget"]
+    L = int(w.seq_lens[-1])
+    assert L - chunk == 6144 and (L - chunk) % 16 == 0 and L % 16 == 0
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 1.0 + 2**-9], np.float32)
+    got = W.f32_to_words(x, "bf16")
+    # 1+2^-8 is a tie between 1 and 1+2^-7: even mantissa (1.0); 1+3*2^-8 ties up to 1+2^-6
+    assert list(got) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F80]
+
+
+def test_generator_is_deterministic():
+    a, b = W.build([30, 50], 4, 2, 64, "bf16", seed=9), W.build([30, 50], 4, 2, 64, "bf16", seed=9)
+    assert np.array_equal(a.k_cache, b.k_cache) and np.array_equal(a.block_tables, b.block_tables)
+    c = W.build([30, 50], 4, 2, 64, "bf16", seed=10)
+    assert not np.array_equal(a.k_cache, c.k_cache)
