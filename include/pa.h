@@ -1,0 +1,158 @@
+/*
+ * pa.h -- C ABI of the paged-attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of PagedAttention as the pages state them:
+ *   [MEM] openeuler.csdn.net "高并发 AI 服务的内存瓶颈": KV cache cut into fixed 16-token blocks
+ *         reached through a per-sequence block table (sections "vLLM - PagedAttention",
+ *         "Block Table 数据结构", "Attention 计算时的 Block 映射"); copy-on-write of shared blocks
+ *         (section "机制 2：写时复制").
+ *   [PD]  lilinji.mintlify.site lecture 32 "LLM 在线推理两阶段（Prefill vs Decode）…": attention
+ *         softmax(Q K^T / sqrt(d_k)) V and the decode step that appends k_t, v_t and attends the whole
+ *         history (§3.1); GQA head groups (§3.4); causal masking (§1.1); chunked prefill mixed with
+ *         decodes under one token budget (§5.4, §5.5).
+ *   [OV]  devpress.csdn.net/amd vLLM overview: per-block attention over the block table (§3 (3))
+ *         combined with a running maximum and sum of exponentials (§9 (4) online softmax).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller, row-major and contiguous, and
+ *    aligned to 16 bytes. The library allocates no memory, keeps no state between calls (apart from
+ *    a thread-local error message) and may be called from several threads.
+ *  - 16-bit element type: PA_DTYPE_F16 (IEEE binary16) or PA_DTYPE_BF16 (bfloat16). Queries, keys,
+ *    values, caches and outputs all share it. Arithmetic is float32; outputs are rounded to nearest
+ *    even.
+ *  - Cache layout: k_cache and v_cache are [num_blocks][num_kv_heads][PA_BLOCK_SIZE][head_dim].
+ *    Slot s (the storage position of a token, physical_block * 16 + offset, [MEM] Block Table
+ *    数据结构) is block s / 16, in-block offset s % 16; each (block, kv head) tile of 16 rows is
+ *    contiguous.
+ *  - head_dim is 64 or 128. Query head h reads kv head h / (num_q_heads / num_kv_heads) ([PD] §3.4).
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work: they return
+ *    before it runs and never synchronise with the device.
+ *  - Argument checks run on the host before anything is enqueued; a failed check returns its status
+ *    and enqueues nothing. Index CONTENTS live on the device and are not read by the host. The
+ *    kernels never access memory outside the arguments for any index values: a slot, block id or
+ *    copy pair outside the pool is skipped (it writes nothing / contributes nothing), and a sequence
+ *    length beyond the stated maximum is clamped to it. Such inputs give unspecified results, not
+ *    faults.
+ *  - Errors: PA_ERR_INVALID_ARG (bad pointer, alignment, count or size), PA_ERR_UNSUPPORTED (a
+ *    head_dim or head-group size with no kernel), PA_ERR_WORKSPACE (workspace too small),
+ *    PA_ERR_HIP (a launch failed). pa_last_error() gives the calling thread's last message.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,
+    PA_ERR_UNSUPPORTED = 2,
+    PA_ERR_WORKSPACE = 3,
+    PA_ERR_HIP = 4
+} pa_status_t;
+
+typedef enum { PA_DTYPE_F16 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+
+/*
+ * pa_reshape_and_cache -- write the new tokens' keys and values into their cache slots.
+ * [PD] §3.1: a decode step computes k_t, v_t and appends them to the cache; [OV] §8 (1)(2): each
+ * layer stores its new K and V into the paged cache; [MEM] Block Table 数据结构: the slot of a
+ * position is physical_block * 16 + offset.
+ *   key, value    [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  [num_tokens] int32; token t goes to slot slot_mapping[t]; a negative slot means
+ *                 "skip this token". Slots in one call must be distinct (else the surviving write is
+ *                 unspecified). The values are copied bit for bit.
+ *   k_cache, v_cache  updated in place; every other word is left untouched.
+ * num_tokens == 0 is a no-op.
+ */
+pa_status_t pa_reshape_and_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                 int32_t head_dim, const void *key, const void *value,
+                                 void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                 int32_t num_tokens, void *stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write of shared blocks ([MEM] 机制 2：写时复制: samples that share a
+ * prompt's blocks by reference count get a private copy where they diverge).
+ *   block_mapping [num_pairs][2] int32 (src, dst): the WHOLE block src -- all 16 slots, all kv heads
+ *                 -- is copied to block dst, in both caches, bit for bit. Destinations must be
+ *                 distinct and no destination may also be a source (the order of the copies is then
+ *                 irrelevant).
+ * num_pairs == 0 is a no-op.
+ */
+pa_status_t pa_copy_blocks(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, void *k_cache, void *v_cache,
+                           const int32_t *block_mapping, int32_t num_pairs, void *stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (0 when no partial results are kept:
+ * partition_size == 0 or max_seq_len <= partition_size).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * pa_decode -- one query token per sequence attends its whole paged history.
+ * [PD] §3.1: the step's query q_t attends K_{1:t}, V_{1:t}, which already hold its own k_t, v_t
+ * (write them first with pa_reshape_and_cache); [MEM] Attention 计算时的 Block 映射: position i is
+ * read from block block_tables[s][i / 16] at offset i % 16; [PD] §3.4: GQA groups.
+ *   out, query    [num_seqs][num_q_heads][head_dim]; out[s][h] = softmax(scale * q K^T) V over
+ *                 positions 0 .. seq_lens[s]-1 of kv head h / group; a zero length gives zeros.
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32; only entries < ceil(seq_lens[s] / 16) are
+ *                 read (padding such as -1 is never read).
+ *   seq_lens      [num_seqs] int32, counting the token being decoded.
+ *   max_seq_len   a host-side upper bound on seq_lens (sizes the launch); <= 16 * max_blocks_per_seq.
+ *   partition_size  0: one pass per (sequence, kv head). Otherwise a multiple of 16 (at most 1024):
+ *                 each sequence is cut into parts of that many tokens, processed in parallel, and
+ *                 merged by rescaling with the parts' maxima and sums of exponentials ([OV] §9 (4)).
+ *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL when
+ *                 that is 0); its contents are overwritten.
+ * `out` must not alias any input.
+ */
+pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                      int32_t head_dim, void *out, const void *query, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * pa_prefill_chunk -- causal attention of prefill chunks over their paged context.
+ * [PD] §5.4: a long prompt is processed in chunks; a chunk attends the already-cached context and
+ * the earlier part of itself. [PD] §1.1: causal order.
+ *   query, out    [total_q][num_q_heads][head_dim]. Sequence s owns rows cu_q_lens[s] ..
+ *                 cu_q_lens[s+1]-1, which are its last q_len_s = cu_q_lens[s+1] - cu_q_lens[s]
+ *                 positions: row i of the chunk is at position p = seq_lens[s] - q_len_s + i and
+ *                 attends positions 0..p inclusive. The chunk's own keys and values must already be
+ *                 in the cache (pa_reshape_and_cache).
+ *   cu_q_lens     [num_seqs + 1] int32, non-decreasing from 0 to total_q.
+ *   seq_lens      [num_seqs] int32 (context including the chunk); block_tables as in pa_decode.
+ *   max_q_len     a host-side upper bound on q_len_s (sizes the launch).
+ * Rows whose position would be negative (q_len_s > seq_lens[s]) are written as zeros.
+ */
+pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, void *out, const void *query,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, const int32_t *cu_q_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, float scale, void *stream);
+
+/* Static text for a status code. */
+const char *pa_status_string(pa_status_t status);
+
+/* The calling thread's last error message ("" when the last call succeeded). */
+const char *pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,194 @@
+"""Thin ctypes binding of libpa.so (include/pa.h).
+
+Argument marshalling only: each wrapper checks tensor shapes, dtypes and devices, passes raw device
+pointers, sizes and the current HIP stream to the C entry point of the same name, and raises on a
+non-zero status. All work runs in the library's HIP kernels; there is no fallback path, and loading
+fails loudly when the library has not been built.
+
+Tensors are torch tensors on the GPU: float16 or bfloat16 for queries/keys/values/caches/outputs,
+int32 for tables and index arrays. Caches have shape [num_blocks, num_kv_heads, 16, head_dim].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+BLOCK_SIZE = 16
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int32
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so. Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libpa.so not built: {LIB_PATH} (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [_i]
+        L.pa_last_error.restype = ctypes.c_char_p
+        L.pa_last_error.argtypes = []
+        L.pa_reshape_and_cache.restype = _i
+        L.pa_reshape_and_cache.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p]
+        L.pa_copy_blocks.restype = _i
+        L.pa_copy_blocks.argtypes = [_i, _i, _i, _i, _p, _p, _p, _i, _p]
+        L.pa_decode_workspace_size.restype = _sz
+        L.pa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        L.pa_decode.restype = _i
+        L.pa_decode.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _i,
+                                _p, _sz, _p]
+        L.pa_prefill_chunk.restype = _i
+        L.pa_prefill_chunk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _i,
+                                       _i, _f, _p]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        L = lib()
+        msg = L.pa_last_error().decode() or L.pa_status_string(status).decode()
+        raise PAError(status, f"{L.pa_status_string(status).decode()}: {msg}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache differ in shape or dtype")
+    if k_cache.dtype not in _DTYPE:
+        raise ValueError(f"cache dtype {k_cache.dtype}: float16 or bfloat16")
+    for t in (k_cache, v_cache):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("caches must be contiguous GPU tensors")
+    nb, hkv, _, d = k_cache.shape
+    return _DTYPE[k_cache.dtype], int(nb), int(hkv), int(d)
+
+
+def _gpu(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """pa_reshape_and_cache: key/value [T, H_kv, D] into the slots slot_mapping[T] (int32)."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    T = int(slot_mapping.shape[0])
+    for t, n in ((key, "key"), (value, "value")):
+        _gpu(t, n, k_cache.dtype)
+        if tuple(t.shape) != (T, hkv, d):
+            raise ValueError(f"{n} must be [{T}, {hkv}, {d}]")
+    _gpu(slot_mapping, "slot_mapping", torch.int32)
+    _check(lib().pa_reshape_and_cache(dt, nb, hkv, d, key.data_ptr(), value.data_ptr(),
+                                      k_cache.data_ptr(), v_cache.data_ptr(),
+                                      slot_mapping.data_ptr(), T, _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
+    """pa_copy_blocks: whole-block copies of the (src, dst) rows of block_mapping [N, 2] int32."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    _gpu(block_mapping, "block_mapping", torch.int32)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [N, 2]")
+    n = int(block_mapping.shape[0])
+    _check(lib().pa_copy_blocks(dt, nb, hkv, d, k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_mapping.data_ptr() if n else None, n, _stream(stream)))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                              partition_size))
+
+
+def default_partition_size(max_seq_len: int) -> int:
+    """Split long contexts into 512-token parts; short ones run unsplit."""
+    return 512 if max_seq_len > 512 else 0
+
+
+def alloc_decode_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size,
+                           device=None) -> Optional[torch.Tensor]:
+    n = decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+           partition_size: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> None:
+    """pa_decode: out/query [B, H_q, D]; block_tables [B, max_blocks] int32; seq_lens [B] int32."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, k_cache.dtype)
+        if tuple(t.shape) != (B, hq, d):
+            raise ValueError(f"{n} must be [{B}, {hq}, {d}]")
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(seq_lens, "seq_lens", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
+    if partition_size is None:
+        partition_size = default_partition_size(max_seq_len)
+    need = decode_workspace_size(B, hq, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = alloc_decode_workspace(B, hq, d, max_seq_len, partition_size, query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(),
+                           v_cache.data_ptr(), block_tables.data_ptr(),
+                           int(block_tables.shape[1]), seq_lens.data_ptr(), B, int(max_seq_len),
+                           hq, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+                           _stream(stream)))
+
+
+def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,
+                  max_q_len: int, scale: float, stream=None) -> None:
+    """pa_prefill_chunk: out/query [total_q, H_q, D]; cu_q_lens [S+1]; seq_lens [S]; tables
+    [S, max_blocks]."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    tq, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, k_cache.dtype)
+        if tuple(t.shape) != (tq, hq, d):
+            raise ValueError(f"{n} must be [{tq}, {hq}, {d}]")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (cu_q_lens, "cu_q_lens")):
+        _gpu(t, n, torch.int32)
+    S = int(seq_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q_lens.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and cu_q_lens [S + 1]")
+    _check(lib().pa_prefill_chunk(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
+                                  k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                  int(block_tables.shape[1]), seq_lens.data_ptr(),
+                                  cu_q_lens.data_ptr(), S, tq, int(max_q_len), hq, float(scale),
+                                  _stream(stream)))

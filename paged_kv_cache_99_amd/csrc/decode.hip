@@ -1,0 +1,350 @@
+// decode.hip -- paged decode attention for gfx950 (HBM-bound; vector ALU, no MFMA).
+//
+// What it computes: for each sequence s and query head h, softmax(scale * q K^T) V over positions
+// 0..L-1 of kv head h / group (lecture 32 "LLM 在线推理两阶段" §3.1 formula and decode step, §3.4
+// GQA groups), with position i read from block table[s][i / 16] at offset i % 16
+// (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", Attention 计算时的 Block 映射). Blocks are
+// consumed one at a time with a running maximum and running sum of exponentials, and partial results
+// are combined by rescaling to the common maximum (devpress.csdn.net/amd vLLM overview, §9 (4)
+// online softmax; §3 (3) per-block accumulation over the block table).
+//
+// Work unit: one wavefront per (sequence, kv head, query-head subgroup, partition). A (block,
+// kv head) tile is 16 rows x D contiguous 16-bit words (4 KiB at D = 128). Lane l of the wave
+// loads 16 bytes at offset 16*l of each 1 KiB piece of the tile, so every load instruction reads
+// one contiguous KiB, and lane l then holds 8 dims (l % RL)*8.. of token rows (l / RL) + ROWS*i.
+// Scores: each lane dots its 8 dims with the G queries (v_dot2_f32_{f16,bf16}); the RL lanes of a
+// row finish the sum with DPP. Softmax and P*V need no cross-lane traffic at all: every lane keeps
+// its own running max / sum / 8-dim accumulator for the tokens of its row class, and the ROWS row
+// classes are merged once at the end of the unit. The next tile's loads are issued before the
+// current tile is consumed.
+//
+// Split-K: with partition_size P > 0 the unit covers tokens [part*P, (part+1)*P) and writes its
+// unnormalised accumulator, max and sum (log2 domain) to the workspace; a merge kernel rescales the
+// parts of each (sequence, head) to their common maximum and normalises.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+struct DecodeParams {
+    const uint16_t *__restrict__ query;
+    const uint16_t *__restrict__ k_cache;
+    const uint16_t *__restrict__ v_cache;
+    const int32_t *__restrict__ block_tables;
+    const int32_t *__restrict__ seq_lens;
+    uint16_t *__restrict__ out;
+    float *__restrict__ ws_acc;
+    float *__restrict__ ws_ml;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t num_blocks;
+    int32_t max_seq_len;
+    int32_t part_tokens;  // tokens per unit (multiple of 16)
+    int32_t max_parts;
+    int32_t n_sub;        // query-head subgroups per kv head
+    int32_t n_units;
+    int32_t split;
+    float scale_log2;     // scale * log2(e): scores live in the log2 domain
+};
+
+template <bool BF, int D, int GK>
+__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
+{
+    constexpr int RL = D / 8;            // lanes per token row (8 elements = 16 bytes each)
+    constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
+    constexpr int NCH = kBlock / ROWS;   // loads per (block, kv head) tile
+    const int lane = threadIdx.x;
+    const int r = lane / RL;
+
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
+    if (unit >= p.n_units)
+        return;
+    const int seq = unit % p.num_seqs;
+    int rest = unit / p.num_seqs;
+    const int part = rest % p.max_parts;
+    rest /= p.max_parts;
+    const int sub = rest % p.n_sub;
+    const int kvh = rest / p.n_sub;
+    const int h0 = (kvh * p.n_sub + sub) * GK;  // first query head of this unit
+
+    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
+    const int t0 = part * p.part_tokens;
+    if (p.split && t0 >= L)
+        return;  // a part with no tokens: the merge never reads it
+    const int t1 = min(L, t0 + p.part_tokens);
+
+    uint4 q[GK];
+#pragma unroll
+    for (int h = 0; h < GK; ++h)
+        q[h] = *(const uint4 *)(p.query + ((size_t)seq * p.num_q_heads + h0 + h) * D +
+                                (lane % RL) * 8);
+
+    float m[GK], l[GK], acc[GK][8];
+#pragma unroll
+    for (int h = 0; h < GK; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[h][j] = 0.0f;
+    }
+
+    const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
+    const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D;
+    const size_t tile_off = (size_t)kvh * kBlock * D + lane * 8;
+
+    for (int bb = t0 / kBlock; bb * kBlock < t1; bb += kWave) {
+        const int nb = min(kWave, (t1 - bb * kBlock + kBlock - 1) / kBlock);
+        const int my_blk = lane < nb ? table[bb + lane] : 0;
+
+        auto load = [&](int k, uint4(&kk)[NCH], uint4(&vv)[NCH]) {
+            int blk = __builtin_amdgcn_readlane(my_blk, k);
+            blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+            const uint16_t *kp = p.k_cache + blk * block_stride + tile_off;
+            const uint16_t *vp = p.v_cache + blk * block_stride + tile_off;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                kk[i] = *(const uint4 *)(kp + i * ROWS * D);
+                vv[i] = *(const uint4 *)(vp + i * ROWS * D);
+            }
+        };
+
+        auto consume = [&](int k, const uint4(&kk)[NCH], uint4(&vv)[NCH]) {
+            const int base = (bb + k) * kBlock;
+            const int raw = __builtin_amdgcn_readlane(my_blk, k);
+            const bool good_blk = (unsigned)raw < (unsigned)p.num_blocks;
+            float s[GK][NCH];
+#pragma unroll
+            for (int h = 0; h < GK; ++h)
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    s[h][i] = group_sum<RL>(dot8<BF>(q[h], kk[i])) * p.scale_log2;
+            if (!(good_blk && base + kBlock <= t1)) {  // a tail block (or a bad id): mask
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const bool ok = good_blk && base + i * ROWS + r < t1;
+#pragma unroll
+                    for (int h = 0; h < GK; ++h)
+                        s[h][i] = ok ? s[h][i] : -INFINITY;
+                    // a masked row may hold any bits (NaN included): zero it before P*V
+                    vv[i] = ok ? vv[i] : make_uint4(0, 0, 0, 0);
+                }
+            }
+            float pr[GK][NCH];
+#pragma unroll
+            for (int h = 0; h < GK; ++h) {
+                float mx = s[h][0];
+#pragma unroll
+                for (int i = 1; i < NCH; ++i)
+                    mx = fmaxf(mx, s[h][i]);
+                const float mn = fmaxf(m[h], mx);
+                const float ms = mn == -INFINITY ? 0.0f : mn;
+                const float alpha = fast_exp2(m[h] - ms);
+                float psum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    pr[h][i] = fast_exp2(s[h][i] - ms);
+                    psum += pr[h][i];
+                }
+                l[h] = l[h] * alpha + psum;
+                m[h] = mn;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[h][j] *= alpha;
+            }
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = lo_f32<BF>(w[j]), v1 = hi_f32<BF>(w[j]);
+#pragma unroll
+                    for (int h = 0; h < GK; ++h) {
+                        acc[h][2 * j] += pr[h][i] * v0;
+                        acc[h][2 * j + 1] += pr[h][i] * v1;
+                    }
+                }
+            }
+        };
+
+        uint4 ka[NCH], va[NCH], kn[NCH], vn[NCH];
+        load(0, ka, va);
+        for (int k = 0; k < nb; ++k) {
+            if (k + 1 < nb)
+                load(k + 1, kn, vn);
+            consume(k, ka, va);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                ka[i] = kn[i];
+                va[i] = vn[i];
+            }
+        }
+    }
+
+    // merge the ROWS row classes of every head (lanes that differ in their row index)
+#pragma unroll
+    for (int h = 0; h < GK; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int off = RL; off < kWave; off <<= 1)
+            M = fmaxf(M, xor_shfl(M, off));
+        const float f = fast_exp2(m[h] - (M == -INFINITY ? 0.0f : M));
+        float lh = l[h] * f;
+#pragma unroll
+        for (int off = RL; off < kWave; off <<= 1)
+            lh += xor_shfl(lh, off);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float a = acc[h][j] * f;
+#pragma unroll
+            for (int off = RL; off < kWave; off <<= 1)
+                a += xor_shfl(a, off);
+            acc[h][j] = a;
+        }
+        m[h] = M;
+        l[h] = lh;
+    }
+
+    if (lane < RL) {
+#pragma unroll
+        for (int h = 0; h < GK; ++h) {
+            const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
+            if (p.split) {
+                float *wa = p.ws_acc + (row * p.max_parts + part) * D + lane * 8;
+                *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                if (lane == 0)
+                    *(float2 *)(p.ws_ml + (row * p.max_parts + part) * 2) = make_float2(m[h], l[h]);
+            } else {
+                const float inv = l[h] > 0.0f ? 1.0f / l[h] : 0.0f;
+                uint4 o;
+                o.x = pack2<BF>(acc[h][0] * inv, acc[h][1] * inv);
+                o.y = pack2<BF>(acc[h][2] * inv, acc[h][3] * inv);
+                o.z = pack2<BF>(acc[h][4] * inv, acc[h][5] * inv);
+                o.w = pack2<BF>(acc[h][6] * inv, acc[h][7] * inv);
+                *(uint4 *)(p.out + row * D + lane * 8) = o;
+            }
+        }
+    }
+}
+
+// One wave per (sequence, query head): rescale every part to the common maximum M,
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
+{
+    constexpr int DPL = D / kWave;  // dims per lane
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int idx = blockIdx.x * 4 + wave;
+    if (idx >= p.num_seqs * p.num_q_heads)
+        return;
+    const int seq = idx / p.num_q_heads;
+    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
+    const int np = (L + p.part_tokens - 1) / p.part_tokens;
+    const float *ml = p.ws_ml + (size_t)idx * p.max_parts * 2;
+    const float *ac = p.ws_acc + (size_t)idx * p.max_parts * D + lane * DPL;
+
+    float M = -INFINITY;
+    for (int j = lane; j < np; j += kWave)
+        M = fmaxf(M, ml[2 * j]);
+    M = wave_max(M);
+    float W = 0.0f;
+    for (int j = lane; j < np; j += kWave)
+        W += fast_exp2(ml[2 * j] - M) * ml[2 * j + 1];
+    W = wave_sum(W);
+
+    float o[DPL];
+#pragma unroll
+    for (int d = 0; d < DPL; ++d)
+        o[d] = 0.0f;
+    for (int j = 0; j < np; ++j) {
+        const float w = fast_exp2(ml[2 * j] - M);
+#pragma unroll
+        for (int d = 0; d < DPL; ++d)
+            o[d] += w * ac[(size_t)j * D + d];
+    }
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    uint16_t *dst = p.out + (size_t)idx * D + lane * DPL;
+    if constexpr (DPL == 2)
+        *(uint32_t *)dst = pack2<BF>(o[0] * inv, o[1] * inv);
+    else
+        *dst = (uint16_t)to_word<BF>(o[0] * inv);
+}
+
+template <bool BF, int D, int GK>
+hipError_t launch_typed(const DecodeParams &p, hipStream_t stream)
+{
+    const int grid = round_up8(p.n_units);
+    hipLaunchKernelGGL((decode_partition_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0, stream,
+                       p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.split)
+        return e;
+    const int rows = p.num_seqs * p.num_q_heads;
+    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <bool BF, int D>
+hipError_t launch_gk(int gk, const DecodeParams &p, hipStream_t stream)
+{
+    switch (gk) {
+    case 8: return launch_typed<BF, D, 8>(p, stream);
+    case 4: return launch_typed<BF, D, 4>(p, stream);
+    case 2: return launch_typed<BF, D, 2>(p, stream);
+    default: return launch_typed<BF, D, 1>(p, stream);
+    }
+}
+
+}  // namespace
+
+bool decode_supported(int32_t head_dim, int32_t group)
+{
+    return (head_dim == 64 || head_dim == 128) && group >= 1;
+}
+
+hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
+{
+    if (d.num_seqs == 0)
+        return hipSuccess;
+    const int group = d.num_q_heads / d.c.num_kv_heads;
+    const int gk = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    DecodeParams p;
+    p.query = (const uint16_t *)d.query;
+    p.k_cache = (const uint16_t *)d.k_cache;
+    p.v_cache = (const uint16_t *)d.v_cache;
+    p.block_tables = d.block_tables;
+    p.seq_lens = d.seq_lens;
+    p.out = (uint16_t *)d.out;
+    p.ws_acc = d.ws_acc;
+    p.ws_ml = d.ws_ml;
+    p.max_blocks = d.max_blocks;
+    p.num_seqs = d.num_seqs;
+    p.num_kv_heads = d.c.num_kv_heads;
+    p.num_q_heads = d.num_q_heads;
+    p.num_blocks = d.c.num_blocks;
+    p.max_seq_len = d.max_seq_len;
+    p.split = d.max_parts > 0 ? 1 : 0;
+    p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
+    if (p.part_tokens < kBlock)
+        p.part_tokens = kBlock;
+    p.max_parts = p.split ? d.max_parts : 1;
+    p.n_sub = group / gk;
+    const int64_t units = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.max_parts;
+    if (units > 0x7ffffff0)
+        return hipErrorInvalidValue;
+    p.n_units = (int32_t)units;
+    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    if (d.c.bf16)
+        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, stream)
+                                  : launch_gk<true, 128>(gk, p, stream);
+    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, stream)
+                              : launch_gk<false, 128>(gk, p, stream);
+}
+
+}  // namespace pa

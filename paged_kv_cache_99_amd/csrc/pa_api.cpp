@@ -1,0 +1,258 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: host-side argument checks, workspace layout
+// and dispatch to the kernel launchers. Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+pa_status_t fail(pa_status_t s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pa_status_t ok()
+{
+    g_error[0] = '\0';
+    return PA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                    \
+    do {                                                      \
+        if (!(cond))                                          \
+            return fail(PA_ERR_INVALID_ARG, __VA_ARGS__);     \
+    } while (0)
+
+#define REQUIRE_PTR(p, name)                                                              \
+    do {                                                                                  \
+        REQUIRE((p) != nullptr, "%s is NULL", name);                                      \
+        REQUIRE(aligned16(p), "%s is not 16-byte aligned", name);                         \
+    } while (0)
+
+pa_status_t check_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, pa::CacheDims *c)
+{
+    REQUIRE(dtype == PA_DTYPE_F16 || dtype == PA_DTYPE_BF16, "dtype %d is not F16 or BF16",
+            (int)dtype);
+    REQUIRE(num_blocks >= 0, "num_blocks %d < 0", num_blocks);
+    REQUIRE(num_kv_heads > 0, "num_kv_heads %d <= 0", num_kv_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", head_dim);
+    REQUIRE((int64_t)num_blocks * num_kv_heads * PA_BLOCK_SIZE * head_dim < ((int64_t)1 << 40),
+            "cache of %d blocks is too large", num_blocks);
+    c->num_blocks = num_blocks;
+    c->num_kv_heads = num_kv_heads;
+    c->head_dim = head_dim;
+    c->bf16 = dtype == PA_DTYPE_BF16;
+    return PA_OK;
+}
+
+pa_status_t launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int32_t parts_of(int32_t max_seq_len, int32_t partition_size)
+{
+    if (partition_size <= 0 || max_seq_len <= partition_size)
+        return 0;
+    return (max_seq_len + partition_size - 1) / partition_size;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(pa_status_t status)
+{
+    switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: an argument failed its check";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: no kernel for this shape";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown pa_status_t";
+}
+
+const char *pa_last_error(void) { return g_error; }
+
+pa_status_t pa_reshape_and_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                 int32_t head_dim, const void *key, const void *value,
+                                 void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                 int32_t num_tokens, void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_tokens >= 0, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0)
+        return ok();
+    REQUIRE_PTR(key, "key");
+    REQUIRE_PTR(value, "value");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(slot_mapping != nullptr, "slot_mapping is NULL");
+    return launched(pa::launch_reshape_and_cache(c, key, value, k_cache, v_cache, slot_mapping,
+                                                 num_tokens, (hipStream_t)stream),
+                    "reshape_and_cache");
+}
+
+pa_status_t pa_copy_blocks(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, void *k_cache, void *v_cache,
+                           const int32_t *block_mapping, int32_t num_pairs, void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_pairs >= 0, "num_pairs %d < 0", num_pairs);
+    if (num_pairs == 0)
+        return ok();
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(block_mapping != nullptr, "block_mapping is NULL");
+    return launched(pa::launch_copy_blocks(c, k_cache, v_cache, block_mapping, num_pairs,
+                                           (hipStream_t)stream),
+                    "copy_blocks");
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_seq_len, int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0)
+        return 0;
+    const int32_t parts = parts_of(max_seq_len, partition_size);
+    return (size_t)num_seqs * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                      int32_t head_dim, void *out, const void *query, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_seqs >= 0, "num_seqs %d < 0", num_seqs);
+    REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
+            "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+            num_kv_heads);
+    REQUIRE(max_blocks_per_seq >= 0, "max_blocks_per_seq %d < 0", max_blocks_per_seq);
+    REQUIRE(max_seq_len >= 0 && (int64_t)max_seq_len <= (int64_t)PA_BLOCK_SIZE * max_blocks_per_seq,
+            "max_seq_len %d is outside [0, 16 * max_blocks_per_seq = %lld]", max_seq_len,
+            (long long)PA_BLOCK_SIZE * max_blocks_per_seq);
+    REQUIRE(partition_size >= 0 && partition_size % PA_BLOCK_SIZE == 0 && partition_size <= 1024,
+            "partition_size %d is not 0 or a multiple of 16 up to 1024", partition_size);
+    REQUIRE(scale == scale, "scale is NaN");
+    if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
+                    num_q_heads / num_kv_heads);
+    if (num_seqs == 0)
+        return ok();
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(query, "query");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(block_tables != nullptr, "block_tables is NULL");
+    REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
+    const size_t need =
+        pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                        need);
+        REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    }
+    pa::DecodeLaunch d;
+    d.c = c;
+    d.out = out;
+    d.query = query;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.max_blocks = max_blocks_per_seq;
+    d.seq_lens = seq_lens;
+    d.num_seqs = num_seqs;
+    d.max_seq_len = max_seq_len;
+    d.num_q_heads = num_q_heads;
+    d.scale = scale;
+    d.partition_size = partition_size;
+    d.max_parts = parts_of(max_seq_len, partition_size);
+    d.ws_acc = (float *)workspace;
+    d.ws_ml = need ? (float *)workspace + (size_t)num_seqs * num_q_heads * d.max_parts * head_dim
+                   : nullptr;
+    return launched(pa::launch_decode(d, (hipStream_t)stream), "decode");
+}
+
+pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, void *out, const void *query,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, const int32_t *cu_q_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, float scale, void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_seqs >= 0, "num_seqs %d < 0", num_seqs);
+    REQUIRE(total_q >= 0, "total_q %d < 0", total_q);
+    REQUIRE(max_q_len >= 0, "max_q_len %d < 0", max_q_len);
+    REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
+            "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+            num_kv_heads);
+    REQUIRE(max_blocks_per_seq >= 0, "max_blocks_per_seq %d < 0", max_blocks_per_seq);
+    REQUIRE(scale == scale, "scale is NaN");
+    if (!pa::prefill_supported(head_dim, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %d, group %d", head_dim,
+                    num_q_heads / num_kv_heads);
+    if (num_seqs == 0 || total_q == 0)
+        return ok();
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(query, "query");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(block_tables != nullptr, "block_tables is NULL");
+    REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
+    REQUIRE(cu_q_lens != nullptr, "cu_q_lens is NULL");
+    pa::PrefillLaunch p;
+    p.c = c;
+    p.out = out;
+    p.query = query;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.cu_q_lens = cu_q_lens;
+    p.num_seqs = num_seqs;
+    p.total_q = total_q;
+    p.max_q_len = max_q_len;
+    p.num_q_heads = num_q_heads;
+    p.scale = scale;
+    return launched(pa::launch_prefill(p, (hipStream_t)stream), "prefill_chunk");
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// pa_device.h -- device-side helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per physical block
+constexpr int kWave = 64;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ 16-bit words <-> float32
+template <bool BF>
+__device__ __forceinline__ float lo_f32(uint32_t w)  // low 16-bit element of a 32-bit word
+{
+    if constexpr (BF) {
+        return __uint_as_float(w << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+}
+
+template <bool BF>
+__device__ __forceinline__ float hi_f32(uint32_t w)  // high 16-bit element
+{
+    if constexpr (BF) {
+        return __uint_as_float(w & 0xffff0000u);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+}
+
+// Round a float32 to the 16-bit type, nearest even (NaN stays a quiet NaN).
+template <bool BF>
+__device__ __forceinline__ uint32_t to_word(float x)
+{
+    if constexpr (BF) {
+        uint32_t u = __float_as_uint(x);
+        if ((u & 0x7fffffffu) > 0x7f800000u)
+            return 0x7fc0u;
+        return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    } else {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+}
+
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    return to_word<BF>(lo) | (to_word<BF>(hi) << 16);
+}
+
+// c + a.lo*b.lo + a.hi*b.hi in float32 (v_dot2_f32_f16 / v_dot2_f32_bf16).
+template <bool BF>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    if constexpr (BF) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                               __builtin_bit_cast(bf16x2, b), c, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
+                                      c, false);
+    }
+}
+
+// Dot product of two runs of 8 16-bit elements held in 16-byte vectors.
+template <bool BF>
+__device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b)
+{
+    float s = dot2<BF>(a.x, b.x, 0.0f);
+    s = dot2<BF>(a.y, b.y, s);
+    s = dot2<BF>(a.z, b.z, s);
+    return dot2<BF>(a.w, b.w, s);
+}
+
+// ------------------------------------------------------------------ cross-lane reductions (DPP)
+// DPP controls of GFX9: quad_perm(1,0,3,2) swaps neighbours, quad_perm(2,3,0,1) swaps pairs,
+// row_half_mirror reverses each 8-lane half row, row_mirror reverses each 16-lane row.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_id)
+{
+    int x = __float_as_int(v);
+    switch (ctrl_id) {
+    case 0: x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); break;
+    case 1: x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); break;
+    case 2: x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true); break;
+    default: x = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true); break;
+    }
+    return __int_as_float(x);
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group gets the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    v += dpp_f(v, 0);
+    v += dpp_f(v, 1);
+    v += dpp_f(v, 2);
+    if constexpr (N == 16)
+        v += dpp_f(v, 3);
+    return v;
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int mask)
+{
+    return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, xor_shfl(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int m = 32; m >= 1; m >>= 1)
+        v += xor_shfl(v, m);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+// ------------------------------------------------------------------ launch helpers
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup w runs on XCD w % 8). Renumbering so
+// that consecutive logical ids share an XCD keeps neighbouring work units on one L2.
+__device__ __forceinline__ int xcd_logical_id(int wg, int grid)
+{
+    const int per_xcd = grid >> 3;  // grid is a multiple of 8
+    return (wg & 7) * per_xcd + (wg >> 3);
+}
+
+__host__ __device__ constexpr int round_up8(int n) { return (n + 7) & ~7; }
+
+}  // namespace pa

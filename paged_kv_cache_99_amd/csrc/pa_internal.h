@@ -1,0 +1,69 @@
+// pa_internal.h -- launch-side interface between the C ABI (pa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct CacheDims {
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    bool bf16;
+};
+
+// reshape_and_cache.hip
+hipError_t launch_reshape_and_cache(const CacheDims &c, const void *key, const void *value,
+                                    void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                    int32_t num_tokens, hipStream_t stream);
+
+// copy_blocks.hip
+hipError_t launch_copy_blocks(const CacheDims &c, void *k_cache, void *v_cache,
+                              const int32_t *block_mapping, int32_t num_pairs, hipStream_t stream);
+
+// decode.hip
+struct DecodeLaunch {
+    CacheDims c;
+    void *out;
+    const void *query;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks;
+    const int32_t *seq_lens;
+    int32_t num_seqs;
+    int32_t max_seq_len;
+    int32_t num_q_heads;
+    float scale;
+    int32_t partition_size;  // 0 = unsplit
+    float *ws_acc;           // [num_seqs][num_q_heads][max_parts][head_dim]
+    float *ws_ml;            // [num_seqs][num_q_heads][max_parts][2]
+    int32_t max_parts;
+};
+// Group sizes with a dedicated kernel; any other group size runs as several of these.
+bool decode_supported(int32_t head_dim, int32_t group);
+hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+
+// prefill.hip
+struct PrefillLaunch {
+    CacheDims c;
+    void *out;
+    const void *query;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks;
+    const int32_t *seq_lens;
+    const int32_t *cu_q_lens;
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t max_q_len;
+    int32_t num_q_heads;
+    float scale;
+};
+bool prefill_supported(int32_t head_dim, int32_t group);
+hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,99 @@
+"""One step of the paged-attention hot path on the GPU.
+
+The order is the one the pages give for a layer of a serving step: blocks that diverge are copied
+on write (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2 写时复制), the step's new keys and
+values are written into their slots (lecture 32 "LLM 在线推理两阶段" §3.1), then the decodes and the
+prefill chunk attend their paged context (§5.4, §5.5: decodes first, the remaining token budget to a
+prefill chunk). Every stage is a call into libpa.so; this class only holds the device buffers.
+
+A step description is any object with the fields of a workload: dtype ("f16"/"bf16"), H_q, H_kv, D,
+num_blocks, seq_lens, block_tables, k_cache, v_cache (16-bit words), new_key, new_value,
+slot_mapping, copy_pairs, n_decode, query_decode, cu_q_lens, query_prefill, scale and optionally
+partition_size.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding
+
+TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def words_to_device(words: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload 16-bit words (numpy uint16) as a float16/bfloat16 tensor of the same shape."""
+    a = np.ascontiguousarray(words, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).view(TORCH_DTYPE[dtype]).to(device)
+
+
+def words_from_device(t: torch.Tensor) -> np.ndarray:
+    """Download a float16/bfloat16 tensor as its 16-bit words (numpy uint16)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ints_to_device(a, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class GpuStep:
+    def __init__(self, w, device="cuda", partition_size: Optional[int] = None):
+        self.w = w
+        self.device = torch.device(device)
+        dt, dev = w.dtype, self.device
+        shape = (w.num_blocks, w.H_kv, binding.BLOCK_SIZE, w.D)
+        self.k_cache = words_to_device(w.k_cache, dt, dev).view(shape)
+        self.v_cache = words_to_device(w.v_cache, dt, dev).view(shape)
+        self.new_key = words_to_device(w.new_key, dt, dev)
+        self.new_value = words_to_device(w.new_value, dt, dev)
+        self.slot_mapping = ints_to_device(w.slot_mapping, dev)
+        self.copy_pairs = ints_to_device(np.asarray(w.copy_pairs).reshape(-1, 2), dev)
+        nd = int(w.n_decode)
+        self.n_decode = nd
+        self.dec_tables = ints_to_device(w.block_tables[:nd], dev)
+        self.dec_lens = ints_to_device(w.seq_lens[:nd], dev)
+        self.dec_query = words_to_device(w.query_decode, dt, dev)
+        self.dec_out = torch.empty_like(self.dec_query)
+        self.max_seq_len = int(np.max(w.seq_lens[:nd])) if nd else 0
+        if partition_size is None:
+            partition_size = getattr(w, "partition_size", None)
+        if partition_size is None:
+            partition_size = binding.default_partition_size(self.max_seq_len)
+        self.partition_size = int(partition_size)
+        self.workspace = binding.alloc_decode_workspace(nd, w.H_q, w.D, self.max_seq_len,
+                                                        self.partition_size, dev) if nd else None
+        self.pre_tables = ints_to_device(w.block_tables[nd:], dev)
+        self.pre_lens = ints_to_device(w.seq_lens[nd:], dev)
+        self.pre_cu = ints_to_device(w.cu_q_lens, dev)
+        self.pre_query = words_to_device(w.query_prefill, dt, dev)
+        self.pre_out = torch.empty_like(self.pre_query)
+        cu = np.asarray(w.cu_q_lens)
+        self.max_q_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
+
+    # ---- stages
+    def copy(self, stream=None):
+        binding.copy_blocks(self.k_cache, self.v_cache, self.copy_pairs, stream)
+
+    def scatter(self, stream=None):
+        binding.reshape_and_cache(self.new_key, self.new_value, self.k_cache, self.v_cache,
+                                  self.slot_mapping, stream)
+
+    def decode(self, stream=None):
+        if self.n_decode:
+            binding.decode(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
+                           self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,
+                           self.partition_size, self.workspace, stream)
+
+    def prefill(self, stream=None):
+        if self.pre_query.shape[0]:
+            binding.prefill_chunk(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
+                                  self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
+                                  self.w.scale, stream)
+
+    def run(self, stream=None):
+        self.copy(stream)
+        self.scatter(stream)
+        self.decode(stream)
+        self.prefill(stream)

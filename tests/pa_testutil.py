@@ -1,0 +1,80 @@
+"""Shared helpers of the GPU parity tests: expected values from the oracle, and the comparison gates.
+
+Expected values come only from oracle/ applied to the generator's inputs: the oracle's own copy and
+scatter produce the pool the oracle's attention then reads.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+ATOL = 2e-3      # max |gpu - oracle| over every element
+ROW_RTOL = 1e-2  # max over (token, head) rows of ||gpu - oracle||_inf / ||oracle||_inf
+
+
+def words_to_f64(words, dtype):
+    """16-bit words to float64 (numpy / torch decoding, equal to oracle.to_double on all codes)."""
+    w = np.ascontiguousarray(words, dtype=np.uint16)
+    if dtype == "f16":
+        return w.view(np.float16).astype(np.float64)
+    return torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def oracle_pool_after_step(w, poison=False):
+    """The pool the attention of a step reads: copy_blocks, then reshape_and_cache, on the CPU."""
+    kc, vc = w.k_cache, w.v_cache
+    if poison:
+        kc, vc = oracle.poison_free_slots(kc, vc, w.block_tables, w.seq_lens, w.num_blocks,
+                                          w.H_kv, w.D, w.dtype)
+    if len(w.copy_pairs):
+        kc, vc = oracle.copy_blocks(kc, vc, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+    kc, vc = oracle.reshape_and_cache(w.new_key, w.new_value, kc, vc, w.slot_mapping,
+                                      w.num_blocks, w.H_kv, w.D)
+    return kc, vc
+
+
+def oracle_decode(w, kc, vc, pairs=None, nthreads=0):
+    nd = w.n_decode
+    return oracle.decode(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
+                         w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, pairs=pairs,
+                         nthreads=nthreads)
+
+
+def oracle_prefill(w, kc, vc, rows=None, nthreads=0):
+    nd = w.n_decode
+    return oracle.prefill(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
+                          w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                          rows=rows, nthreads=nthreads)
+
+
+def attention_errors(got_words, ref, dtype):
+    """(max abs error, max row-normwise relative error) of 16-bit outputs against float64."""
+    got = words_to_f64(got_words, dtype).reshape(ref.shape)
+    D = ref.shape[-1]
+    err = np.abs(got - ref).reshape(-1, D)
+    row_ref = np.abs(ref).reshape(-1, D).max(axis=1)
+    row_err = err.max(axis=1)
+    zero = row_ref == 0
+    rel = np.where(zero, np.where(row_err == 0, 0.0, np.inf), row_err / np.where(zero, 1, row_ref))
+    return (float(err.max()) if err.size else 0.0), (float(rel.max()) if rel.size else 0.0), got
+
+
+def assert_attention_close(got_words, ref, dtype, what="", strict=True):
+    """Gate of an attention output against the float64 oracle.
+
+    Always: every element within |gpu - ref| <= 2e-3 + 1e-2 * |ref| (absolute 2e-3 and relative
+    1e-2 read together, as torch.testing.assert_close does). strict=True adds the stronger gate used
+    on the named workloads: max |gpu - ref| <= 2e-3 over every element and a row-normwise relative
+    error <= 1e-2. Short contexts give outputs near 1, where rounding to bfloat16 alone moves a value
+    by up to 2^-9 * |ref| (3.9e-3 at |ref| in [1, 2)): edge-case tests of such contexts run with
+    strict=False.
+    """
+    max_abs, max_rel, got = attention_errors(got_words, ref, dtype)
+    excess = float((np.abs(got - ref) - (ATOL + ROW_RTOL * np.abs(ref))).max()) if ref.size else 0.0
+    print(f"[parity] {what}: max_abs={max_abs:.3e} max_row_rel={max_rel:.3e} "
+          f"max(|d| - (atol + rtol|ref|))={excess:.3e} n={ref.size}", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert excess <= 0, f"{what}: |d| exceeds 2e-3 + 1e-2 |ref| by {excess:.3e}"
+    if strict:
+        assert max_abs <= ATOL, f"{what}: max abs error {max_abs:.3e} > {ATOL}"
+        assert max_rel <= ROW_RTOL, f"{what}: row-normwise relative error {max_rel:.3e} > {ROW_RTOL}"

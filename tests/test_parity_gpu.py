@@ -1,0 +1,177 @@
+"""GPU parity: libpa.so (through its C ABI) against the CPU oracle on the same seeded inputs.
+
+Gates: the pool after copy_blocks and reshape_and_cache is bit-identical to the oracle's (every
+word of both caches, including blocks no sequence uses); attention outputs are within 2e-3 absolute
+error everywhere and 1e-2 row-normwise relative error of the float64 oracle; attention outputs are
+bitwise reproducible and independent of which physical blocks hold the context.
+"""
+import dataclasses
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pa_workloads as W
+from paged_kv_cache_99_amd import binding
+from paged_kv_cache_99_amd.step import GpuStep, words_from_device
+from pa_testutil import (assert_attention_close, oracle_decode, oracle_pool_after_step,
+                         oracle_prefill)
+
+pytestmark = pytest.mark.gpu
+
+NAMED_DECODE = ["tiny_decode", "llama2_7b_decode", "llama70b_gqa_decode", "prefix_sharing_2040",
+                "prefix_sharing_2048", "chunked_prefill_mixed"]
+
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        t = time.time()
+        _cache.clear()  # full-size pools are large: keep one at a time
+        _cache[name] = W.named(name)
+        print(f"[parity] built {name} in {time.time() - t:.1f}s", flush=True)
+    return _cache[name]
+
+
+def poisoned(w):
+    kc, vc = oracle.poison_free_slots(w.k_cache, w.v_cache, w.block_tables, w.seq_lens,
+                                      w.num_blocks, w.H_kv, w.D, w.dtype)
+    return dataclasses.replace(w, k_cache=kc, v_cache=vc)
+
+
+def run_on_gpu(w, stages=("copy", "scatter", "decode", "prefill"), partition_size=None):
+    print(f"[parity] gpu step {w.name}: stages={stages} partition={partition_size}", flush=True)
+    g = GpuStep(w, partition_size=partition_size)
+    for s in stages:
+        getattr(g, s)()
+    torch.cuda.synchronize()
+    return g
+
+
+# ------------------------------------------------------------------- scatter and copy: bit exact
+@pytest.mark.parametrize("name", ["tiny_decode", "llama2_7b_decode", "prefix_sharing_2040",
+                                  "chunked_prefill_mixed"])
+def test_copy_and_scatter_pool_bit_exact(name):
+    w = workload(name)
+    g = run_on_gpu(w, stages=("copy", "scatter"))
+    kc, vc = oracle_pool_after_step(w)
+    assert np.array_equal(words_from_device(g.k_cache).ravel(), kc)
+    assert np.array_equal(words_from_device(g.v_cache).ravel(), vc)
+
+
+def test_copy_blocks_alone_bit_exact():
+    w = workload("prefix_sharing_2040")
+    assert len(w.copy_pairs) == 224
+    g = run_on_gpu(w, stages=("copy",))
+    kc, vc = oracle.copy_blocks(w.k_cache, w.v_cache, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+    assert np.array_equal(words_from_device(g.k_cache).ravel(), kc)
+    assert np.array_equal(words_from_device(g.v_cache).ravel(), vc)
+
+
+def test_scatter_skips_negative_and_out_of_pool_slots():
+    w = W.build([20, 5, 40], 4, 2, 128, "f16", seed=71)
+    sm = w.slot_mapping.copy()
+    sm[1] = -1
+    sm[2] = w.num_blocks * 16 + 3          # outside the pool: skipped by the kernel
+    w2 = dataclasses.replace(w, slot_mapping=sm)
+    g = run_on_gpu(w2, stages=("scatter",))
+    keep = sm.copy()
+    keep[2] = -1
+    kc, vc = oracle.reshape_and_cache(w.new_key, w.new_value, w.k_cache, w.v_cache, keep,
+                                      w.num_blocks, w.H_kv, w.D)
+    assert np.array_equal(words_from_device(g.k_cache).ravel(), kc)
+    assert np.array_equal(words_from_device(g.v_cache).ravel(), vc)
+
+
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "f16")])
+def test_scatter_many_tokens_small_heads(D, dtype):
+    w = W.build([300, 17, 1000], 2, 1, D, dtype, seed=72, n_decode=0, q_lens=[300, 17, 999])
+    g = run_on_gpu(w, stages=("scatter",))
+    kc, vc = oracle_pool_after_step(w)
+    assert np.array_equal(words_from_device(g.k_cache).ravel(), kc)
+    assert np.array_equal(words_from_device(g.v_cache).ravel(), vc)
+
+
+# ------------------------------------------------------------------------ decode: named workloads
+@pytest.mark.parametrize("name", NAMED_DECODE)
+def test_decode_named_workload(name):
+    w = workload(name)
+    g = run_on_gpu(w, stages=("copy", "scatter", "decode"))
+    kc, vc = oracle_pool_after_step(w)
+    t = time.time()
+    ref = oracle_decode(w, kc, vc)
+    print(f"[parity] oracle decode {name}: {time.time() - t:.1f}s", flush=True)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype,
+                           f"decode {name} (partition {g.partition_size})")
+
+
+# --------------------------------------------------------------------- decode: shapes and edges
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 4), (16, 4), (8, 1), (32, 2), (12, 4), (6, 2)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_head_groups(H_q, H_kv, D, dtype):
+    lens = [1, 15, 16, 17, 100, 531, 1024, 1100]
+    w = poisoned(W.build(lens, H_q, H_kv, D, dtype, seed=80 + H_q + D))
+    for part in (0, 512):
+        g = run_on_gpu(w, stages=("scatter", "decode"), partition_size=part)
+        kc, vc = oracle_pool_after_step(w)
+        assert_attention_close(words_from_device(g.dec_out), oracle_decode(w, kc, vc), dtype,
+                               f"decode H_q={H_q} H_kv={H_kv} D={D} {dtype} part={part}", strict=False)
+
+
+@pytest.mark.parametrize("part", [0, 16, 48, 256, 512, 1024])
+def test_decode_partition_sizes(part):
+    w = poisoned(W.build([2049, 16, 1, 700, 3333], 16, 2, 128, "bf16", seed=90))
+    g = run_on_gpu(w, stages=("scatter", "decode"), partition_size=part)
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.dec_out), oracle_decode(w, kc, vc), w.dtype,
+                           f"decode partition {part}", strict=False)
+
+
+def test_decode_zero_length_and_larger_max_seq_len():
+    w = W.build([0, 5, 0, 33], 4, 2, 64, "f16", seed=91, max_blocks=8)
+    g = GpuStep(w, partition_size=16)
+    g.max_seq_len = 128             # an upper bound above every length
+    g.workspace = binding.alloc_decode_workspace(4, 4, 64, 128, 16)
+    g.scatter()
+    g.decode()
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool_after_step(w)
+    out = words_from_device(g.dec_out)
+    assert not out[0].any() and not out[2].any()
+    assert_attention_close(out, oracle_decode(w, kc, vc), w.dtype, "decode zero lengths", strict=False)
+
+
+def test_decode_is_deterministic_and_independent_of_block_placement():
+    w = W.build([777, 2048, 35, 4000], 32, 8, 128, "bf16", seed=92)
+    g = run_on_gpu(w, stages=("scatter", "decode"))
+    first = words_from_device(g.dec_out)
+    g.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(first, words_from_device(g.dec_out))
+    # the same logical content under a different block assignment: physical block b -> perm[b]
+    perm = np.random.default_rng(7).permutation(w.num_blocks)
+    shape = (w.num_blocks, w.H_kv, 16, w.D)
+    kc = np.empty(shape, np.uint16)
+    vc = np.empty(shape, np.uint16)
+    kc[perm] = w.k_cache.reshape(shape)
+    vc[perm] = w.v_cache.reshape(shape)
+    bt = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    sm = (perm[w.slot_mapping // 16] * 16 + w.slot_mapping % 16).astype(np.int32)
+    w3 = dataclasses.replace(w, k_cache=kc.ravel(), v_cache=vc.ravel(), block_tables=bt,
+                             slot_mapping=sm)
+    g3 = run_on_gpu(w3, stages=("scatter", "decode"))
+    assert np.array_equal(first, words_from_device(g3.dec_out))
+
+
+# --------------------------------------------------------------------------------- errors
+def test_decode_rejects_small_workspace_without_launching():
+    w = W.build([600, 700], 4, 4, 128, "f16", seed=93)
+    g = GpuStep(w, partition_size=512)
+    with pytest.raises(binding.PAError) as e:
+        binding.decode(g.dec_out, g.dec_query, g.k_cache, g.v_cache, g.dec_tables, g.dec_lens,
+                       g.max_seq_len, w.scale, 512, g.workspace[:16])
+    assert e.value.status == binding.PA_ERR_WORKSPACE
