@@ -25,6 +25,8 @@
  *    Slot s (the storage position of a token, physical_block * 16 + offset, [MEM] Block Table
  *    数据结构) is block s / 16, in-block offset s % 16; each (block, kv head) tile of 16 rows is
  *    contiguous.
+ *  - scale (the softmax temperature, 1/sqrt(head_dim) for the pages' attention) must be finite and
+ *    positive.
  *  - head_dim is 64 or 128. Query head h reads kv head h / (num_q_heads / num_kv_heads) ([PD] §3.4).
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work: they return
  *    before it runs and never synchronise with the device.

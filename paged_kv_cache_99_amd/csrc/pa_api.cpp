@@ -164,7 +164,7 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
             (long long)PA_BLOCK_SIZE * max_blocks_per_seq);
     REQUIRE(partition_size >= 0 && partition_size % PA_BLOCK_SIZE == 0 && partition_size <= 1024,
             "partition_size %d is not 0 or a multiple of 16 up to 1024", partition_size);
-    REQUIRE(scale == scale, "scale is NaN");
+    REQUIRE(scale > 0.0f && scale < 3.0e38f, "scale %g is not a finite positive number", (double)scale);
     if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
                     num_q_heads / num_kv_heads);
@@ -224,7 +224,7 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
             "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
             num_kv_heads);
     REQUIRE(max_blocks_per_seq >= 0, "max_blocks_per_seq %d < 0", max_blocks_per_seq);
-    REQUIRE(scale == scale, "scale is NaN");
+    REQUIRE(scale > 0.0f && scale < 3.0e38f, "scale %g is not a finite positive number", (double)scale);
     if (!pa::prefill_supported(head_dim, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %d, group %d", head_dim,
                     num_q_heads / num_kv_heads);

@@ -33,24 +33,28 @@ __device__ __forceinline__ float hi_f32(uint32_t w)  // high 16-bit element
     }
 }
 
-// Round a float32 to the 16-bit type, nearest even (NaN stays a quiet NaN).
+// Round float32 values to the 16-bit type, nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on
+// gfx950; NaN stays NaN).
 template <bool BF>
-__device__ __forceinline__ uint32_t to_word(float x)
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
 {
     if constexpr (BF) {
-        uint32_t u = __float_as_uint(x);
-        if ((u & 0x7fffffffu) > 0x7f800000u)
-            return 0x7fc0u;
-        return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
     } else {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+        const f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
     }
 }
 
 template <bool BF>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+__device__ __forceinline__ uint32_t to_word(float x)
 {
-    return to_word<BF>(lo) | (to_word<BF>(hi) << 16);
+    if constexpr (BF) {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+    } else {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+    }
 }
 
 // c + a.lo*b.lo + a.hi*b.hi in float32 (v_dot2_f32_f16 / v_dot2_f32_bf16).

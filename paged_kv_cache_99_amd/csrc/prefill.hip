@@ -1,11 +1,349 @@
-// prefill.hip -- paged causal attention of prefill chunks (MFMA). Not yet implemented.
+// prefill.hip -- paged causal attention of prefill chunks on the gfx950 matrix cores (MFMA).
+//
+// What it computes: sequence s owns query rows cu_q_lens[s] .. cu_q_lens[s+1]-1, its last q_len
+// positions; row i at position p = seq_lens[s] - q_len + i attends keys 0..p (lecture 32
+// "LLM 在线推理两阶段" §5.4 chunked prefill: a chunk sees the cached context and the earlier part of
+// itself; §1.1 causal order; §3.1 softmax(QK^T/sqrt(d))V; §3.4 GQA groups). Keys are read through
+// the block table (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", Attention 计算时的 Block 映射) and
+// consumed tile by tile with a running max and sum (devpress.csdn.net/amd vLLM overview §9 (3)(4):
+// query and key/value tiling with online softmax).
+//
+// Tiling. A workgroup of 4 waves owns 128 (query row, query head) pairs of one kv-head group: the
+// GK heads that share the kv head, for 128/GK consecutive rows, so each K/V tile staged in LDS serves
+// every head of the group. Per 64-key tile (4 paged blocks):
+//   - K rows go to LDS as they are; V goes to LDS transposed (V^T, one row per dim).
+//   - Each wave computes S^T = K Q^T for its 32 pairs with v_mfma_f32_32x32x16 (A = 32 keys x 16
+//     dims from LDS, B = Q^T held in registers for the whole kernel).
+//   - Online softmax in the accumulator layout: lane l holds column l%32 (one pair) and 16 keys per
+//     32-key tile; the two lanes of a column exchange the maximum once per tile.
+//   - O^T += V^T P^T, again 32x32x16 MFMAs, where P^T is the softmax tile packed to 16 bits straight
+//     from the S^T accumulators (no LDS round trip). The accumulator gives lane half h the keys
+//     {4h..4h+3, 8+4h..8+4h+3} of each 16-key step while the B operand expects slots 8h..8h+7; V^T is
+//     therefore written to LDS with the two middle groups of 4 keys of every 16 swapped, which puts
+//     key and probability on the same slot. The sum over keys is unchanged.
+// The causal mask is applied only on tiles that reach past the workgroup's first position; key rows
+// beyond the context are zero-filled so no stale bits (NaN) reach the MFMAs.
+#include <math.h>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
+namespace {
 
-bool prefill_supported(int32_t, int32_t) { return false; }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-hipError_t launch_prefill(const PrefillLaunch &, hipStream_t) { return hipErrorNotSupported; }
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma32(const uint4 &a, const uint4 &b, const f32x16 &c)
+{
+    if constexpr (BF) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+struct PrefillParams {
+    const uint16_t *__restrict__ query;
+    const uint16_t *__restrict__ k_cache;
+    const uint16_t *__restrict__ v_cache;
+    const int32_t *__restrict__ block_tables;
+    const int32_t *__restrict__ seq_lens;
+    const int32_t *__restrict__ cu_q_lens;
+    uint16_t *__restrict__ out;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t num_blocks;
+    int32_t n_sub;
+    int32_t row_tiles;
+    int32_t n_items;
+    int32_t total_q;
+    float scale_log2;
+};
+
+constexpr int kThreads = 256;
+constexpr int kKeys = 64;  // keys per tile
+
+// In-tile key index -> V^T column: swap bits 2 and 3 (see the tiling note above).
+__device__ __forceinline__ int vt_column(int k)
+{
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <bool BF, int D, int GK>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
+{
+    constexpr int R = 128 / GK;                 // query rows per workgroup
+    constexpr int DC = D / 16;                  // k-steps of S^T = K Q^T
+    constexpr int DT = D / 32;                  // 32-dim tiles of O^T
+    constexpr int KPITCH = D + 8;               // K row pitch in LDS (words): +16 bytes
+    constexpr int VPITCH = kKeys + 8;           // V^T row pitch in LDS (words): +16 bytes
+    constexpr int CPR = D / 8;                  // 16-byte pieces per key row
+    constexpr int NPASS = kKeys * CPR / kThreads;
+    __shared__ __align__(16) uint16_t k_lds[kKeys * KPITCH];
+    __shared__ __align__(16) uint16_t vt_lds[D * VPITCH];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hh = lane >> 5;
+
+    const int item = xcd_logical_id(blockIdx.x, gridDim.x);
+    if (item >= p.n_items)
+        return;
+    int rest = item;
+    const int tile_r = rest % p.row_tiles;
+    rest /= p.row_tiles;
+    const int sub = rest % p.n_sub;
+    rest /= p.n_sub;
+    const int kvh = rest % p.num_kv_heads;
+    const int seq = rest / p.num_kv_heads;
+
+    // offsets are clamped to [0, total_q] so that no index contents can reach outside the arrays
+    const int q0 = min(max(p.cu_q_lens[seq], 0), p.total_q);
+    const int q_len = min(max(p.cu_q_lens[seq + 1], q0), p.total_q) - q0;
+    const int row_base = tile_r * R;
+    if (row_base >= q_len)
+        return;
+    const int L = min(max(p.seq_lens[seq], 0), p.max_blocks * kBlock);
+    const int first_pos = L - q_len;  // position of the chunk's row 0
+
+    // this lane's (row, head) pair: column n of the wave's S^T / O^T tiles
+    const int pair = wave * 32 + n;
+    const int row = row_base + pair / GK;
+    const int head = (kvh * p.n_sub + sub) * GK + pair % GK;
+    const bool row_ok = row < q_len;
+    const int pos = row_ok ? first_pos + row : -1;  // attends keys 0..pos
+
+    uint4 qv[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+        qv[c] = row_ok ? *(const uint4 *)(p.query +
+                                          ((size_t)(q0 + row) * p.num_q_heads + head) * D +
+                                          c * 16 + hh * 8)
+                       : make_uint4(0, 0, 0, 0);
+
+    const int last_row = min(row_base + R, q_len) - 1;
+    const int key_end = max(0, min(L, first_pos + last_row + 1));
+    const int n_tiles = (key_end + kKeys - 1) / kKeys;
+    const int unmasked_below = first_pos + row_base;  // every row of the group sees keys <= this
+    const bool ragged_rows = row_base + R > q_len;
+
+    const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
+    const size_t blk_stride = (size_t)p.num_kv_heads * kBlock * D;
+
+    uint4 kst[NPASS], vst[NPASS];
+    auto gload = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < NPASS; ++i) {
+            const int c = i * kThreads + tid;
+            const int kk = c / CPR, dc = c % CPR;
+            const int key = t * kKeys + kk;
+            uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+            if (key < L) {
+                const int blk = table[key / kBlock];
+                if ((unsigned)blk < (unsigned)p.num_blocks) {
+                    const size_t off = (size_t)blk * blk_stride +
+                                       ((size_t)kvh * kBlock + (key % kBlock)) * D + dc * 8;
+                    kx = *(const uint4 *)(p.k_cache + off);
+                    vx = *(const uint4 *)(p.v_cache + off);
+                }
+            }
+            kst[i] = kx;
+            vst[i] = vx;
+        }
+    };
+    auto swrite = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPASS; ++i) {
+            const int c = i * kThreads + tid;
+            const int kk = c / CPR, dc = c % CPR;
+            *(uint4 *)(k_lds + kk * KPITCH + dc * 8) = kst[i];
+            uint16_t *col = vt_lds + (dc * 8) * VPITCH + vt_column(kk);
+            const uint32_t wv[4] = {vst[i].x, vst[i].y, vst[i].z, vst[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                col[(2 * e) * VPITCH] = (uint16_t)(wv[e] & 0xffffu);
+                col[(2 * e + 1) * VPITCH] = (uint16_t)(wv[e] >> 16);
+            }
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            o[dt][v] = 0.0f;
+
+    if (n_tiles > 0)
+        gload(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();  // every wave is done with the previous tile
+        swrite();
+        __syncthreads();
+        if (t + 1 < n_tiles)
+            gload(t + 1);  // lands while this tile is computed
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                s[kt][v] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const uint4 a = *(const uint4 *)(k_lds + (kt * 32 + n) * KPITCH + c * 16 + hh * 8);
+                s[kt] = mfma32<BF>(a, qv[c], s[kt]);
+            }
+        }
+
+        const int k0 = t * kKeys;
+        const bool need_mask = ragged_rows || k0 + kKeys - 1 > unmasked_below;
+        if (need_mask) {
+            const int last = pos - k0 - 4 * hh;  // key index 8*(v/4) + v%4 + 32*kt must be <= last
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    s[kt][v] = kt * 32 + 8 * (v >> 2) + (v & 3) <= last ? s[kt][v] : -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                mx = fmaxf(mx, s[kt][v]);
+        mx = fmaxf(mx, xor_shfl(mx, 32)) * p.scale_log2;  // scale > 0 keeps the order
+        const float mn = fmaxf(m_run, mx);
+        const float ms = mn == -INFINITY ? 0.0f : mn;
+        const float alpha = fast_exp2(m_run - ms);
+        float psum = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[kt][v] = fast_exp2(fmaf(s[kt][v], p.scale_log2, -ms));
+                psum += s[kt][v];
+            }
+        l_run = l_run * alpha + psum;
+        m_run = mn;
+        if (!__all(alpha == 1.0f)) {  // some lane's running max moved: rescale its accumulators
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    o[dt][v] *= alpha;
+        }
+
+        // P^T operands. In bfloat16 a probability keeps 8 significant bits, which on a few
+        // dominant keys costs up to 2^-9 of the output's spread; bf16 P is therefore split into
+        // hi + lo parts (both bf16, hi = round(p), lo = round(p - hi)) and both are multiplied, so
+        // P enters the float32 accumulation with ~16 significant bits. fp16 keeps 11 bits: one part.
+        uint4 pb[4], pl[4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int kt = c4 >> 1, b = 8 * (c4 & 1);
+            uint32_t *hw = &pb[c4].x, *lw = &pl[c4].x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = s[kt][b + 2 * e], p1 = s[kt][b + 2 * e + 1];
+                hw[e] = pack2<BF>(p0, p1);
+                if constexpr (BF)
+                    lw[e] = pack2<BF>(p0 - lo_f32<BF>(hw[e]), p1 - hi_f32<BF>(hw[e]));
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const uint4 a = *(const uint4 *)(vt_lds + (dt * 32 + n) * VPITCH + c4 * 16 + hh * 8);
+                o[dt] = mfma32<BF>(a, pb[c4], o[dt]);
+                if constexpr (BF)
+                    o[dt] = mfma32<BF>(a, pl[c4], o[dt]);
+            }
+    }
+
+    l_run += xor_shfl(l_run, 32);
+    if (!row_ok)
+        return;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    uint16_t *dst = p.out + ((size_t)(q0 + row) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint2 w;
+            w.x = pack2<BF>(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
+            w.y = pack2<BF>(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
+            *(uint2 *)(dst + dt * 32 + 8 * j + 4 * hh) = w;
+        }
+}
+
+template <bool BF, int D, int GK>
+hipError_t launch_typed(const PrefillParams &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((prefill_kernel<BF, D, GK>), dim3(round_up8(p.n_items)), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <bool BF, int D>
+hipError_t launch_gk(int gk, const PrefillParams &p, hipStream_t stream)
+{
+    switch (gk) {
+    case 8: return launch_typed<BF, D, 8>(p, stream);
+    case 4: return launch_typed<BF, D, 4>(p, stream);
+    case 2: return launch_typed<BF, D, 2>(p, stream);
+    default: return launch_typed<BF, D, 1>(p, stream);
+    }
+}
+
+}  // namespace
+
+bool prefill_supported(int32_t head_dim, int32_t group)
+{
+    return (head_dim == 64 || head_dim == 128) && group >= 1;
+}
+
+hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
+{
+    if (d.num_seqs == 0 || d.total_q == 0 || d.max_q_len == 0)
+        return hipSuccess;
+    const int group = d.num_q_heads / d.c.num_kv_heads;
+    const int gk = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    PrefillParams p;
+    p.query = (const uint16_t *)d.query;
+    p.k_cache = (const uint16_t *)d.k_cache;
+    p.v_cache = (const uint16_t *)d.v_cache;
+    p.block_tables = d.block_tables;
+    p.seq_lens = d.seq_lens;
+    p.cu_q_lens = d.cu_q_lens;
+    p.out = (uint16_t *)d.out;
+    p.max_blocks = d.max_blocks;
+    p.num_seqs = d.num_seqs;
+    p.num_kv_heads = d.c.num_kv_heads;
+    p.num_q_heads = d.num_q_heads;
+    p.num_blocks = d.c.num_blocks;
+    p.n_sub = group / gk;
+    p.total_q = d.total_q;
+    const int rows_per_wg = 128 / gk;
+    p.row_tiles = (d.max_q_len + rows_per_wg - 1) / rows_per_wg;
+    const int64_t items = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.row_tiles;
+    if (items > 0x7ffffff0)
+        return hipErrorInvalidValue;
+    p.n_items = (int32_t)items;
+    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    if (d.c.bf16)
+        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, stream)
+                                  : launch_gk<true, 128>(gk, p, stream);
+    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, stream)
+                              : launch_gk<false, 128>(gk, p, stream);
+}
 
 }  // namespace pa

@@ -175,3 +175,82 @@ def test_decode_rejects_small_workspace_without_launching():
         binding.decode(g.dec_out, g.dec_query, g.k_cache, g.v_cache, g.dec_tables, g.dec_lens,
                        g.max_seq_len, w.scale, 512, g.workspace[:16])
     assert e.value.status == binding.PA_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------------------- prefill chunk
+def sample_rows(w, n_rows, H_q, seed):
+    """(row, head) pairs: the first and last row of every chunk, the rows at each 64-key tile edge
+    of the first chunk, and random rows; every head."""
+    cu = w.cu_q_lens
+    rows = set()
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            rows.update([a, b - 1, min(b - 1, a + 1)])
+            rows.update(range(a, b, 64))
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, int(cu[-1]), size=n_rows).tolist())
+    rows = sorted(rows)
+    return np.array([(r, h) for r in rows for h in range(H_q)], np.int32), rows
+
+
+def test_prefill_mixed_batch_chunk_sampled():
+    """The 1856-row chunk of the mixed 2048-token step at full size: the GPU runs the whole chunk,
+    the oracle checks a sample of rows (all heads) that covers both ends and every tile edge."""
+    w = workload("chunked_prefill_mixed")
+    g = run_on_gpu(w, stages=("copy", "scatter", "decode", "prefill"))
+    kc, vc = oracle_pool_after_step(w)
+    pairs, rows = sample_rows(w, 24, w.H_q, seed=5)
+    t = time.time()
+    ref = oracle_prefill(w, kc, vc, rows=pairs)
+    print(f"[parity] oracle prefill sample of {len(rows)} rows: {time.time() - t:.1f}s", flush=True)
+    got = words_from_device(g.pre_out)[pairs[:, 0], pairs[:, 1]]
+    assert_attention_close(got, ref, w.dtype, "prefill chunk (mixed batch, sampled rows)")
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (16, 4), (32, 2), (6, 2), (12, 12)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_chunks_full(H_q, H_kv, D, dtype):
+    """Several ragged chunks over contexts of every alignment, compared row by row in full."""
+    lens = [300, 77, 129, 16, 1, 200]
+    q_lens = [150, 77, 64, 16, 1, 3]   # mid-prompt chunk, whole prompts, tile- and block-sized
+    w = poisoned(W.build(lens, H_q, H_kv, D, dtype, seed=100 + H_q + D, n_decode=0, q_lens=q_lens))
+    g = run_on_gpu(w, stages=("scatter", "prefill"))
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.pre_out), oracle_prefill(w, kc, vc), dtype,
+                           f"prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}", strict=False)
+
+
+def test_prefill_long_chunk_gqa_full():
+    """A 700-row chunk of a 2500-token sequence plus a whole 333-token prompt, 32 q / 8 kv heads:
+    every row. The prompt's first rows see a handful of keys (outputs near 1): element-wise gate."""
+    w = poisoned(W.build([2500, 333], 32, 8, 128, "bf16", seed=120, n_decode=0, q_lens=[700, 333]))
+    g = run_on_gpu(w, stages=("scatter", "prefill"))
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.pre_out), oracle_prefill(w, kc, vc), w.dtype,
+                           "prefill long chunk", strict=False)
+
+
+def test_prefill_single_row_chunks_match_decode():
+    """A chunk of one row is a decode step: both kernels agree within the gate of each."""
+    lens = [5, 600, 1500]
+    w = W.build(lens, 16, 4, 128, "f16", seed=121, n_decode=0, q_lens=[1, 1, 1])
+    g = run_on_gpu(w, stages=("scatter", "prefill"))
+    kc, vc = oracle_pool_after_step(w)
+    ref = oracle_prefill(w, kc, vc)
+    assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "prefill q_len 1")
+    wd = dataclasses.replace(w, n_decode=3, query_decode=w.query_prefill,
+                             cu_q_lens=np.zeros(1, np.int32),
+                             query_prefill=np.zeros((0, 16, 128), np.uint16))
+    gd = run_on_gpu(wd, stages=("scatter", "decode"))
+    assert_attention_close(words_from_device(gd.dec_out), ref, w.dtype, "decode vs prefill rows")
+
+
+def test_prefill_is_deterministic():
+    w = W.build([900, 260], 32, 8, 128, "bf16", seed=122, n_decode=0, q_lens=[300, 260])
+    g = run_on_gpu(w, stages=("scatter", "prefill"))
+    first = words_from_device(g.pre_out)
+    g.prefill()
+    torch.cuda.synchronize()
+    assert np.array_equal(first, words_from_device(g.pre_out))
