@@ -113,6 +113,23 @@ def cpu_baseline(w, max_seconds):
             "seconds": round(elapsed, 3)}
 
 
+def calibration_copy(g, pairs):
+    """Copy `pairs` blocks src = 0..pairs-1 -> dst = pairs..2*pairs-1 in both caches (the timed steps
+    are over; the pool contents no longer matter) and report the bytes a perfect copy moves."""
+    import torch
+    from paged_kv_cache_99_amd import binding
+    nb = g.k_cache.shape[0]
+    pairs = min(pairs, nb // 2)
+    mapping = torch.stack([torch.arange(pairs), torch.arange(pairs, 2 * pairs)], 1)
+    mapping = mapping.to(torch.int32).contiguous().to(g.device)
+    torch.cuda.synchronize()
+    binding.copy_blocks(g.k_cache, g.v_cache, mapping)
+    torch.cuda.synchronize()
+    per_cache = pairs * g.k_cache[0].numel() * g.k_cache.element_size()
+    print(f"[bench] calibration copy: {pairs} blocks x 2 caches = {2 * per_cache} bytes read and "
+          f"{2 * per_cache} bytes written", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +139,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="decode partition size override")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
+                    help="after timing, copy PAIRS whole blocks with pa_copy_blocks (a plain copy of "
+                         "known size, for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -171,6 +191,9 @@ def main():
     ms_per_step = wall * 1e3 / K
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if g.n_decode else 0.0
     pre_ms = float(np.mean([a.elapsed_time(b) for a, b in evp])) if has_prefill else 0.0
+
+    if args.copy_calibration:
+        calibration_copy(g, args.copy_calibration)
 
     d_bytes = decode_bytes(w)
     p_bytes, p_flops = prefill_bytes_flops(w)

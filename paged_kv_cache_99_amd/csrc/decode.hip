@@ -109,8 +109,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
             const uint16_t *vp = p.v_cache + blk * block_stride + tile_off;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                kk[i] = *(const uint4 *)(kp + i * ROWS * D);
-                vv[i] = *(const uint4 *)(vp + i * ROWS * D);
+                kk[i] = load_nt(kp + i * ROWS * D);
+                vv[i] = load_nt(vp + i * ROWS * D);
             }
         };
 
