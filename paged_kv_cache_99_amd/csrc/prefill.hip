@@ -11,18 +11,23 @@
 // Tiling. A workgroup of 4 waves owns 128 (query row, query head) pairs of one kv-head group: the
 // GK heads that share the kv head, for 128/GK consecutive rows, so each K/V tile staged in LDS serves
 // every head of the group. Per 64-key tile (4 paged blocks):
-//   - K rows go to LDS as they are; V goes to LDS transposed (V^T, one row per dim).
+//   - K and V rows go to LDS untouched, straight from HBM (global_load_lds_dwordx4: no staging
+//     registers), into one of two buffers while the other is computed. Rows are stored without
+//     padding; the 16-byte pieces of row r are XOR-swizzled (piece c at c ^ swz(r)) so that the
+//     column reads below hit distinct banks.
 //   - Each wave computes S^T = K Q^T for its 32 pairs with v_mfma_f32_32x32x16 (A = 32 keys x 16
-//     dims from LDS, B = Q^T held in registers for the whole kernel).
+//     dims, one ds_read_b128 per lane; B = Q^T held in registers for the whole kernel).
 //   - Online softmax in the accumulator layout: lane l holds column l%32 (one pair) and 16 keys per
 //     32-key tile; the two lanes of a column exchange the maximum once per tile.
-//   - O^T += V^T P^T, again 32x32x16 MFMAs, where P^T is the softmax tile packed to 16 bits straight
-//     from the S^T accumulators (no LDS round trip). The accumulator gives lane half h the keys
-//     {4h..4h+3, 8+4h..8+4h+3} of each 16-key step while the B operand expects slots 8h..8h+7; V^T is
-//     therefore written to LDS with the two middle groups of 4 keys of every 16 swapped, which puts
-//     key and probability on the same slot. The sum over keys is unchanged.
-// The causal mask is applied only on tiles that reach past the workgroup's first position; key rows
-// beyond the context are zero-filled so no stale bits (NaN) reach the MFMAs.
+//   - O^T += V^T P^T, again 32x32x16 MFMAs. P^T is the softmax tile packed to 16 bits straight from
+//     the S^T accumulators, whose layout gives lane half h the keys {4h..4h+3, 8+4h..8+4h+3} of each
+//     16-key step. The V^T operand comes from row-major V with ds_read_b64_tr_b16, which hands lane j
+//     of a 16-lane group element j%4 of the 8 bytes addressed by lane 4k + j/4 (k = 0..3): each lane
+//     addresses 4 dims of one key row, and the key rows are chosen so that key and probability meet on
+//     the same MFMA k-slot.
+// The causal mask is applied only on tiles that reach past the workgroup's first position. Keys
+// beyond the context are never loaded; LDS starts zeroed, so such slots hold finite stale values that
+// meet zero probabilities (no NaN reaches an MFMA).
 #include <math.h>
 
 #include "pa_device.h"
@@ -70,24 +75,33 @@ struct PrefillParams {
 constexpr int kThreads = 256;
 constexpr int kKeys = 64;  // keys per tile
 
-// In-tile key index -> V^T column: swap bits 2 and 3 (see the tiling note above).
-__device__ __forceinline__ int vt_column(int k)
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// XOR swizzle of the 16-byte pieces of LDS row r (D = 128: 16 pieces; D = 64: 8 pieces). Chosen so
+// that 16 consecutive rows read at one column (the K operand) and 4 consecutive rows read at 2
+// adjacent pieces (the transposed V operand) fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r)
 {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+    if constexpr (D == 128)
+        return 2 * (r & 7) + ((r >> 3) & 1);
+    else
+        return (r >> 1) & 7;
 }
 
 template <bool BF, int D, int GK>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
 {
-    constexpr int R = 128 / GK;                 // query rows per workgroup
-    constexpr int DC = D / 16;                  // k-steps of S^T = K Q^T
-    constexpr int DT = D / 32;                  // 32-dim tiles of O^T
-    constexpr int KPITCH = D + 8;               // K row pitch in LDS (words): +16 bytes
-    constexpr int VPITCH = kKeys + 8;           // V^T row pitch in LDS (words): +16 bytes
-    constexpr int CPR = D / 8;                  // 16-byte pieces per key row
-    constexpr int NPASS = kKeys * CPR / kThreads;
-    __shared__ __align__(16) uint16_t k_lds[kKeys * KPITCH];
-    __shared__ __align__(16) uint16_t vt_lds[D * VPITCH];
+    constexpr int R = 128 / GK;                     // query rows per workgroup
+    constexpr int DC = D / 16;                      // k-steps of S^T = K Q^T
+    constexpr int DT = D / 32;                      // 32-dim tiles of O^T
+    constexpr int ROWB = D * 2;                     // bytes per LDS row (no padding)
+    constexpr int CPR = D / 8;                      // 16-byte pieces per row
+    constexpr int TILEB = kKeys * ROWB;             // bytes of one K or V tile
+    constexpr int NLOAD = TILEB / (kThreads * 16);  // direct-to-LDS loads per thread per tile
+    __shared__ __align__(16) uint8_t smem[2][2][TILEB];  // [buffer][0 = K, 1 = V]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, hh = lane >> 5;
@@ -136,39 +150,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
     const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
     const size_t blk_stride = (size_t)p.num_kv_heads * kBlock * D;
 
-    uint4 kst[NPASS], vst[NPASS];
-    auto gload = [&](int t) {
+    // LDS starts zeroed: slots of keys that are never loaded then hold finite values
 #pragma unroll
-        for (int i = 0; i < NPASS; ++i) {
-            const int c = i * kThreads + tid;
-            const int kk = c / CPR, dc = c % CPR;
-            const int key = t * kKeys + kk;
-            uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+    for (int i = tid; i < 4 * TILEB / 16; i += kThreads)
+        ((uint4 *)&smem[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    // Direct-to-LDS loads of tile t into buffer b: load j of the wave covers LDS bytes
+    // [(j*4 + wave) * 1 KiB, +1 KiB); lane i writes the 16-byte piece at offset 16*i of that range.
+    auto issue = [&](int t, int b) {
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) {
+            const int u = j * kThreads + tid;        // 16-byte slot in the tile
+            const int r = u / CPR;                   // key row in the tile
+            const int c = (u % CPR) ^ swz<D>(r);     // global piece stored at this slot
+            const int key = t * kKeys + r;
             if (key < L) {
                 const int blk = table[key / kBlock];
                 if ((unsigned)blk < (unsigned)p.num_blocks) {
                     const size_t off = (size_t)blk * blk_stride +
-                                       ((size_t)kvh * kBlock + (key % kBlock)) * D + dc * 8;
-                    kx = *(const uint4 *)(p.k_cache + off);
-                    vx = *(const uint4 *)(p.v_cache + off);
+                                       ((size_t)kvh * kBlock + (key % kBlock)) * D + c * 8;
+                    const int lds_off = (j * kThreads + wave * kWave) * 16;
+                    __builtin_amdgcn_global_load_lds(p.k_cache + off, (lds_void *)(&smem[b][0][lds_off]),
+                                                     16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(p.v_cache + off, (lds_void *)(&smem[b][1][lds_off]),
+                                                     16, 0, 0);
                 }
-            }
-            kst[i] = kx;
-            vst[i] = vx;
-        }
-    };
-    auto swrite = [&]() {
-#pragma unroll
-        for (int i = 0; i < NPASS; ++i) {
-            const int c = i * kThreads + tid;
-            const int kk = c / CPR, dc = c % CPR;
-            *(uint4 *)(k_lds + kk * KPITCH + dc * 8) = kst[i];
-            uint16_t *col = vt_lds + (dc * 8) * VPITCH + vt_column(kk);
-            const uint32_t wv[4] = {vst[i].x, vst[i].y, vst[i].z, vst[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                col[(2 * e) * VPITCH] = (uint16_t)(wv[e] & 0xffffu);
-                col[(2 * e + 1) * VPITCH] = (uint16_t)(wv[e] >> 16);
             }
         }
     };
@@ -181,14 +188,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
         for (int v = 0; v < 16; ++v)
             o[dt][v] = 0.0f;
 
+    // lane-constant parts of the LDS read addresses
+    const int k_sw = swz<D>(n);                      // K operand: rows kt*32 + n share swz(n)
+    const int g16 = lane >> 4, sl = lane & 15;       // transposed V reads: 16-lane group, source lane
+    const int v_k = sl >> 2, v_q = sl & 3;           // source lane 4k + q: key row k, dims 4q..4q+3
+    const int v_half = g16 >> 1;                     // lane half h of the destination lanes
+    const int v_dim = (g16 & 1) * 16 + 4 * v_q;      // dim within a 32-dim tile
+
     if (n_tiles > 0)
-        gload(0);
+        issue(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();  // every wave is done with the previous tile
-        swrite();
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed in LDS
+        __syncthreads();                // everyone's have; everyone is done with tile t-1
         if (t + 1 < n_tiles)
-            gload(t + 1);  // lands while this tile is computed
+            issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
+        const uint8_t *kb = &smem[t & 1][0][0];
+        const uint8_t *vb = &smem[t & 1][1][0];
 
         f32x16 s[2];
 #pragma unroll
@@ -196,9 +211,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 s[kt][v] = 0.0f;
+            const uint8_t *krow = kb + (kt * 32 + n) * ROWB;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const uint4 a = *(const uint4 *)(k_lds + (kt * 32 + n) * KPITCH + c * 16 + hh * 8);
+                const uint4 a = *(const uint4 *)(krow + (((2 * c + hh) ^ k_sw) * 16));
                 s[kt] = mfma32<BF>(a, qv[c], s[kt]);
             }
         }
@@ -259,14 +275,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p)
             }
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int c4 = 0; c4 < 4; ++c4) {
+            // destination slots 0..3 hold keys 16*c4 + 4h + (0..3), slots 4..7 keys 16*c4 + 8 + 4h + (0..3)
+            const int r1 = c4 * 16 + 4 * v_half + v_k, r2 = r1 + 8;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const uint4 a = *(const uint4 *)(vt_lds + (dt * 32 + n) * VPITCH + c4 * 16 + hh * 8);
+            for (int dt = 0; dt < DT; ++dt) {
+                const int dim = dt * 32 + v_dim;
+                const int off1 = r1 * ROWB + (((dim >> 3) ^ swz<D>(r1)) << 4) + (dim & 7) * 2;
+                const int off2 = r2 * ROWB + (((dim >> 3) ^ swz<D>(r2)) << 4) + (dim & 7) * 2;
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off1));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off2));
+                uint4 a;
+                a.x = __builtin_bit_cast(uint2, lo4).x;
+                a.y = __builtin_bit_cast(uint2, lo4).y;
+                a.z = __builtin_bit_cast(uint2, hi4).x;
+                a.w = __builtin_bit_cast(uint2, hi4).y;
                 o[dt] = mfma32<BF>(a, pb[c4], o[dt]);
                 if constexpr (BF)
                     o[dt] = mfma32<BF>(a, pl[c4], o[dt]);
             }
+        }
     }
 
     l_run += xor_shfl(l_run, 32);
