@@ -158,27 +158,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
 
     // Direct-to-LDS loads of tile t into buffer b: load j of the wave covers LDS bytes
     // [(j*4 + wave) * 1 KiB, +1 KiB); lane i writes the 16-byte piece at offset 16*i of that range.
+    // Those rows all lie in one paged block, so the block id and the source base are wave-uniform;
+    // the lane's offset inside the (block, kv head) tile -- its row, and the swizzled piece it
+    // stores -- is the same for every tile and every load.
+    // Block ids come from a register window: lane i holds table entry 64*w + i of window w (16
+    // tiles). The next window is fetched one window ahead, so no tile waits on a table read.
+    const int lane_row = lane / CPR;
+    const int lane_piece = lane % CPR;
+    const int n_blocks = (L + kBlock - 1) / kBlock;
+    auto table_window = [&](int w) {
+        const int i = w * kWave + lane;
+        return i < n_blocks ? table[i] : -1;
+    };
+    int win_cur = table_window(0), win_next = table_window(1);
     auto issue = [&](int t, int b) {
+        const bool whole = (t + 1) * kKeys <= L;  // no key of this tile lies past the context
 #pragma unroll
         for (int j = 0; j < NLOAD; ++j) {
-            const int u = j * kThreads + tid;        // 16-byte slot in the tile
-            const int r = u / CPR;                   // key row in the tile
-            const int c = (u % CPR) ^ swz<D>(r);     // global piece stored at this slot
-            const int key = t * kKeys + r;
-            if (key < L) {
-                const int blk = table[key / kBlock];
-                if ((unsigned)blk < (unsigned)p.num_blocks) {
-                    const size_t off = (size_t)blk * blk_stride +
-                                       ((size_t)kvh * kBlock + (key % kBlock)) * D + c * 8;
-                    const int lds_off = (j * kThreads + wave * kWave) * 16;
-                    __builtin_amdgcn_global_load_lds(p.k_cache + off, (lds_void *)(&smem[b][0][lds_off]),
-                                                     16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(p.v_cache + off, (lds_void *)(&smem[b][1][lds_off]),
-                                                     16, 0, 0);
-                }
+            const int first_row = (j * kThreads + wave * kWave) / CPR;  // wave-uniform
+            const int key0 = t * kKeys + first_row;
+            if (key0 >= L)
+                continue;
+            const int bi = (key0 / kBlock) & (kWave - 1);  // slot in the window of tile t
+            const int blk = __builtin_amdgcn_readlane(win_cur, bi);
+            if ((unsigned)blk >= (unsigned)p.num_blocks)
+                continue;
+            const size_t off = (size_t)blk * blk_stride +
+                               ((size_t)kvh * kBlock + (key0 % kBlock) + lane_row) * D +
+                               (lane_piece ^ swz<D>(first_row + lane_row)) * 8;
+            const int lds_off = (j * kThreads + wave * kWave) * 16;
+            if (whole || key0 + lane_row < L) {
+                __builtin_amdgcn_global_load_lds(p.k_cache + off, (lds_void *)(&smem[b][0][lds_off]),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(p.v_cache + off, (lds_void *)(&smem[b][1][lds_off]),
+                                                 16, 0, 0);
             }
         }
     };
+    constexpr int kTilesPerWindow = kWave * kBlock / kKeys;  // 16
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 o[DT];
@@ -200,8 +217,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
     for (int t = 0; t < n_tiles; ++t) {
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed in LDS
         __syncthreads();                // everyone's have; everyone is done with tile t-1
-        if (t + 1 < n_tiles)
+        if (t + 1 < n_tiles) {
+            if ((t + 1) % kTilesPerWindow == 0) {  // tile t+1 opens the next window
+                win_cur = win_next;
+                win_next = table_window((t + 1) / kTilesPerWindow + 1);
+            }
             issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
+        }
         const uint8_t *kb = &smem[t & 1][0][0];
         const uint8_t *vb = &smem[t & 1][1][0];
 
