@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_99_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_99_amd", "csrc", f)
+               for f in ("decode.hip", "pa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_traffic.json")
 
 
@@ -67,9 +68,12 @@ def prefill_bytes_flops(w):
     return kv + 2 * rows * w.H_q * w.D * 2, flops
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(per_launch_algorithmic):
@@ -79,7 +83,7 @@ def committed_traffic(per_launch_algorithmic):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("decode_src_sha256_16") != src_hash(DECODE_SRC):
+    if t.get("decode_src_sha256_16") != src_hash(DECODE_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -139,10 +143,15 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="decode partition size override")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--print-decode-src-hash", action="store_true",
+                    help="print the hash of the decode sources (recorded with counter summaries)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
                     help="after timing, copy PAIRS whole blocks with pa_copy_blocks (a plain copy of "
                          "known size, for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.print_decode_src_hash:
+        print(src_hash(DECODE_SRCS))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path is not sharded across GPUs in this build "
