@@ -233,6 +233,300 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
     }
 }
 
+// ------------------------------------------------------------------ head groups of 4 and 8
+// The kernel above computes every score in all 16 lanes of a token row and repeats the softmax
+// there, once per query head: for GQA groups that redundancy, not HBM, bounds it. Here each
+// (block, kv head) K tile is staged in LDS and re-read in a scoring layout where GK lanes own one
+// token (lane j covers dims [j*D/GK, (j+1)*D/GK) for all GK heads). A transpose-reduce over those
+// GK lanes leaves lane j with the full score of head j, so the exponential and the running sum are
+// computed once per (token, head). The softmax reference point m is wave-uniform per head and
+// moves only when a score exceeds it by more than 2^kLazy (then the accumulators are rescaled): all
+// tokens of a head share one m, so P*V may use any lane layout. Probabilities reach the P*V lanes
+// (the coalesced V layout of the kernel above) through a 16 x GK float buffer in LDS.
+constexpr float kLazy = 8.0f;  // log2 units: partial sums stay below 2^8 times their true scale
+
+// Sum the GK values x[0..GK) of each lane over aligned groups of GK lanes, leaving lane j of a
+// group with the group's total of x[j]. Stage s pairs lanes that differ in bit s of j (for GK = 8,
+// bit 2 via row_half_mirror, which reverses each group of 8): each lane keeps the half of its values
+// selected by that bit and adds the partner's copy of the same half.
+template <int GK>
+__device__ __forceinline__ float transpose_reduce(float (&x)[GK], int j)
+{
+    if constexpr (GK == 8) {
+        const bool b2 = (j >> 2) & 1;
+        float y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float keep = b2 ? x[4 + k] : x[k], send = b2 ? x[k] : x[4 + k];
+            y[k] = keep + dpp_f(send, 2);  // row_half_mirror: lane j <-> 7 - j
+        }
+        const bool b1 = (j >> 1) & 1;
+        float z[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float keep = b1 ? y[2 + k] : y[k], send = b1 ? y[k] : y[2 + k];
+            z[k] = keep + dpp_f(send, 1);  // j <-> j ^ 2
+        }
+        const bool b0 = j & 1;
+        const float keep = b0 ? z[1] : z[0], send = b0 ? z[0] : z[1];
+        return keep + dpp_f(send, 0);  // j <-> j ^ 1
+    } else {
+        static_assert(GK == 4, "groups of 4 or 8");
+        const bool b1 = (j >> 1) & 1;
+        float z[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float keep = b1 ? x[2 + k] : x[k], send = b1 ? x[k] : x[2 + k];
+            z[k] = keep + dpp_f(send, 1);
+        }
+        const bool b0 = j & 1;
+        const float keep = b0 ? z[1] : z[0], send = b0 ? z[0] : z[1];
+        return keep + dpp_f(send, 0);
+    }
+}
+
+// XOR swizzle of the 16-byte pieces of K row `row` in LDS: the coalesced writes fill whole rows;
+// the scoring reads (16 lanes = 16/GK*... rows x pieces) then fall on distinct banks.
+template <int D, int GK>
+__device__ __forceinline__ int kswz(int row)
+{
+    if constexpr (D == 128)
+        return row & (16 / GK - 1);
+    else
+        return (row >> 1) & (8 / GK - 1);
+}
+
+template <bool BF, int D, int GK>
+__global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
+{
+    constexpr int RL = D / 8;            // P*V layout: lanes per token row
+    constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
+    constexpr int NCH = kBlock / ROWS;   // loads per (block, kv head) tile
+    constexpr int TPP = kWave / GK;      // tokens scored per pass
+    constexpr int NPASS = kBlock / TPP;  // passes per block
+    constexpr int CPL = D / GK / 8;      // 16-byte pieces of a K row per scoring lane
+    constexpr int ROWB = D * 2;
+    __shared__ __align__(16) uint8_t k_lds[kBlock * ROWB];
+    __shared__ __align__(16) float p_lds[kBlock * GK];
+
+    const int lane = threadIdx.x;
+    const int r = lane / RL, c = lane % RL;  // P*V layout
+    const int ts = lane / GK, j = lane % GK; // scoring layout: token slot, dim slice = own head
+
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
+    if (unit >= p.n_units)
+        return;
+    const int seq = unit % p.num_seqs;
+    int rest = unit / p.num_seqs;
+    const int part = rest % p.max_parts;
+    rest /= p.max_parts;
+    const int sub = rest % p.n_sub;
+    const int kvh = rest / p.n_sub;
+    const int h0 = (kvh * p.n_sub + sub) * GK;
+
+    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
+    const int t0 = part * p.part_tokens;
+    if (p.split && t0 >= L)
+        return;
+    const int t1 = min(L, t0 + p.part_tokens);
+
+    // queries in the scoring layout: dims [j*D/GK, (j+1)*D/GK) of every head of the group
+    uint4 q[GK][CPL];
+#pragma unroll
+    for (int h = 0; h < GK; ++h)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+            q[h][k] = *(const uint4 *)(p.query + ((size_t)seq * p.num_q_heads + h0 + h) * D +
+                                       (j * CPL + k) * 8);
+
+    float m_own = -INFINITY, l_own = 0.0f;  // reference point and partial sum of head j
+    float acc[GK][8];
+#pragma unroll
+    for (int h = 0; h < GK; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[h][e] = 0.0f;
+
+    const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
+    const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D;
+    const size_t tile_off = (size_t)kvh * kBlock * D + lane * 8;
+
+    for (int bb = t0 / kBlock; bb * kBlock < t1; bb += kWave) {
+        const int nb = min(kWave, (t1 - bb * kBlock + kBlock - 1) / kBlock);
+        const int my_blk = lane < nb ? table[bb + lane] : 0;
+
+        auto load = [&](int k, uint4(&kk)[NCH], uint4(&vv)[NCH]) {
+            int blk = __builtin_amdgcn_readlane(my_blk, k);
+            blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+            const uint16_t *kp = p.k_cache + blk * block_stride + tile_off;
+            const uint16_t *vp = p.v_cache + blk * block_stride + tile_off;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                kk[i] = load_nt(kp + i * ROWS * D);
+                vv[i] = load_nt(vp + i * ROWS * D);
+            }
+        };
+
+        auto consume = [&](int k, const uint4(&kk)[NCH], uint4(&vv)[NCH]) {
+            const int base = (bb + k) * kBlock;
+            const int raw = __builtin_amdgcn_readlane(my_blk, k);
+            const bool good_blk = (unsigned)raw < (unsigned)p.num_blocks;
+            const bool whole = good_blk && base + kBlock <= t1;
+
+            // stage the K tile: row ROWS*i + r, piece c (swizzled)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int row = ROWS * i + r;
+                *(uint4 *)(k_lds + row * ROWB + ((c ^ kswz<D, GK>(row)) << 4)) = kk[i];
+            }
+
+            // scores of head j for tokens ts + TPP*pass
+            float sc[NPASS];
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const int row = ps * TPP + ts;
+                uint4 kr[CPL];
+#pragma unroll
+                for (int k2 = 0; k2 < CPL; ++k2)
+                    kr[k2] = *(const uint4 *)(k_lds + row * ROWB +
+                                              (((j * CPL + k2) ^ kswz<D, GK>(row)) << 4));
+                float part_sum[GK];
+#pragma unroll
+                for (int h = 0; h < GK; ++h) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int k2 = 0; k2 < CPL; ++k2)
+                        a += dot8<BF>(q[h][k2], kr[k2]);
+                    part_sum[h] = a;
+                }
+                float x = transpose_reduce<GK>(part_sum, j) * p.scale_log2;
+                if (!whole && !(good_blk && base + row < t1))
+                    x = -INFINITY;
+                sc[ps] = x;
+            }
+
+            // lazy reference point: move it (and rescale) only when a score passes it by 2^kLazy
+            float over = sc[0] - m_own;
+#pragma unroll
+            for (int ps = 1; ps < NPASS; ++ps)
+                over = fmaxf(over, sc[ps] - m_own);
+            if (!__all(!(over > kLazy))) {
+                float mx = sc[0];
+#pragma unroll
+                for (int ps = 1; ps < NPASS; ++ps)
+                    mx = fmaxf(mx, sc[ps]);
+#pragma unroll
+                for (int off = GK; off < kWave; off <<= 1)
+                    mx = fmaxf(mx, xor_shfl(mx, off));  // max over the token slots of head j
+                const float mn = fmaxf(m_own, mx);
+                const float alpha = fast_exp2(m_own - mn);  // 0 on the first block
+                m_own = mn;
+                l_own *= alpha;
+#pragma unroll
+                for (int h = 0; h < GK; ++h) {
+                    const float ah = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(alpha), h));  // lane h has head h
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[h][e] *= ah;
+                }
+            }
+
+            // probabilities: own head, own tokens; to LDS as p[token][head]
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const float pr = fast_exp2(sc[ps] - m_own);  // masked: exp2(-inf) = 0
+                l_own += pr;
+                p_lds[(ps * TPP + ts) * GK + j] = pr;
+            }
+
+            // P*V in the coalesced layout: lane (r, c) holds tokens ROWS*i + r, dims c*8..c*8+7
+            if (!whole) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const bool ok = good_blk && base + ROWS * i + r < t1;
+                    vv[i] = ok ? vv[i] : make_uint4(0, 0, 0, 0);  // masked rows may hold NaN bits
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                float pv[GK];
+#pragma unroll
+                for (int h4 = 0; h4 < GK; h4 += 4) {
+                    const float4 t = *(const float4 *)(p_lds + (ROWS * i + r) * GK + h4);
+                    pv[h4] = t.x;
+                    pv[h4 + 1] = t.y;
+                    pv[h4 + 2] = t.z;
+                    pv[h4 + 3] = t.w;
+                }
+                const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v0 = lo_f32<BF>(w[e]), v1 = hi_f32<BF>(w[e]);
+#pragma unroll
+                    for (int h = 0; h < GK; ++h) {
+                        acc[h][2 * e] += pv[h] * v0;
+                        acc[h][2 * e + 1] += pv[h] * v1;
+                    }
+                }
+            }
+        };
+
+        uint4 ka[NCH], va[NCH], kn[NCH], vn[NCH];
+        load(0, ka, va);
+        for (int k = 0; k < nb; ++k) {
+            if (k + 1 < nb)
+                load(k + 1, kn, vn);
+            consume(k, ka, va);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                ka[i] = kn[i];
+                va[i] = vn[i];
+            }
+        }
+    }
+
+    // totals: l of head j over its token slots; acc over the row classes (one m per head: no
+    // rescaling needed)
+#pragma unroll
+    for (int off = GK; off < kWave; off <<= 1)
+        l_own += xor_shfl(l_own, off);
+#pragma unroll
+    for (int h = 0; h < GK; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = acc[h][e];
+#pragma unroll
+            for (int off = RL; off < kWave; off <<= 1)
+                a += xor_shfl(a, off);
+            acc[h][e] = a;
+        }
+
+#pragma unroll
+    for (int h = 0; h < GK; ++h) {
+        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_own), h));
+        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_own), h));
+        if (lane < RL) {
+            const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
+            if (p.split) {
+                float *wa = p.ws_acc + (row * p.max_parts + part) * D + lane * 8;
+                *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                if (lane == 0)
+                    *(float2 *)(p.ws_ml + (row * p.max_parts + part) * 2) = make_float2(mh, lh);
+            } else {
+                const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+                uint4 o;
+                o.x = pack2<BF>(acc[h][0] * inv, acc[h][1] * inv);
+                o.y = pack2<BF>(acc[h][2] * inv, acc[h][3] * inv);
+                o.z = pack2<BF>(acc[h][4] * inv, acc[h][5] * inv);
+                o.w = pack2<BF>(acc[h][6] * inv, acc[h][7] * inv);
+                *(uint4 *)(p.out + row * D + lane * 8) = o;
+            }
+        }
+    }
+}
+
 // One wave per (sequence, query head): rescale every part to the common maximum M,
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 template <bool BF, int D>
@@ -280,8 +574,11 @@ template <bool BF, int D, int GK>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream)
 {
     const int grid = round_up8(p.n_units);
-    hipLaunchKernelGGL((decode_partition_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0, stream,
-                       p);
+    if constexpr (GK >= 4)
+        hipLaunchKernelGGL((decode_gqa_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_partition_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0,
+                           stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.split)
         return e;
