@@ -17,6 +17,8 @@ Prints ONE JSON line:
 
 Algorithmic bytes (what the method must move, per stage):
   decode   sum_s L_s * 2 * H_kv * D * 2 (each valid token's K and V row once) + query + output;
+           with shared-prefix groups read once, a group's common blocks count once for the group
+           (the per-sequence count is reported as decode_logical_bytes);
   scatter  T * H_kv * D * 2 * 2 read + the same written;
   copy     pairs * 2 caches * (16 * H_kv * D * 2) read + the same written;
   prefill  K/V rows of the context once + query + output (its roofline is MFMA: 4*D*H_q*sum(p+1)).
@@ -44,6 +46,20 @@ def decode_bytes(w):
     nd = w.n_decode
     kv = int(np.sum(w.seq_lens[:nd].astype(np.int64))) * 2 * w.H_kv * w.D * 2
     return kv + 2 * nd * w.H_q * w.D * 2
+
+
+def decode_unique_bytes(w):
+    """Bytes when every group's common blocks are read once (shared-prefix workloads)."""
+    meta = getattr(w, "meta", {}) or {}
+    if "group_starts" not in meta:
+        return decode_bytes(w)
+    nd = w.n_decode
+    gs = np.asarray(meta["group_starts"])
+    pre = np.asarray(meta["shared_prefix"], np.int64)[:nd]
+    lens = w.seq_lens[:nd].astype(np.int64)
+    shared = int(sum(pre[gs[g]] for g in range(len(gs) - 1) if gs[g + 1] > gs[g]))
+    tokens = shared + int(np.sum(lens - pre))
+    return tokens * 2 * w.H_kv * w.D * 2 + 2 * nd * w.H_q * w.D * 2
 
 
 def scatter_bytes(w):
@@ -143,6 +159,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="decode partition size override")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode shared-prefix groups per sequence instead of reading each "
+                         "group's common blocks once")
     ap.add_argument("--print-decode-src-hash", action="store_true",
                     help="print the hash of the decode sources (recorded with counter summaries)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
@@ -170,7 +189,7 @@ def main():
     w = W.named(args.workload)
     print(f"[bench] workload {w.name}: {len(w.seq_lens)} sequences, pool {w.num_blocks} blocks, "
           f"built in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    g = GpuStep(w, partition_size=args.partition)
+    g = GpuStep(w, partition_size=args.partition, shared_prefix=not args.no_shared_prefix)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -205,10 +224,11 @@ def main():
         calibration_copy(g, args.copy_calibration)
 
     d_bytes = decode_bytes(w)
+    u_bytes = decode_unique_bytes(w) if g.shared_prefix else d_bytes
     p_bytes, p_flops = prefill_bytes_flops(w)
-    step_bytes = d_bytes + scatter_bytes(w) + copy_bytes(w) + p_bytes
+    step_bytes = u_bytes + scatter_bytes(w) + copy_bytes(w) + p_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = d_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0
+    dec_gbs = u_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0
     traffic = committed_traffic(d_bytes) if w.name == "llama2_7b_decode" else None
     out = {
         "metric": "pa_decode HBM GB/s (% of 8 TB/s peak) + decode tokens/s, 7B-shaped layer",
@@ -235,6 +255,7 @@ def main():
             "copy_pairs": int(len(w.copy_pairs)),
             "scatter_tokens": int(len(w.slot_mapping)),
             "prefill_rows": int(g.pre_query.shape[0]),
+            "shared_prefix_read_once": bool(g.shared_prefix),
         },
         "decode_tokens_per_s": round(w.n_decode / (ms_per_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 5),
@@ -248,9 +269,12 @@ def main():
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(d_bytes),
+            "algorithmic_bytes_per_launch": int(u_bytes),
         },
     }
+    if g.shared_prefix or u_bytes != d_bytes:
+        out["decode_logical_bytes"] = int(d_bytes)
+        out["decode_GBps_logical"] = round(d_bytes / (dec_ms * 1e-3) / 1e9, 2)
     if has_prefill:
         out["prefill_ms"] = round(pre_ms, 5)
         out["prefill_TFLOPs"] = round(p_flops / (pre_ms * 1e-3) / 1e12, 2)

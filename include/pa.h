@@ -12,6 +12,8 @@
  *         decodes under one token budget (§5.4, §5.5).
  *   [OV]  devpress.csdn.net/amd vLLM overview: per-block attention over the block table (§3 (3))
  *         combined with a running maximum and sum of exponentials (§9 (4) online softmax).
+ *   [V1]  lilinji.mintlify.site lecture 34 "vLLM 生产级系统架构全景剖析…": §2.2 shared prefixes
+ *         and block reference counts.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -124,6 +126,38 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
                       int32_t max_seq_len, int32_t num_q_heads, float scale,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode for batches whose sequences share prompt blocks, reading
+ * each shared block once. [MEM] 机制 2：写时复制: parallel samples of one prompt share its
+ * physical blocks (reference-counted) and diverge into private blocks; [V1] §2.2: shared prefixes.
+ * Group g is the consecutive sequences group_starts[g] .. group_starts[g+1]-1 (group_starts[0] = 0;
+ * sequences from group_starts[num_groups] on belong to no group). prefix_lens[s] (a multiple of 16)
+ * is the number of leading positions whose blocks every member of s's group holds in common: the
+ * same for all members, <= seq_lens of every member, and 0 for a sequence in no group. The
+ * caller guarantees that those table entries are equal across the members.
+ * Per (group, kv head) the shared positions are attended once for all members' queries, each
+ * sequence's remaining positions by itself, and the parts are merged by rescaling with their
+ * maxima and sums of exponentials ([OV] §9 (4)). out equals pa_decode's definition.
+ *   Arguments as in pa_decode, plus group_starts [num_groups + 1], prefix_lens [num_seqs],
+ *   max_group_size (>= every group's size, <= 64) and max_prefix_len (>= every prefix_lens).
+ *   partition_size must be a multiple of 16 in [16, 1024]; workspace of at least
+ *   pa_decode_shared_prefix_workspace_size(...) bytes.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_seq_len,
+                                              int32_t max_prefix_len, int32_t partition_size);
+
+pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, void *out, const void *query,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens, int32_t num_seqs,
+                                    int32_t max_seq_len, const int32_t *group_starts,
+                                    const int32_t *prefix_lens, int32_t num_groups,
+                                    int32_t max_group_size, int32_t max_prefix_len,
+                                    int32_t num_q_heads, float scale, int32_t partition_size,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_prefill_chunk -- causal attention of prefill chunks over their paged context.

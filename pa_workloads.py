@@ -248,50 +248,81 @@ def build(seq_lens: Sequence[int], H_q: int, H_kv: int, D: int, dtype: str, seed
                    new_positions, [], pool, partition_size, max_blocks)
 
 
-def build_prefix_sharing(groups: int, samples: int, prefix: int, suffix_max: int, H: int, D: int,
-                         dtype: str, seed: int, partition_size: Optional[int] = None,
-                         name: str = "prefix_sharing") -> Workload:
-    """Parallel sampling: each group of `samples` sequences shares a `prefix`-token prompt (its
-    blocks have ref_cnt == samples) and then holds a private suffix of U{1..suffix_max} tokens.
+def build_shared_groups(groups, H_q: int, H_kv: int, D: int, dtype: str, seed: int,
+                        independent: Sequence[int] = (), partition_size: Optional[int] = None,
+                        name: str = "shared_groups") -> Workload:
+    """Groups of parallel samples, each sharing a prompt, followed by independent sequences.
 
-    The step it describes: when the samples diverge, a shared block that is only partly filled is
-    copied on write for every sample but the last holder (copy_blocks pairs); each sample then writes
-    its own tokens of that block and its newest token (reshape_and_cache); then all decode.
-    Blocks are taken from one seeded permutation: per group its prefix blocks, then per sample its
-    copy-on-write block (if any) and its private blocks.
+    groups: list of (prefix_tokens, [total length of each member]) -- every member holds the
+    prompt's blocks with a reference count equal to the group size. When the prompt ends inside a
+    block, that block is copied on write for every member but the last holder (copy_blocks pairs);
+    each member then writes its own tokens of that block and its newest token (reshape_and_cache).
+    independent: lengths of sequences in no group (one new token each).
+    meta: group_starts [groups + 1] and shared_prefix [S] = tokens of the blocks all members still
+    hold in common (the prompt rounded down to whole blocks; 0 outside a group).
+    Blocks are taken from one seeded permutation: per group its prompt blocks, then per member its
+    copy-on-write block (if any) and its private blocks; then the independent sequences' blocks.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    suffix = rng.integers(1, suffix_max, size=groups * samples, endpoint=True)
-    seq_lens = [prefix + int(x) for x in suffix]
-    n_pre = blocks_needed(prefix)
-    partial = prefix % BLOCK != 0
-    need = groups * n_pre
-    for i, L in enumerate(seq_lens):
-        need += blocks_needed(L) - n_pre + (1 if partial and (i % samples) != samples - 1 else 0)
+    need = 0
+    for prefix, lens in groups:
+        n_pre = blocks_needed(prefix)
+        need += n_pre + sum(blocks_needed(L) - n_pre for L in lens)
+        if prefix % BLOCK:
+            need += len(lens) - 1
+    need += sum(blocks_needed(L) for L in independent)
     nb = need + (need + 9) // 10
     pool = BlockPool(nb, rng.permutation(nb))
-    tables, pairs, new_positions = [], [], []
-    for g in range(groups):
-        shared = pool.take(n_pre)
-        pool.share([b for b in shared for _ in range(samples - 1)])
-        for j in range(samples):
-            s = g * samples + j
-            t = list(shared)
-            if partial:
+    tables, pairs, new_positions, seq_lens, shared, starts = [], [], [], [], [], [0]
+    for prefix, lens in groups:
+        if any(L <= prefix for L in lens):
+            raise ValueError("every member extends its prompt")
+        n_pre = blocks_needed(prefix)
+        common = pool.take(n_pre)
+        pool.share([b for b in common for _ in range(len(lens) - 1)])
+        for L in lens:
+            s = len(seq_lens)
+            t = list(common)
+            if prefix % BLOCK:
                 src = t[n_pre - 1]
                 fresh = pool.write_block(t, n_pre - 1)
                 if fresh is not None:
                     pairs.append((src, fresh))
-            t += pool.take(blocks_needed(seq_lens[s]) - n_pre)
+            t += pool.take(blocks_needed(L) - n_pre)
             tables.append(t)
-            L = seq_lens[s]
+            seq_lens.append(int(L))
+            shared.append((prefix // BLOCK) * BLOCK)
             pos = list(range(prefix, min(n_pre * BLOCK, L)))
             if L - 1 not in pos:
                 pos.append(L - 1)
-            new_positions += [(s, p) for p in pos]
-    w = _finish(name, rng, dtype, H, H, D, nb, seq_lens, tables, len(seq_lens), [],
-                new_positions, pairs, pool, partition_size,
-                meta={"groups": groups, "samples": samples, "prefix": prefix})
+            new_positions += [(s, q) for q in pos]
+        starts.append(len(seq_lens))
+    for L in independent:
+        s = len(seq_lens)
+        tables.append(pool.take(blocks_needed(L)))
+        seq_lens.append(int(L))
+        shared.append(0)
+        if L > 0:
+            new_positions.append((s, L - 1))
+    return _finish(name, rng, dtype, H_q, H_kv, D, nb, seq_lens, tables, len(seq_lens), [],
+                   new_positions, pairs, pool, partition_size,
+                   meta={"group_starts": np.asarray(starts, np.int32),
+                         "shared_prefix": np.asarray(shared, np.int32)})
+
+
+def build_prefix_sharing(groups: int, samples: int, prefix: int, suffix_max: int, H: int, D: int,
+                         dtype: str, seed: int, partition_size: Optional[int] = None,
+                         name: str = "prefix_sharing") -> Workload:
+    """`groups` groups of `samples` parallel samples: each group shares a `prefix`-token prompt
+    (its blocks have ref_cnt == samples), each sample then holds a private suffix of U{1..suffix_max}
+    tokens (drawn first, group by group). See build_shared_groups for the step it describes."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    suffix = rng.integers(1, suffix_max, size=groups * samples, endpoint=True)
+    spec = [(prefix, [prefix + int(x) for x in suffix[g * samples:(g + 1) * samples]])
+            for g in range(groups)]
+    w = build_shared_groups(spec, H, H, D, dtype, int(rng.integers(0, 2**31 - 1)),
+                            partition_size=partition_size, name=name)
+    w.meta.update({"groups": groups, "samples": samples, "prefix": prefix})
     return w
 
 

@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode.restype = _i
         L.pa_decode.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _i,
                                 _p, _sz, _p]
+        L.pa_decode_shared_prefix_workspace_size.restype = _sz
+        L.pa_decode_shared_prefix_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.pa_decode_shared_prefix.restype = _i
+        L.pa_decode_shared_prefix.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i,
+                                              _p, _p, _i, _i, _i, _i, _f, _i, _p, _sz, _p]
         L.pa_prefill_chunk.restype = _i
         L.pa_prefill_chunk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _i,
                                        _i, _f, _p]
@@ -170,6 +175,46 @@ def decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: in
                            int(block_tables.shape[1]), seq_lens.data_ptr(), B, int(max_seq_len),
                            hq, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                            _stream(stream)))
+
+
+def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                        max_prefix_len, partition_size) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                            max_seq_len, max_prefix_len,
+                                                            partition_size))
+
+
+def decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+                         group_starts, prefix_lens, max_group_size: int, max_prefix_len: int,
+                         scale: float, partition_size: int = 512,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode_shared_prefix: pa_decode whose groups of sequences (group_starts [G+1], int32)
+    read their common leading blocks (prefix_lens [B], int32) once."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, k_cache.dtype)
+        if tuple(t.shape) != (B, hq, d):
+            raise ValueError(f"{n} must be [{B}, {hq}, {d}]")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (group_starts, "group_starts"), (prefix_lens, "prefix_lens")):
+        _gpu(t, n, torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,) \
+            or prefix_lens.shape != (B,) or group_starts.dim() != 1:
+        raise ValueError("block_tables [B, max_blocks], seq_lens and prefix_lens [B], "
+                         "group_starts [G + 1]")
+    G = int(group_starts.shape[0]) - 1
+    need = decode_shared_prefix_workspace_size(B, hq, d, max_seq_len, max_prefix_len,
+                                               partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_shared_prefix(
+        dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), int(block_tables.shape[1]), seq_lens.data_ptr(), B,
+        int(max_seq_len), group_starts.data_ptr(), prefix_lens.data_ptr(), max(G, 0),
+        int(max_group_size), int(max_prefix_len), hq, float(scale), int(partition_size),
+        workspace.data_ptr(), ws_bytes, _stream(stream)))
 
 
 def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,

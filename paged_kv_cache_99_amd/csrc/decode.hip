@@ -50,7 +50,21 @@ struct DecodeParams {
     int32_t n_units;
     int32_t split;
     float scale_log2;     // scale * log2(e): scores live in the log2 domain
+    // Shared-prefix (cascade) support; zero / null for a plain decode.
+    const int32_t *__restrict__ seq_starts;   // [num_seqs] first position of a unit's range
+    const int32_t *__restrict__ group_starts; // [num_groups + 1] members of prefix group g
+    int32_t num_groups;
+    int32_t ws_slots;     // partial-result slots per (sequence, head) row of the workspace
+    int32_t slot_base;    // first slot these units write
+    int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix parts (merge)
+    int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
 };
+
+// Position range of unit `part` of a sequence: [start + part*P, min(L, start + (part+1)*P)).
+__device__ __forceinline__ int unit_start(const DecodeParams &p, int seq, int L)
+{
+    return p.seq_starts ? min(max(p.seq_starts[seq], 0), L) : 0;
+}
 
 template <bool BF, int D, int GK>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
@@ -73,7 +87,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
     const int h0 = (kvh * p.n_sub + sub) * GK;  // first query head of this unit
 
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
-    const int t0 = part * p.part_tokens;
+    const int t0 = unit_start(p, seq, L) + part * p.part_tokens;
     if (p.split && t0 >= L)
         return;  // a part with no tokens: the merge never reads it
     const int t1 = min(L, t0 + p.part_tokens);
@@ -124,10 +138,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
 #pragma unroll
                 for (int i = 0; i < NCH; ++i)
                     s[h][i] = group_sum<RL>(dot8<BF>(q[h], kk[i])) * p.scale_log2;
-            if (!(good_blk && base + kBlock <= t1)) {  // a tail block (or a bad id): mask
+            if (!(good_blk && base >= t0 && base + kBlock <= t1)) {  // an edge block or a bad id
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    const bool ok = good_blk && base + i * ROWS + r < t1;
+                    const int tok = base + i * ROWS + r;
+                    const bool ok = good_blk && tok >= t0 && tok < t1;
 #pragma unroll
                     for (int h = 0; h < GK; ++h)
                         s[h][i] = ok ? s[h][i] : -INFINITY;
@@ -215,11 +230,12 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
         for (int h = 0; h < GK; ++h) {
             const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
             if (p.split) {
-                float *wa = p.ws_acc + (row * p.max_parts + part) * D + lane * 8;
+                const size_t slot = row * p.ws_slots + p.slot_base + part;
+                float *wa = p.ws_acc + slot * D + lane * 8;
                 *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
                 *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
                 if (lane == 0)
-                    *(float2 *)(p.ws_ml + (row * p.max_parts + part) * 2) = make_float2(m[h], l[h]);
+                    *(float2 *)(p.ws_ml + slot * 2) = make_float2(m[h], l[h]);
             } else {
                 const float inv = l[h] > 0.0f ? 1.0f / l[h] : 0.0f;
                 uint4 o;
@@ -296,8 +312,12 @@ __device__ __forceinline__ int kswz(int row)
         return (row >> 1) & (8 / GK - 1);
 }
 
+// One unit over positions [t0, t1) of the table `table` and kv head kvh, for GK query rows qrow[h]
+// (rows of query / out / workspace; -1 = no query). Split units write slot `slot` of each row.
 template <bool BF, int D, int GK>
-__global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
+__device__ __forceinline__ void gqa_unit(const DecodeParams &p, const int (&qrow)[GK],
+                                         const int32_t *table, int kvh, int t0, int t1, int slot,
+                                         bool split)
 {
     constexpr int RL = D / 8;            // P*V layout: lanes per token row
     constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
@@ -313,31 +333,14 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
     const int r = lane / RL, c = lane % RL;  // P*V layout
     const int ts = lane / GK, j = lane % GK; // scoring layout: token slot, dim slice = own head
 
-    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (unit >= p.n_units)
-        return;
-    const int seq = unit % p.num_seqs;
-    int rest = unit / p.num_seqs;
-    const int part = rest % p.max_parts;
-    rest /= p.max_parts;
-    const int sub = rest % p.n_sub;
-    const int kvh = rest / p.n_sub;
-    const int h0 = (kvh * p.n_sub + sub) * GK;
-
-    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
-    const int t0 = part * p.part_tokens;
-    if (p.split && t0 >= L)
-        return;
-    const int t1 = min(L, t0 + p.part_tokens);
-
     // queries in the scoring layout: dims [j*D/GK, (j+1)*D/GK) of every head of the group
     uint4 q[GK][CPL];
 #pragma unroll
     for (int h = 0; h < GK; ++h)
 #pragma unroll
         for (int k = 0; k < CPL; ++k)
-            q[h][k] = *(const uint4 *)(p.query + ((size_t)seq * p.num_q_heads + h0 + h) * D +
-                                       (j * CPL + k) * 8);
+            q[h][k] = qrow[h] >= 0 ? *(const uint4 *)(p.query + (size_t)qrow[h] * D + (j * CPL + k) * 8)
+                                   : make_uint4(0, 0, 0, 0);
 
     float m_own = -INFINITY, l_own = 0.0f;  // reference point and partial sum of head j
     float acc[GK][8];
@@ -347,7 +350,6 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
         for (int e = 0; e < 8; ++e)
             acc[h][e] = 0.0f;
 
-    const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
     const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D;
     const size_t tile_off = (size_t)kvh * kBlock * D + lane * 8;
 
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
             const int base = (bb + k) * kBlock;
             const int raw = __builtin_amdgcn_readlane(my_blk, k);
             const bool good_blk = (unsigned)raw < (unsigned)p.num_blocks;
-            const bool whole = good_blk && base + kBlock <= t1;
+            const bool whole = good_blk && base >= t0 && base + kBlock <= t1;
 
             // stage the K tile: row ROWS*i + r, piece c (swizzled)
 #pragma unroll
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
                     part_sum[h] = a;
                 }
                 float x = transpose_reduce<GK>(part_sum, j) * p.scale_log2;
-                if (!whole && !(good_blk && base + row < t1))
+                if (!whole && !(good_blk && base + row >= t0 && base + row < t1))
                     x = -INFINITY;
                 sc[ps] = x;
             }
@@ -444,7 +446,8 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
             if (!whole) {
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    const bool ok = good_blk && base + ROWS * i + r < t1;
+                    const int tok = base + ROWS * i + r;
+                    const bool ok = good_blk && tok >= t0 && tok < t1;
                     vv[i] = ok ? vv[i] : make_uint4(0, 0, 0, 0);  // masked rows may hold NaN bits
                 }
             }
@@ -506,14 +509,15 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
     for (int h = 0; h < GK; ++h) {
         const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_own), h));
         const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_own), h));
-        if (lane < RL) {
-            const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
-            if (p.split) {
-                float *wa = p.ws_acc + (row * p.max_parts + part) * D + lane * 8;
+        if (lane < RL && qrow[h] >= 0) {
+            const size_t row = (size_t)qrow[h];
+            if (split) {
+                const size_t sl = row * p.ws_slots + slot;
+                float *wa = p.ws_acc + sl * D + lane * 8;
                 *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
                 *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
                 if (lane == 0)
-                    *(float2 *)(p.ws_ml + (row * p.max_parts + part) * 2) = make_float2(mh, lh);
+                    *(float2 *)(p.ws_ml + sl * 2) = make_float2(mh, lh);
             } else {
                 const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
                 uint4 o;
@@ -525,6 +529,72 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
             }
         }
     }
+}
+
+// Plain decode unit for a head group of GK: (sequence, kv head, subgroup, part).
+template <bool BF, int D, int GK>
+__global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
+{
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
+    if (unit >= p.n_units)
+        return;
+    const int seq = unit % p.num_seqs;
+    int rest = unit / p.num_seqs;
+    const int part = rest % p.max_parts;
+    rest /= p.max_parts;
+    const int sub = rest % p.n_sub;
+    const int kvh = rest / p.n_sub;
+    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
+    const int t0 = unit_start(p, seq, L) + part * p.part_tokens;
+    if (p.split && t0 >= L)
+        return;
+    const int t1 = min(L, t0 + p.part_tokens);
+    int qrow[GK];
+#pragma unroll
+    for (int h = 0; h < GK; ++h)
+        qrow[h] = seq * p.num_q_heads + (kvh * p.n_sub + sub) * GK + h;
+    gqa_unit<BF, D, GK>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
+                        p.slot_base + part, p.split != 0);
+}
+
+// Shared-prefix unit: (prefix group g, kv head, subgroup of GK (member, query head) pairs, part).
+// The members of group g are sequences group_starts[g] .. group_starts[g+1]-1; they share the
+// blocks of positions [0, seq_starts[first member]), read here once through the first member's
+// table for all of them (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are
+// stored once). Pair v of the group is member v / G, query head kvh*G + v % G.
+template <bool BF, int D, int GK>
+__global__ __launch_bounds__(64) void decode_prefix_kernel(DecodeParams p)
+{
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
+    if (unit >= p.n_units)
+        return;
+    int rest = unit;
+    const int vsub = rest % p.n_vsub;
+    rest /= p.n_vsub;
+    const int kvh = rest % p.num_kv_heads;
+    rest /= p.num_kv_heads;
+    const int part = rest % p.max_parts;
+    const int g = rest / p.max_parts;
+    const int first = min(max(p.group_starts[g], 0), p.num_seqs);
+    const int n_mem = min(max(p.group_starts[g + 1], first), p.num_seqs) - first;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int v0 = vsub * GK;
+    if (n_mem == 0 || v0 >= n_mem * G)
+        return;
+    const int L0 = min(max(p.seq_lens[first], 0), p.max_seq_len);
+    const int prefix = min(max(p.seq_starts[first], 0), L0);
+    const int t0 = part * p.part_tokens;
+    if (t0 >= prefix)
+        return;
+    const int t1 = min(prefix, t0 + p.part_tokens);
+    int qrow[GK];
+#pragma unroll
+    for (int h = 0; h < GK; ++h) {
+        const int v = v0 + h;
+        qrow[h] = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
+    }
+    gqa_unit<BF, D, GK>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1, part,
+                        true);
 }
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
@@ -539,28 +609,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
         return;
     const int seq = idx / p.num_q_heads;
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
-    const int np = (L + p.part_tokens - 1) / p.part_tokens;
-    const float *ml = p.ws_ml + (size_t)idx * p.max_parts * 2;
-    const float *ac = p.ws_acc + (size_t)idx * p.max_parts * D + lane * DPL;
+    const int start = unit_start(p, seq, L);
+    // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots
+    const int n_pre = p.pre_slots > 0 ? (start + p.part_tokens - 1) / p.part_tokens : 0;
+    const int n_own = (L - start + p.part_tokens - 1) / p.part_tokens;
+    const int np = n_pre + n_own;
+    auto slot_of = [&](int jj) { return jj < n_pre ? jj : p.pre_slots + (jj - n_pre); };
+    const float *ml = p.ws_ml + (size_t)idx * p.ws_slots * 2;
+    const float *ac = p.ws_acc + (size_t)idx * p.ws_slots * D + lane * DPL;
 
     float M = -INFINITY;
-    for (int j = lane; j < np; j += kWave)
-        M = fmaxf(M, ml[2 * j]);
+    for (int jj = lane; jj < np; jj += kWave)
+        M = fmaxf(M, ml[2 * slot_of(jj)]);
     M = wave_max(M);
     float W = 0.0f;
-    for (int j = lane; j < np; j += kWave)
-        W += fast_exp2(ml[2 * j] - M) * ml[2 * j + 1];
+    for (int jj = lane; jj < np; jj += kWave)
+        W += fast_exp2(ml[2 * slot_of(jj)] - M) * ml[2 * slot_of(jj) + 1];
     W = wave_sum(W);
 
     float o[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d)
         o[d] = 0.0f;
-    for (int j = 0; j < np; ++j) {
-        const float w = fast_exp2(ml[2 * j] - M);
+    for (int jj = 0; jj < np; ++jj) {
+        const int sl = slot_of(jj);
+        const float w = fast_exp2(ml[2 * sl] - M);
 #pragma unroll
         for (int d = 0; d < DPL; ++d)
-            o[d] += w * ac[(size_t)j * D + d];
+            o[d] += w * ac[(size_t)sl * D + d];
     }
     const float inv = W > 0.0f ? 1.0f / W : 0.0f;
     uint16_t *dst = p.out + (size_t)idx * D + lane * DPL;
@@ -571,7 +647,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
 }
 
 template <bool BF, int D, int GK>
-hipError_t launch_typed(const DecodeParams &p, hipStream_t stream)
+hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
 {
     const int grid = round_up8(p.n_units);
     if constexpr (GK >= 4)
@@ -579,23 +655,41 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t stream)
     else
         hipLaunchKernelGGL((decode_partition_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0,
                            stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !p.split)
-        return e;
-    const int rows = p.num_seqs * p.num_q_heads;
-    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 template <bool BF, int D>
-hipError_t launch_gk(int gk, const DecodeParams &p, hipStream_t stream)
+hipError_t launch_units_gk(int gk, const DecodeParams &p, hipStream_t stream)
 {
     switch (gk) {
-    case 8: return launch_typed<BF, D, 8>(p, stream);
-    case 4: return launch_typed<BF, D, 4>(p, stream);
-    case 2: return launch_typed<BF, D, 2>(p, stream);
-    default: return launch_typed<BF, D, 1>(p, stream);
+    case 8: return launch_units<BF, D, 8>(p, stream);
+    case 4: return launch_units<BF, D, 4>(p, stream);
+    case 2: return launch_units<BF, D, 2>(p, stream);
+    default: return launch_units<BF, D, 1>(p, stream);
     }
+}
+
+template <bool BF, int D>
+hipError_t run_decode(int gk, int gkp, const DecodeParams &p, const DecodeParams *pre,
+                      hipStream_t stream)
+{
+    hipError_t e;
+    if (pre) {
+        const int grid = round_up8(pre->n_units);
+        if (gkp == 8)
+            hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 8>), dim3(grid), dim3(kWave), 0,
+                               stream, *pre);
+        else
+            hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 4>), dim3(grid), dim3(kWave), 0,
+                               stream, *pre);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    if ((e = launch_units_gk<BF, D>(gk, p, stream)) != hipSuccess || !p.split)
+        return e;
+    const int rows = p.num_seqs * p.num_q_heads;
+    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -611,7 +705,8 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
         return hipSuccess;
     const int group = d.num_q_heads / d.c.num_kv_heads;
     const int gk = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-    DecodeParams p;
+    const bool cascade = d.group_starts != nullptr && d.num_groups > 0;
+    DecodeParams p = {};
     p.query = (const uint16_t *)d.query;
     p.k_cache = (const uint16_t *)d.k_cache;
     p.v_cache = (const uint16_t *)d.v_cache;
@@ -626,22 +721,46 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.num_q_heads = d.num_q_heads;
     p.num_blocks = d.c.num_blocks;
     p.max_seq_len = d.max_seq_len;
+    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    p.n_sub = group / gk;
     p.split = d.max_parts > 0 ? 1 : 0;
     p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
     if (p.part_tokens < kBlock)
         p.part_tokens = kBlock;
     p.max_parts = p.split ? d.max_parts : 1;
-    p.n_sub = group / gk;
+    p.ws_slots = p.max_parts;
+
+    DecodeParams pre;
+    int gkp = 8;
+    if (cascade) {
+        // slots [0, pre_parts) of every row hold shared-prefix parts, the rest its own parts
+        const int pre_parts = (d.max_prefix_len + d.partition_size - 1) / d.partition_size;
+        p.seq_starts = d.seq_starts;
+        p.pre_slots = pre_parts;
+        p.slot_base = pre_parts;
+        p.ws_slots = pre_parts + p.max_parts;
+        pre = p;
+        pre.group_starts = d.group_starts;
+        pre.num_groups = d.num_groups;
+        const int pairs = d.max_group_size * group;  // (member, query head) pairs per kv head
+        gkp = pairs >= 8 ? 8 : 4;
+        pre.n_vsub = (pairs + gkp - 1) / gkp;
+        pre.max_parts = pre_parts;
+        const int64_t pre_units = (int64_t)d.num_groups * pre_parts * d.c.num_kv_heads * pre.n_vsub;
+        if (pre_units > 0x7ffffff0)
+            return hipErrorInvalidValue;
+        pre.n_units = (int32_t)pre_units;
+    }
     const int64_t units = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.max_parts;
     if (units > 0x7ffffff0)
         return hipErrorInvalidValue;
     p.n_units = (int32_t)units;
-    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    const DecodeParams *pp = cascade ? &pre : nullptr;
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, stream)
-                                  : launch_gk<true, 128>(gk, p, stream);
-    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, stream)
-                              : launch_gk<false, 128>(gk, p, stream);
+        return d.c.head_dim == 64 ? run_decode<true, 64>(gk, gkp, p, pp, stream)
+                                  : run_decode<true, 128>(gk, gkp, p, pp, stream);
+    return d.c.head_dim == 64 ? run_decode<false, 64>(gk, gkp, p, pp, stream)
+                              : run_decode<false, 128>(gk, gkp, p, pp, stream);
 }
 
 }  // namespace pa

@@ -199,10 +199,113 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
     d.scale = scale;
     d.partition_size = partition_size;
     d.max_parts = parts_of(max_seq_len, partition_size);
+    d.seq_starts = nullptr;
+    d.group_starts = nullptr;
+    d.num_groups = 0;
+    d.max_group_size = 0;
+    d.max_prefix_len = 0;
     d.ws_acc = (float *)workspace;
     d.ws_ml = need ? (float *)workspace + (size_t)num_seqs * num_q_heads * d.max_parts * head_dim
                    : nullptr;
     return launched(pa::launch_decode(d, (hipStream_t)stream), "decode");
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_seq_len,
+                                              int32_t max_prefix_len, int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0 ||
+        max_seq_len < 0 || max_prefix_len < 0)
+        return 0;
+    const int64_t own = max_seq_len > 0 ? (max_seq_len + partition_size - 1) / partition_size : 1;
+    const int64_t pre = (max_prefix_len + partition_size - 1) / partition_size;
+    return (size_t)num_seqs * num_q_heads * (size_t)(pre + own) * (head_dim + 2) * sizeof(float);
+}
+
+pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, void *out, const void *query,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens, int32_t num_seqs,
+                                    int32_t max_seq_len, const int32_t *group_starts,
+                                    const int32_t *prefix_lens, int32_t num_groups,
+                                    int32_t max_group_size, int32_t max_prefix_len,
+                                    int32_t num_q_heads, float scale, int32_t partition_size,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_seqs >= 0, "num_seqs %d < 0", num_seqs);
+    REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
+            "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+            num_kv_heads);
+    REQUIRE(max_blocks_per_seq >= 0, "max_blocks_per_seq %d < 0", max_blocks_per_seq);
+    REQUIRE(max_seq_len >= 0 && (int64_t)max_seq_len <= (int64_t)PA_BLOCK_SIZE * max_blocks_per_seq,
+            "max_seq_len %d is outside [0, 16 * max_blocks_per_seq = %lld]", max_seq_len,
+            (long long)PA_BLOCK_SIZE * max_blocks_per_seq);
+    REQUIRE(partition_size > 0 && partition_size % PA_BLOCK_SIZE == 0 && partition_size <= 1024,
+            "partition_size %d is not a multiple of 16 in [16, 1024]", partition_size);
+    REQUIRE(scale > 0.0f && scale < 3.0e38f, "scale %g is not a finite positive number", (double)scale);
+    REQUIRE(num_groups >= 0 && num_groups <= num_seqs, "num_groups %d is outside [0, num_seqs]",
+            num_groups);
+    REQUIRE(max_group_size >= 1 && max_group_size <= 64, "max_group_size %d is outside [1, 64]",
+            max_group_size);
+    REQUIRE(max_prefix_len >= 0 && max_prefix_len <= max_seq_len,
+            "max_prefix_len %d is outside [0, max_seq_len]", max_prefix_len);
+    if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
+                    num_q_heads / num_kv_heads);
+    if (num_seqs == 0)
+        return ok();
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(query, "query");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(block_tables != nullptr, "block_tables is NULL");
+    REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
+    REQUIRE(prefix_lens != nullptr, "prefix_lens is NULL");
+    REQUIRE(num_groups == 0 || group_starts != nullptr, "group_starts is NULL");
+    const size_t need = pa_decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                               max_seq_len, max_prefix_len,
+                                                               partition_size);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    const int32_t own = max_seq_len > 0 ? (max_seq_len + partition_size - 1) / partition_size : 1;
+    const int32_t pre = (max_prefix_len + partition_size - 1) / partition_size;
+    (void)pre;
+    pa::DecodeLaunch d;
+    d.c = c;
+    d.out = out;
+    d.query = query;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.max_blocks = max_blocks_per_seq;
+    d.seq_lens = seq_lens;
+    d.num_seqs = num_seqs;
+    d.max_seq_len = max_seq_len;
+    d.num_q_heads = num_q_heads;
+    d.scale = scale;
+    d.partition_size = partition_size;
+    d.max_parts = own;
+    d.seq_starts = prefix_lens;
+    d.group_starts = num_groups > 0 ? group_starts : nullptr;
+    d.num_groups = num_groups;
+    d.max_group_size = max_group_size;
+    d.max_prefix_len = max_prefix_len;
+    if (d.group_starts == nullptr) {
+        // no groups: a plain split decode (every prefix length must then be 0)
+        d.seq_starts = nullptr;
+        d.max_prefix_len = 0;
+    }
+    // workspace: acc [rows][slots][D], then (m, l) [rows][slots][2]; slots = prefix parts + own
+    const int32_t slots = (d.max_prefix_len + partition_size - 1) / partition_size + own;
+    d.ws_acc = (float *)workspace;
+    d.ws_ml = (float *)workspace + (size_t)num_seqs * num_q_heads * slots * head_dim;
+    return launched(pa::launch_decode(d, (hipStream_t)stream), "decode_shared_prefix");
 }
 
 pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,

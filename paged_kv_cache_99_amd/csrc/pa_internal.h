@@ -39,8 +39,14 @@ struct DecodeLaunch {
     float scale;
     int32_t partition_size;  // 0 = unsplit
     float *ws_acc;           // [num_seqs][num_q_heads][max_parts][head_dim]
-    float *ws_ml;            // [num_seqs][num_q_heads][max_parts][2]
-    int32_t max_parts;
+    float *ws_ml;            // [num_seqs][num_q_heads][slots][2]
+    int32_t max_parts;       // own parts per sequence (0 = unsplit)
+    // shared-prefix (cascade) decode; group_starts == nullptr for a plain decode
+    const int32_t *seq_starts;    // [num_seqs] shared-prefix length of each sequence
+    const int32_t *group_starts;  // [num_groups + 1]
+    int32_t num_groups;
+    int32_t max_group_size;
+    int32_t max_prefix_len;
 };
 // Group sizes with a dedicated kernel; any other group size runs as several of these.
 bool decode_supported(int32_t head_dim, int32_t group);

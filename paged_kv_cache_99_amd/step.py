@@ -39,7 +39,8 @@ def ints_to_device(a, device) -> torch.Tensor:
 
 
 class GpuStep:
-    def __init__(self, w, device="cuda", partition_size: Optional[int] = None):
+    def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
+                 shared_prefix: bool = False):
         self.w = w
         self.device = torch.device(device)
         dt, dev = w.dtype, self.device
@@ -64,6 +65,21 @@ class GpuStep:
         self.partition_size = int(partition_size)
         self.workspace = binding.alloc_decode_workspace(nd, w.H_q, w.D, self.max_seq_len,
                                                         self.partition_size, dev) if nd else None
+        # read-once shared prefixes: groups of sequences that hold common leading blocks
+        meta = getattr(w, "meta", {}) or {}
+        self.shared_prefix = bool(shared_prefix and "group_starts" in meta and nd)
+        if self.shared_prefix:
+            gs = np.asarray(meta["group_starts"], np.int32)
+            pl = np.asarray(meta["shared_prefix"], np.int32)[:nd]
+            self.group_starts = ints_to_device(gs, dev)
+            self.prefix_lens = ints_to_device(pl, dev)
+            self.max_group_size = int(np.max(np.diff(gs))) if len(gs) > 1 else 1
+            self.max_prefix_len = int(pl.max()) if len(pl) else 0
+            if self.partition_size == 0:
+                self.partition_size = 512
+            self.workspace = torch.empty(max(16, binding.decode_shared_prefix_workspace_size(
+                nd, w.H_q, w.D, self.max_seq_len, self.max_prefix_len, self.partition_size)),
+                dtype=torch.uint8, device=dev)
         self.pre_tables = ints_to_device(w.block_tables[nd:], dev)
         self.pre_lens = ints_to_device(w.seq_lens[nd:], dev)
         self.pre_cu = ints_to_device(w.cu_q_lens, dev)
@@ -81,7 +97,13 @@ class GpuStep:
                                   self.slot_mapping, stream)
 
     def decode(self, stream=None):
-        if self.n_decode:
+        if self.n_decode and self.shared_prefix:
+            binding.decode_shared_prefix(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
+                                         self.dec_tables, self.dec_lens, self.max_seq_len,
+                                         self.group_starts, self.prefix_lens,
+                                         self.max_group_size, self.max_prefix_len, self.w.scale,
+                                         self.partition_size, self.workspace, stream)
+        elif self.n_decode:
             binding.decode(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
                            self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,
                            self.partition_size, self.workspace, stream)

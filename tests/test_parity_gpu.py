@@ -42,9 +42,11 @@ def poisoned(w):
     return dataclasses.replace(w, k_cache=kc, v_cache=vc)
 
 
-def run_on_gpu(w, stages=("copy", "scatter", "decode", "prefill"), partition_size=None):
-    print(f"[parity] gpu step {w.name}: stages={stages} partition={partition_size}", flush=True)
-    g = GpuStep(w, partition_size=partition_size)
+def run_on_gpu(w, stages=("copy", "scatter", "decode", "prefill"), partition_size=None,
+               shared_prefix=False):
+    print(f"[parity] gpu step {w.name}: stages={stages} partition={partition_size} "
+          f"shared_prefix={shared_prefix}", flush=True)
+    g = GpuStep(w, partition_size=partition_size, shared_prefix=shared_prefix)
     for s in stages:
         getattr(g, s)()
     torch.cuda.synchronize()
@@ -254,3 +256,40 @@ def test_prefill_is_deterministic():
     g.prefill()
     torch.cuda.synchronize()
     assert np.array_equal(first, words_from_device(g.pre_out))
+
+
+# ------------------------------------------------------------------- read-once shared prefixes
+@pytest.mark.parametrize("name", ["prefix_sharing_2040", "prefix_sharing_2048"])
+def test_shared_prefix_decode_named(name):
+    """Parallel samples: each group's common blocks are read once for all 8 members."""
+    w = workload(name)
+    g = run_on_gpu(w, stages=("copy", "scatter", "decode"), shared_prefix=True)
+    assert g.shared_prefix and g.max_group_size == 8
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.dec_out), oracle_decode(w, kc, vc), w.dtype,
+                           f"shared-prefix decode {name}")
+
+
+SHARED_GROUPS = [
+    (40, [41, 60, 100]),                                        # prompt ends mid-block: CoW
+    (512, [513, 700]),
+    (1000, [1001, 1016, 1017, 1500, 2000, 1050, 1100, 1333]),   # 8 members
+    (0, [5, 9]),                                                # nothing shared
+    (16, [17]),                                                 # a group of one
+    (640, [641, 1300, 2100, 650, 900, 777, 1234, 999, 2222, 700]),  # 10 members > 8 per unit
+]
+
+
+@pytest.mark.parametrize("H_q,H_kv,D,dtype", [(4, 4, 128, "f16"), (8, 2, 128, "bf16"),
+                                              (16, 4, 64, "f16"), (6, 2, 128, "bf16"),
+                                              (2, 2, 64, "bf16")])
+@pytest.mark.parametrize("part", [16, 512])
+def test_shared_prefix_decode_groups(H_q, H_kv, D, dtype, part):
+    w = poisoned(W.build_shared_groups(SHARED_GROUPS, H_q, H_kv, D, dtype, seed=130 + H_q + D,
+                                       independent=[1, 33, 700]))
+    g = run_on_gpu(w, stages=("copy", "scatter", "decode"), partition_size=part,
+                   shared_prefix=True)
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.dec_out), oracle_decode(w, kc, vc), dtype,
+                           f"shared-prefix decode H_q={H_q} H_kv={H_kv} D={D} {dtype} part={part}",
+                           strict=False)
