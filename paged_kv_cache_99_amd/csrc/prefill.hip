@@ -227,16 +227,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
         const uint8_t *kb = &smem[t & 1][0][0];
         const uint8_t *vb = &smem[t & 1][1][0];
 
+        // the two 32-key halves are independent accumulator chains: interleave them so that no
+        // MFMA waits on the one issued just before it
         f32x16 s[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 s[kt][v] = 0.0f;
-            const uint8_t *krow = kb + (kt * 32 + n) * ROWB;
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const uint4 a = *(const uint4 *)(krow + (((2 * c + hh) ^ k_sw) * 16));
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const uint4 a = *(const uint4 *)(kb + (kt * 32 + n) * ROWB + (((2 * c + hh) ^ k_sw) * 16));
                 s[kt] = mfma32<BF>(a, qv[c], s[kt]);
             }
         }
@@ -300,6 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
         for (int c4 = 0; c4 < 4; ++c4) {
             // destination slots 0..3 hold keys 16*c4 + 4h + (0..3), slots 4..7 keys 16*c4 + 8 + 4h + (0..3)
             const int r1 = c4 * 16 + 4 * v_half + v_k, r2 = r1 + 8;
+            uint4 a[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int dim = dt * 32 + v_dim;
@@ -307,14 +311,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
                 const int off2 = r2 * ROWB + (((dim >> 3) ^ swz<D>(r2)) << 4) + (dim & 7) * 2;
                 const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off1));
                 const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off2));
-                uint4 a;
-                a.x = __builtin_bit_cast(uint2, lo4).x;
-                a.y = __builtin_bit_cast(uint2, lo4).y;
-                a.z = __builtin_bit_cast(uint2, hi4).x;
-                a.w = __builtin_bit_cast(uint2, hi4).y;
-                o[dt] = mfma32<BF>(a, pb[c4], o[dt]);
-                if constexpr (BF)
-                    o[dt] = mfma32<BF>(a, pl[c4], o[dt]);
+                a[dt].x = __builtin_bit_cast(uint2, lo4).x;
+                a[dt].y = __builtin_bit_cast(uint2, lo4).y;
+                a[dt].z = __builtin_bit_cast(uint2, hi4).x;
+                a[dt].w = __builtin_bit_cast(uint2, hi4).y;
+            }
+            // consecutive MFMAs go to different accumulators (distance DT)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = mfma32<BF>(a[dt], pb[c4], o[dt]);
+            if constexpr (BF) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    o[dt] = mfma32<BF>(a[dt], pl[c4], o[dt]);
             }
         }
     }
