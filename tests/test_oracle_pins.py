@@ -355,6 +355,23 @@ def test_prefill_last_row_equals_decode_at_same_length():
     assert np.array_equal(pre[-1], dec[0])
 
 
+def test_multi_token_rows_equal_decode_at_each_cut_length():
+    """I8 for k-token steps (speculative verification): row i of a k-row chunk of a length-L
+    sequence is the decode of the sequence cut to L - k + 1 + i tokens, bit for bit."""
+    k = [2, 5, 8]
+    w = W.build([40, 17, 8], 4, 2, 64, "bf16", seed=34, n_decode=0, q_lens=k)
+    pre = oracle.prefill(w.query_prefill, w.k_cache, w.v_cache, w.block_tables, w.seq_lens,
+                         w.cu_q_lens, 4, 2, 64, w.num_blocks, w.dtype, w.scale)
+    tables, cut = [], []
+    for s, ks in enumerate(k):
+        for i in range(ks):
+            tables.append(w.block_tables[s])
+            cut.append(int(w.seq_lens[s]) - ks + 1 + i)
+    dec = oracle.decode(w.query_prefill, w.k_cache, w.v_cache, np.asarray(tables, np.int32),
+                        np.asarray(cut, np.int32), 4, 2, 64, w.num_blocks, w.dtype, w.scale)
+    assert np.array_equal(pre, dec)
+
+
 # ---------------------------------------------------------------------- poison helper
 def test_poison_touches_only_free_slots():
     w = W.build([17, 3], 2, 2, 64, "f16", seed=41)
