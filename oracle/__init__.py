@@ -7,7 +7,8 @@ HIP library and the library imports nothing from here.
 
 Every pool/cache argument is the 16-bit word array (numpy uint16) in the layout
 [num_blocks][num_kv_heads][16][head_dim]; queries, keys and values are uint16 words as well, and
-``dtype`` is "f16" or "bf16".
+``dtype`` is "f16" or "bf16". The ``*_fp8`` functions take caches of E4M3 codes (numpy uint8) in
+the same layout, with one scale per cache.
 """
 import ctypes
 import os
@@ -24,6 +25,7 @@ OK, BAD_INDEX, DUP_SLOT, BAD_MAPPING, BAD_ARG, NO_MEM = range(6)
 _lib = None
 
 _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _c_int, _c_double = ctypes.c_int, ctypes.c_double
@@ -55,6 +57,24 @@ def lib():
         L.oracle_poison_free_slots.restype = ctypes.c_long
         L.oracle_poison_free_slots.argtypes = [_u16p, _u16p, _i32p, _c_int, _i32p, _c_int, _c_int,
                                                _c_int, _c_int, ctypes.c_uint16]
+        L.oracle_poison_free_slots_fp8.restype = ctypes.c_long
+        L.oracle_poison_free_slots_fp8.argtypes = [_u8p, _u8p, _i32p, _c_int, _i32p, _c_int,
+                                                   _c_int, _c_int, _c_int, ctypes.c_uint8]
+        L.oracle_e4m3_to_double.restype = _c_double
+        L.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_from_float.restype = ctypes.c_uint8
+        L.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+        L.oracle_quantize_e4m3.restype = ctypes.c_uint8
+        L.oracle_quantize_e4m3.argtypes = [ctypes.c_uint16, _c_int, ctypes.c_float]
+        L.oracle_reshape_and_cache_fp8.argtypes = [_u16p, _u16p, _u8p, _u8p, _i32p, _c_int,
+                                                   _c_int, _c_int, _c_int, _c_int, ctypes.c_float,
+                                                   ctypes.c_float]
+        L.oracle_copy_blocks_fp8.argtypes = [_u8p, _u8p, _i32p, _c_int, _c_int, _c_int, _c_int]
+        L.oracle_gather_fp8.argtypes = [_u8p, _i32p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_double, _f64p]
+        L.oracle_decode_fp8.argtypes = [_u16p, _u8p, _u8p, _i32p, _c_int, _i32p, _c_int, _c_int,
+                                        _c_int, _c_int, _c_int, _c_int, _c_double, _c_double,
+                                        _c_double, ctypes.c_void_p, _c_int, _c_int, _f64p]
         L.oracle_max_threads.restype = _c_int
         _lib = L
     return _lib
@@ -189,6 +209,96 @@ def poison_free_slots(k_cache, v_cache, block_tables, seq_lens, num_blocks, H_kv
                                        num_blocks, H_kv, D, NAN_WORD[dtype])
     if n < 0:
         raise ValueError("oracle poison_free_slots: bad table entry")
+    return kc, vc
+
+
+# ------------------------------------------------------------------------- FP8 (E4M3) caches
+NAN_E4M3 = 0x7F
+
+
+def _u8(a):
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def e4m3_to_double(codes):
+    """F1: E4M3 codes (any shape) to float64, element by element."""
+    flat = _u8(codes).ravel()
+    f = lib().oracle_e4m3_to_double
+    return np.array([f(int(c)) for c in flat], dtype=np.float64).reshape(np.shape(codes))
+
+
+def e4m3_from_float(x):
+    """F1: float32 values (any shape) to E4M3 codes: nearest, ties to even, saturating at 448."""
+    flat = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    f = lib().oracle_e4m3_from_float
+    return np.array([f(float(v)) for v in flat], dtype=np.uint8).reshape(np.shape(x))
+
+
+def quantize_e4m3(words, dtype, scale):
+    """F2: 16-bit words (any shape) to the E4M3 codes of x / scale (division in float32)."""
+    flat = _u16(words).ravel()
+    f = lib().oracle_quantize_e4m3
+    code = _DTYPES[dtype]
+    return np.array([f(int(b), code, float(scale)) for b in flat],
+                    dtype=np.uint8).reshape(np.shape(words))
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, num_blocks, H_kv, D, dtype,
+                          k_scale, v_scale):
+    """F3: quantizing scatter into copies of E4M3 caches; returns (k_cache', v_cache')."""
+    kc, vc = _u8(k_cache).copy(), _u8(v_cache).copy()
+    sm = _i32(slot_mapping)
+    rc = lib().oracle_reshape_and_cache_fp8(_u16(key), _u16(value), kc, vc, sm, len(sm),
+                                            num_blocks, H_kv, D, _DTYPES[dtype], k_scale, v_scale)
+    _check(rc, "reshape_and_cache_fp8")
+    return kc, vc
+
+
+def copy_blocks_fp8(k_cache, v_cache, mapping, num_blocks, H_kv, D):
+    """F4: whole-block copies on E4M3 caches; returns new (k_cache', v_cache')."""
+    kc, vc = _u8(k_cache).copy(), _u8(v_cache).copy()
+    mp = _i32(np.asarray(mapping).reshape(-1, 2))
+    rc = lib().oracle_copy_blocks_fp8(kc, vc, mp, mp.shape[0], num_blocks, H_kv, D)
+    _check(rc, "copy_blocks_fp8")
+    return kc, vc
+
+
+def gather_fp8(cache, table_row, L, kvh, num_blocks, H_kv, D, cache_scale):
+    """F5: contiguous float64 rows [L][D] of an E4M3 cache, times its scale."""
+    out = np.zeros((max(L, 1), D), dtype=np.float64)
+    rc = lib().oracle_gather_fp8(_u8(cache), _i32(table_row), L, kvh, num_blocks, H_kv, D,
+                                 cache_scale, out)
+    _check(rc, "gather_fp8")
+    return out[:L]
+
+
+def decode_fp8(query, k_cache, v_cache, block_tables, seq_lens, H_q, H_kv, D, num_blocks, dtype,
+               scale, k_scale, v_scale, pairs=None, nthreads=0):
+    """F6: paged decode over E4M3 caches. query [B][H_q][D] words of dtype."""
+    bt = _i32(block_tables)
+    B = bt.shape[0]
+    if pairs is None:
+        out = np.zeros((B, H_q, D), dtype=np.float64)
+        pp, n = None, 0
+    else:
+        pairs = _i32(np.asarray(pairs).reshape(-1, 2))
+        out = np.zeros((pairs.shape[0], D), dtype=np.float64)
+        pp, n = pairs.ctypes.data_as(ctypes.c_void_p), pairs.shape[0]
+    rc = lib().oracle_decode_fp8(_u16(query), _u8(k_cache), _u8(v_cache), bt, bt.shape[1],
+                                 _i32(seq_lens), B, H_q, H_kv, D, num_blocks, _DTYPES[dtype],
+                                 scale, k_scale, v_scale, pp, n, nthreads, out)
+    _check(rc, "decode_fp8")
+    return out
+
+
+def poison_free_slots_fp8(k_cache, v_cache, block_tables, seq_lens, num_blocks, H_kv, D):
+    """Copies of E4M3 caches with every slot that holds no valid token set to the NaN code."""
+    kc, vc = _u8(k_cache).copy(), _u8(v_cache).copy()
+    bt = _i32(block_tables)
+    n = lib().oracle_poison_free_slots_fp8(kc, vc, bt, bt.shape[1], _i32(seq_lens), bt.shape[0],
+                                           num_blocks, H_kv, D, NAN_E4M3)
+    if n < 0:
+        raise ValueError("oracle poison_free_slots_fp8: bad table entry")
     return kc, vc
 
 

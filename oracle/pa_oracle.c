@@ -16,12 +16,18 @@
  *   [OV]   devpress.csdn.net/amd vLLM overview: §3 PagedAttention (3) pseudo-code (per-block
  *          accumulation over the block table), §9 FlashAttention (4) online softmax (running max
  *          and running sum of exponentials, rescaled at the end).
+ *   [V1]   lilinji.mintlify.site lecture 34, "vLLM 生产级系统架构全景剖析…": §4.4 FP8 KV cache.
+ *   [OFP8] the OCP 8-bit floating point specification (not one of the pages): the E4M3 format.
  *
  * Cache layout (an interface fact, fixed by the library's header, restated here on its own):
  *   k_cache, v_cache: 16-bit words, [num_blocks][num_kv_heads][16][head_dim].
  *   The token in slot s lives in physical block s/16 at in-block offset s%16 ([MEM] Block Table
  *   数据结构: position -> physical_block*block_size + offset). The pages leave the arrangement of
  *   heads inside a block open; this layout keeps each (block, kv-head) tile contiguous.
+ *
+ * FP8 cache variant ([V1] lecture 34 §4.4: kv_cache_dtype="fp8" stores each key and value element
+ * in one E4M3 byte instead of two): caches of bytes in the same layout, each code the E4M3 value of
+ * x / scale for a per-cache scale; reading multiplies the value back by the scale.
  *
  * Readings where the pages are silent (each is listed with its reason in the design notes):
  *   - seq_lens counts the token being decoded, so the decode query attends positions 0..L-1
@@ -74,6 +80,63 @@ static size_t cache_at(int blk, int kvh, int off, int d, int H_kv, int D)
     return (((size_t)blk * H_kv + kvh) * OR_BLOCK + off) * D + d;
 }
 
+/* ---------------------------------------------------------------- F1: E4M3 codes ([OFP8])
+ * One byte: sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0. Exponent field 0 holds
+ * the subnormals m * 2^-9; S.1111.111 is NaN; there are no infinities, so the largest magnitude is
+ * 1.75 * 2^8 = 448 (code 0x7E). Every code decodes exactly into a double. */
+double oracle_e4m3_to_double(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);                /* subnormal: (m/8) * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10);      /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* The E4M3 code of a float: the nearest E4M3 value, a tie going to the even mantissa; magnitudes of
+ * 448 and above (infinities included) saturate to 448; NaN gives the NaN code with the input's sign.
+ * Below 2^-6 the grid spacing is 2^-9 (subnormals); in the binade [2^E, 2^(E+1)) it is 2^(E-3). */
+uint8_t oracle_e4m3_from_float(float x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x))
+        return sign | 0x7F;
+    double a = fabs((double)x);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int e;
+    frexp(a, &e);                                /* a = f * 2^e, f in [0.5, 1) */
+    int spacing = a < ldexp(1.0, -6) ? -9 : (e - 1) - 3;
+    double n = nearbyint(ldexp(a, -spacing));    /* round half to even (default mode) */
+    double v = ldexp(n, spacing);                /* the rounded magnitude, at most 448 */
+    if (v == 0.0)
+        return sign;
+    frexp(v, &e);
+    int E = e - 1;                               /* v = (1 + m/8) * 2^E, or subnormal */
+    if (E < -6)
+        return sign | (uint8_t)ldexp(v, 9);      /* m = v / 2^-9 */
+    int m = (int)(ldexp(v, -E) * 8.0) - 8;
+    return sign | (uint8_t)(((E + 7) << 3) | m);
+}
+
+/* F2: quantize one 16-bit element with a per-cache scale: the E4M3 code of x / scale, the division
+ * rounded to float32 (the precision the library takes this decision in). A NaN element keeps its
+ * sign in the NaN code. */
+uint8_t oracle_quantize_e4m3(uint16_t bits, int dtype, float scale)
+{
+    float x = (float)oracle_to_double(bits, dtype);  /* exact: both formats are floats */
+    if (isnan(x))
+        return oracle_e4m3_from_float(x);
+    float q = x / scale;
+    return oracle_e4m3_from_float(q);
+}
+
 /* ---------------------------------------------------------------- O2: scatter ([PD] §3.1; [MEM])
  * For every token t with slot_mapping[t] >= 0, copy its H_kv*D key and value words into slot
  * slot_mapping[t]. A bit copy: no arithmetic on the values. Slots in one call must be distinct and
@@ -109,12 +172,75 @@ int oracle_reshape_and_cache(const uint16_t *key, const uint16_t *value, uint16_
     return OR_OK;
 }
 
+/* F3: the scatter of O2 into E4M3 caches: the element written to the slot is the code of F2 with
+ * k_scale for keys and v_scale for values ([V1] §4.4: one byte per key and value element). */
+int oracle_reshape_and_cache_fp8(const uint16_t *key, const uint16_t *value, uint8_t *k_cache,
+                                 uint8_t *v_cache, const int32_t *slot_mapping, int T,
+                                 int num_blocks, int H_kv, int D, int dtype, float k_scale,
+                                 float v_scale)
+{
+    if (T < 0 || num_blocks < 0 || H_kv <= 0 || D <= 0 || !(k_scale > 0) || !(v_scale > 0))
+        return OR_BAD_ARG;
+    for (int t = 0; t < T; ++t) {
+        int32_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        if ((int64_t)s >= (int64_t)num_blocks * OR_BLOCK)
+            return OR_BAD_INDEX;
+        for (int u = 0; u < t; ++u)
+            if (slot_mapping[u] == s)
+                return OR_DUP_SLOT;
+    }
+    for (int t = 0; t < T; ++t) {
+        int32_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        int blk = s / OR_BLOCK, off = s % OR_BLOCK;
+        for (int g = 0; g < H_kv; ++g)
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)t * H_kv + g) * D + d;
+                k_cache[cache_at(blk, g, off, d, H_kv, D)] = oracle_quantize_e4m3(key[src], dtype, k_scale);
+                v_cache[cache_at(blk, g, off, d, H_kv, D)] = oracle_quantize_e4m3(value[src], dtype, v_scale);
+            }
+    }
+    return OR_OK;
+}
+
 /* ---------------------------------------------------------------- O3: copy-on-write ([MEM] 机制 2)
  * For each (src, dst) pair copy the whole physical block -- all 16 slots, all kv heads -- in both
  * caches. Destinations must be distinct and no destination may also be a source, so the result does
  * not depend on the order of the pairs. */
 int oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int32_t *mapping, int n,
                        int num_blocks, int H_kv, int D)
+{
+    if (n < 0 || num_blocks < 0 || H_kv <= 0 || D <= 0)
+        return OR_BAD_ARG;
+    for (int i = 0; i < n; ++i) {
+        int32_t s = mapping[2 * i], d = mapping[2 * i + 1];
+        if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+            return OR_BAD_INDEX;
+        for (int j = 0; j < n; ++j) {
+            if (j != i && mapping[2 * j + 1] == d)
+                return OR_BAD_MAPPING;
+            if (mapping[2 * j] == d)
+                return OR_BAD_MAPPING;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        int32_t s = mapping[2 * i], d = mapping[2 * i + 1];
+        for (int g = 0; g < H_kv; ++g)
+            for (int off = 0; off < OR_BLOCK; ++off)
+                for (int e = 0; e < D; ++e) {
+                    k_cache[cache_at(d, g, off, e, H_kv, D)] = k_cache[cache_at(s, g, off, e, H_kv, D)];
+                    v_cache[cache_at(d, g, off, e, H_kv, D)] = v_cache[cache_at(s, g, off, e, H_kv, D)];
+                }
+    }
+    return OR_OK;
+}
+
+/* F4: O3 on E4M3 caches (one byte per element): the same whole-block copies. */
+int oracle_copy_blocks_fp8(uint8_t *k_cache, uint8_t *v_cache, const int32_t *mapping, int n,
+                           int num_blocks, int H_kv, int D)
 {
     if (n < 0 || num_blocks < 0 || H_kv <= 0 || D <= 0)
         return OR_BAD_ARG;
@@ -153,6 +279,22 @@ int oracle_gather(const uint16_t *cache, const int32_t *table_row, int L, int kv
             return OR_BAD_INDEX;
         for (int d = 0; d < D; ++d)
             out[(size_t)i * D + d] = oracle_to_double(cache[cache_at(blk, kvh, i % OR_BLOCK, d, H_kv, D)], dtype);
+    }
+    return OR_OK;
+}
+
+/* F5: O4 on an E4M3 cache: each element is its code's value times the cache's scale (exact in
+ * double: at most 4 significant bits times a float). */
+int oracle_gather_fp8(const uint8_t *cache, const int32_t *table_row, int L, int kvh,
+                      int num_blocks, int H_kv, int D, double cache_scale, double *out)
+{
+    for (int i = 0; i < L; ++i) {
+        int32_t blk = table_row[i / OR_BLOCK];
+        if (blk < 0 || blk >= num_blocks)
+            return OR_BAD_INDEX;
+        for (int d = 0; d < D; ++d)
+            out[(size_t)i * D + d] =
+                oracle_e4m3_to_double(cache[cache_at(blk, kvh, i % OR_BLOCK, d, H_kv, D)]) * cache_scale;
     }
     return OR_OK;
 }
@@ -198,11 +340,22 @@ int oracle_attention(const double *q, const double *K, const double *V, int L, i
  * For sequence s and query head h: gather rows 0..seq_lens[s]-1 of kv head h/(H_q/H_kv) through the
  * block table ([MEM] Block 映射, [PD] §3.4) and apply O5 to query row q[s][h] ([PD] §3.1).
  * `pairs` lists the (s, h) pairs to evaluate ([n_pairs][2]); NULL means every pair in order.
- * out is [n_pairs][D] (or [B][H_q][D] when pairs is NULL). */
-int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
-                  const int32_t *block_tables, int max_blocks, const int32_t *seq_lens, int B,
-                  int H_q, int H_kv, int D, int num_blocks, int dtype, double scale,
-                  const int32_t *pairs, int n_pairs, int nthreads, double *out)
+ * out is [n_pairs][D] (or [B][H_q][D] when pairs is NULL). With fp8 set the caches hold E4M3 codes
+ * read through F5 with k_scale and v_scale; otherwise 16-bit words of `dtype`. */
+static int gather_kv(const void *cache, int fp8, double cache_scale, const int32_t *row, int L,
+                     int kvh, int num_blocks, int H_kv, int D, int dtype, double *out)
+{
+    if (fp8)
+        return oracle_gather_fp8((const uint8_t *)cache, row, L, kvh, num_blocks, H_kv, D,
+                                 cache_scale, out);
+    return oracle_gather((const uint16_t *)cache, row, L, kvh, num_blocks, H_kv, D, dtype, out);
+}
+
+static int decode_pairs(const uint16_t *query, const void *k_cache, const void *v_cache, int fp8,
+                        double k_scale, double v_scale, const int32_t *block_tables,
+                        int max_blocks, const int32_t *seq_lens, int B, int H_q, int H_kv, int D,
+                        int num_blocks, int dtype, double scale, const int32_t *pairs,
+                        int n_pairs, int nthreads, double *out)
 {
     if (B < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
         return OR_BAD_ARG;
@@ -232,9 +385,11 @@ int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t
                     rc = OR_NO_MEM;
                 } else {
                     const int32_t *row = block_tables + (size_t)s * max_blocks;
-                    rc = oracle_gather(k_cache, row, L, h / group, num_blocks, H_kv, D, dtype, K);
+                    rc = gather_kv(k_cache, fp8, k_scale, row, L, h / group, num_blocks, H_kv, D,
+                                   dtype, K);
                     if (rc == OR_OK)
-                        rc = oracle_gather(v_cache, row, L, h / group, num_blocks, H_kv, D, dtype, V);
+                        rc = gather_kv(v_cache, fp8, v_scale, row, L, h / group, num_blocks, H_kv,
+                                       D, dtype, V);
                     for (int d = 0; d < D; ++d)
                         q[d] = oracle_to_double(query[((size_t)s * H_q + h) * D + d], dtype);
                     if (rc == OR_OK)
@@ -253,6 +408,29 @@ int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t
         }
     }
     return status;
+}
+
+int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *block_tables, int max_blocks, const int32_t *seq_lens, int B,
+                  int H_q, int H_kv, int D, int num_blocks, int dtype, double scale,
+                  const int32_t *pairs, int n_pairs, int nthreads, double *out)
+{
+    return decode_pairs(query, k_cache, v_cache, 0, 1.0, 1.0, block_tables, max_blocks, seq_lens,
+                        B, H_q, H_kv, D, num_blocks, dtype, scale, pairs, n_pairs, nthreads, out);
+}
+
+/* F6: O6 over E4M3 caches ([V1] §4.4); query and output stay in `dtype`. */
+int oracle_decode_fp8(const uint16_t *query, const uint8_t *k_cache, const uint8_t *v_cache,
+                      const int32_t *block_tables, int max_blocks, const int32_t *seq_lens, int B,
+                      int H_q, int H_kv, int D, int num_blocks, int dtype, double scale,
+                      double k_scale, double v_scale, const int32_t *pairs, int n_pairs,
+                      int nthreads, double *out)
+{
+    if (!(k_scale > 0) || !(v_scale > 0))
+        return OR_BAD_ARG;
+    return decode_pairs(query, k_cache, v_cache, 1, k_scale, v_scale, block_tables, max_blocks,
+                        seq_lens, B, H_q, H_kv, D, num_blocks, dtype, scale, pairs, n_pairs,
+                        nthreads, out);
 }
 
 /* ---------------------------------------------------------------- O7: paged causal prefill chunk
@@ -391,12 +569,12 @@ int oracle_split_merge(const double *q, const double *K, const double *V, int L,
 
 /* ---------------------------------------------------------------- test helper: poison free slots
  * Overwrite every slot of both caches that holds no valid token -- no sequence s has a position
- * i < seq_lens[s] mapped to it by its table -- with the 16-bit word `pattern` (a NaN code for the
- * caller's dtype). Attention must never read such a slot, so a kernel that does turns a finite
+ * i < seq_lens[s] mapped to it by its table -- with the element `pattern` (a NaN code for the
+ * cache's element type). Attention must never read such a slot, so a kernel that does turns a finite
  * result into NaN. Returns the number of poisoned slots, or -1 on a bad table entry. */
-long oracle_poison_free_slots(uint16_t *k_cache, uint16_t *v_cache, const int32_t *block_tables,
-                              int max_blocks, const int32_t *seq_lens, int S, int num_blocks,
-                              int H_kv, int D, uint16_t pattern)
+static long poison_slots(void *k_cache, void *v_cache, int esize, unsigned pattern,
+                         const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                         int S, int num_blocks, int H_kv, int D)
 {
     unsigned char *used = (unsigned char *)calloc((size_t)num_blocks * OR_BLOCK, 1);
     if (!used)
@@ -418,12 +596,34 @@ long oracle_poison_free_slots(uint16_t *k_cache, uint16_t *v_cache, const int32_
             ++count;
             for (int g = 0; g < H_kv; ++g)
                 for (int d = 0; d < D; ++d) {
-                    k_cache[cache_at(blk, g, off, d, H_kv, D)] = pattern;
-                    v_cache[cache_at(blk, g, off, d, H_kv, D)] = pattern;
+                    size_t at = cache_at(blk, g, off, d, H_kv, D);
+                    if (esize == 2) {
+                        ((uint16_t *)k_cache)[at] = (uint16_t)pattern;
+                        ((uint16_t *)v_cache)[at] = (uint16_t)pattern;
+                    } else {
+                        ((uint8_t *)k_cache)[at] = (uint8_t)pattern;
+                        ((uint8_t *)v_cache)[at] = (uint8_t)pattern;
+                    }
                 }
         }
     free(used);
     return count;
+}
+
+long oracle_poison_free_slots(uint16_t *k_cache, uint16_t *v_cache, const int32_t *block_tables,
+                              int max_blocks, const int32_t *seq_lens, int S, int num_blocks,
+                              int H_kv, int D, uint16_t pattern)
+{
+    return poison_slots(k_cache, v_cache, 2, pattern, block_tables, max_blocks, seq_lens, S,
+                        num_blocks, H_kv, D);
+}
+
+long oracle_poison_free_slots_fp8(uint8_t *k_cache, uint8_t *v_cache, const int32_t *block_tables,
+                                  int max_blocks, const int32_t *seq_lens, int S, int num_blocks,
+                                  int H_kv, int D, uint8_t pattern)
+{
+    return poison_slots(k_cache, v_cache, 1, pattern, block_tables, max_blocks, seq_lens, S,
+                        num_blocks, H_kv, D);
 }
 
 int oracle_max_threads(void)
