@@ -66,6 +66,8 @@ def lib():
         L.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
         L.oracle_quantize_e4m3.restype = ctypes.c_uint8
         L.oracle_quantize_e4m3.argtypes = [ctypes.c_uint16, _c_int, ctypes.c_float]
+        L.oracle_quantize_e4m3_n.restype = None
+        L.oracle_quantize_e4m3_n.argtypes = [_u16p, ctypes.c_long, _c_int, ctypes.c_float, _u8p]
         L.oracle_reshape_and_cache_fp8.argtypes = [_u16p, _u16p, _u8p, _u8p, _i32p, _c_int,
                                                    _c_int, _c_int, _c_int, _c_int, ctypes.c_float,
                                                    ctypes.c_float]
@@ -237,10 +239,9 @@ def e4m3_from_float(x):
 def quantize_e4m3(words, dtype, scale):
     """F2: 16-bit words (any shape) to the E4M3 codes of x / scale (division in float32)."""
     flat = _u16(words).ravel()
-    f = lib().oracle_quantize_e4m3
-    code = _DTYPES[dtype]
-    return np.array([f(int(b), code, float(scale)) for b in flat],
-                    dtype=np.uint8).reshape(np.shape(words))
+    out = np.empty(flat.size, dtype=np.uint8)
+    lib().oracle_quantize_e4m3_n(flat, flat.size, _DTYPES[dtype], float(scale), out)
+    return out.reshape(np.shape(words))
 
 
 def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, num_blocks, H_kv, D, dtype,

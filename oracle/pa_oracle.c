@@ -172,6 +172,16 @@ int oracle_reshape_and_cache(const uint16_t *key, const uint16_t *value, uint16_
     return OR_OK;
 }
 
+/* F2 over an array of n elements (OpenMP over elements; each element is independent). */
+void oracle_quantize_e4m3_n(const uint16_t *bits, long n, int dtype, float scale, uint8_t *out)
+{
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (long i = 0; i < n; ++i)
+        out[i] = oracle_quantize_e4m3(bits[i], dtype, scale);
+}
+
 /* F3: the scatter of O2 into E4M3 caches: the element written to the slot is the code of F2 with
  * k_scale for keys and v_scale for values ([V1] §4.4: one byte per key and value element). */
 int oracle_reshape_and_cache_fp8(const uint16_t *key, const uint16_t *value, uint8_t *k_cache,
