@@ -13,7 +13,8 @@
  *   [OV]  devpress.csdn.net/amd vLLM overview: per-block attention over the block table (§3 (3))
  *         combined with a running maximum and sum of exponentials (§9 (4) online softmax).
  *   [V1]  lilinji.mintlify.site lecture 34 "vLLM 生产级系统架构全景剖析…": §2.2 shared prefixes
- *         and block reference counts.
+ *         and block reference counts; §4.4 the FP8 (E4M3) KV cache, one byte per key and value
+ *         element (kv_cache_dtype="fp8").
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -23,6 +24,12 @@
  *  - 16-bit element type: PA_DTYPE_F16 (IEEE binary16) or PA_DTYPE_BF16 (bfloat16). Queries, keys,
  *    values, caches and outputs all share it. Arithmetic is float32; outputs are rounded to nearest
  *    even.
+ *  - FP8 caches ([V1] §4.4): the *_fp8 entry points keep k_cache and v_cache as E4M3 codes (the OCP
+ *    8-bit format: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, largest
+ *    magnitude 448, S.1111.111 = NaN), one byte per element, same layout. Element = code value *
+ *    k_scale (keys) or * v_scale (values), one finite positive scale per cache chosen by the caller.
+ *    Their `dtype` argument is the 16-bit type of queries, new keys/values and outputs.
+ *    pa_copy_blocks takes PA_DTYPE_FP8_E4M3 for such caches.
  *  - Cache layout: k_cache and v_cache are [num_blocks][num_kv_heads][PA_BLOCK_SIZE][head_dim].
  *    Slot s (the storage position of a token, physical_block * 16 + offset, [MEM] Block Table
  *    数据结构) is block s / 16, in-block offset s % 16; each (block, kv head) tile of 16 rows is
@@ -62,7 +69,7 @@ typedef enum {
     PA_ERR_HIP = 4
 } pa_status_t;
 
-typedef enum { PA_DTYPE_F16 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+typedef enum { PA_DTYPE_F16 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_dtype_t;
 
 /*
  * pa_reshape_and_cache -- write the new tokens' keys and values into their cache slots.
@@ -88,6 +95,7 @@ pa_status_t pa_reshape_and_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t n
  *                 -- is copied to block dst, in both caches, bit for bit. Destinations must be
  *                 distinct and no destination may also be a source (the order of the copies is then
  *                 irrelevant).
+ * dtype may be PA_DTYPE_FP8_E4M3 (caches of E4M3 codes: a block is then half as many bytes).
  * num_pairs == 0 is a no-op.
  */
 pa_status_t pa_copy_blocks(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
@@ -180,6 +188,34 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
                              const int32_t *seq_lens, const int32_t *cu_q_lens,
                              int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                              int32_t num_q_heads, float scale, void *stream);
+
+/*
+ * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into E4M3 caches ([V1] §4.4).
+ * key and value are [num_tokens][num_kv_heads][head_dim] elements of `dtype` (F16 or BF16). The
+ * byte written for element x is the E4M3 code of x / k_scale (keys) or x / v_scale (values): the
+ * quotient rounded to float32, then to the nearest E4M3 value with ties to the even code;
+ * magnitudes of 448 and more (infinities included) saturate to 448, and NaN gives code 0x7F with
+ * x's sign. slot_mapping as in pa_reshape_and_cache. k_scale and v_scale: finite and positive.
+ */
+pa_status_t pa_reshape_and_cache_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                     int32_t head_dim, const void *key, const void *value,
+                                     void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                     int32_t num_tokens, float k_scale, float v_scale,
+                                     void *stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over E4M3 caches ([V1] §4.4): keys and values are read as code value
+ * times k_scale / v_scale, everything else as in pa_decode (query and out of `dtype`, the same
+ * workspace size function, partition_size rules and errors). Head groups of any size run; there is
+ * no shared-prefix variant for E4M3 caches.
+ */
+pa_status_t pa_decode_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, void *out, const void *query, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                          int32_t max_seq_len, int32_t num_q_heads, float scale, float k_scale,
+                          float v_scale, int32_t partition_size, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *pa_status_string(pa_status_t status);

@@ -6,7 +6,8 @@ non-zero status. All work runs in the library's HIP kernels; there is no fallbac
 fails loudly when the library has not been built.
 
 Tensors are torch tensors on the GPU: float16 or bfloat16 for queries/keys/values/caches/outputs,
-int32 for tables and index arrays. Caches have shape [num_blocks, num_kv_heads, 16, head_dim].
+int32 for tables and index arrays. Caches have shape [num_blocks, num_kv_heads, 16, head_dim]. The
+``*_fp8`` wrappers take E4M3 caches as uint8 (or float8_e4m3fn) tensors of that shape.
 """
 from __future__ import annotations
 
@@ -22,6 +23,8 @@ BLOCK_SIZE = 16
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 _DTYPE = {torch.float16: 0, torch.bfloat16: 1}
+PA_DTYPE_FP8_E4M3 = 2
+FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 _lib = None
 
@@ -62,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_shared_prefix.restype = _i
         L.pa_decode_shared_prefix.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i,
                                               _p, _p, _i, _i, _i, _i, _f, _i, _p, _sz, _p]
+        L.pa_reshape_and_cache_fp8.restype = _i
+        L.pa_reshape_and_cache_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _f, _f, _p]
+        L.pa_decode_fp8.restype = _i
+        L.pa_decode_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _f,
+                                    _f, _i, _p, _sz, _p]
         L.pa_prefill_chunk.restype = _i
         L.pa_prefill_chunk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _i,
                                        _i, _f, _p]
@@ -86,18 +94,23 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor, fp8: bool = False):
+    """(pa dtype, num_blocks, num_kv_heads, head_dim) of a pair of caches: 16-bit caches, or with
+    fp8 set E4M3 caches (dtype then PA_DTYPE_FP8_E4M3)."""
     if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE:
         raise ValueError("caches must be [num_blocks, num_kv_heads, 16, head_dim]")
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache differ in shape or dtype")
-    if k_cache.dtype not in _DTYPE:
+    if fp8:
+        if k_cache.dtype not in FP8_CACHE_DTYPES:
+            raise ValueError(f"E4M3 cache dtype {k_cache.dtype}: uint8 or float8_e4m3fn")
+    elif k_cache.dtype not in _DTYPE:
         raise ValueError(f"cache dtype {k_cache.dtype}: float16 or bfloat16")
     for t in (k_cache, v_cache):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("caches must be contiguous GPU tensors")
     nb, hkv, _, d = k_cache.shape
-    return _DTYPE[k_cache.dtype], int(nb), int(hkv), int(d)
+    return (PA_DTYPE_FP8_E4M3 if fp8 else _DTYPE[k_cache.dtype]), int(nb), int(hkv), int(d)
 
 
 def _gpu(t: torch.Tensor, name: str, dtype=None) -> None:
@@ -122,8 +135,9 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -
 
 
 def copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
-    """pa_copy_blocks: whole-block copies of the (src, dst) rows of block_mapping [N, 2] int32."""
-    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    """pa_copy_blocks: whole-block copies of the (src, dst) rows of block_mapping [N, 2] int32;
+    16-bit or E4M3 (uint8 / float8_e4m3fn) caches."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=k_cache.dtype in FP8_CACHE_DTYPES)
     _gpu(block_mapping, "block_mapping", torch.int32)
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [N, 2]")
@@ -237,3 +251,57 @@ def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_len
                                   int(block_tables.shape[1]), seq_lens.data_ptr(),
                                   cu_q_lens.data_ptr(), S, tq, int(max_q_len), hq, float(scale),
                                   _stream(stream)))
+
+
+# ------------------------------------------------------------------------- E4M3 caches
+def _act_dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"{name} dtype {t.dtype}: float16 or bfloat16")
+    return _DTYPE[t.dtype]
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: float,
+                          v_scale: float, stream=None) -> None:
+    """pa_reshape_and_cache_fp8: key/value [T, H_kv, D] (float16/bfloat16) quantized to E4M3 codes
+    of x / k_scale and x / v_scale in the slots slot_mapping[T]."""
+    _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=True)
+    dt = _act_dtype(key, "key")
+    T = int(slot_mapping.shape[0])
+    for t, n in ((key, "key"), (value, "value")):
+        _gpu(t, n, key.dtype)
+        if tuple(t.shape) != (T, hkv, d):
+            raise ValueError(f"{n} must be [{T}, {hkv}, {d}]")
+    _gpu(slot_mapping, "slot_mapping", torch.int32)
+    _check(lib().pa_reshape_and_cache_fp8(dt, nb, hkv, d, key.data_ptr(), value.data_ptr(),
+                                          k_cache.data_ptr(), v_cache.data_ptr(),
+                                          slot_mapping.data_ptr(), T, float(k_scale),
+                                          float(v_scale), _stream(stream)))
+
+
+def decode_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+               scale: float, k_scale: float, v_scale: float,
+               partition_size: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> None:
+    """pa_decode_fp8: pa_decode over E4M3 caches (elements = code value * k_scale / v_scale)."""
+    _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=True)
+    dt = _act_dtype(query, "query")
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, query.dtype)
+        if tuple(t.shape) != (B, hq, d):
+            raise ValueError(f"{n} must be [{B}, {hq}, {d}]")
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(seq_lens, "seq_lens", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
+    if partition_size is None:
+        partition_size = default_partition_size(max_seq_len)
+    need = decode_workspace_size(B, hq, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = alloc_decode_workspace(B, hq, d, max_seq_len, partition_size, query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_fp8(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
+                               k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                               int(block_tables.shape[1]), seq_lens.data_ptr(), B,
+                               int(max_seq_len), hq, float(scale), float(k_scale), float(v_scale),
+                               int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -2,7 +2,8 @@
 //
 // openeuler.csdn.net "高并发 AI 服务的内存瓶颈", section 机制 2 写时复制: sequences that share a
 // prompt's blocks (reference-counted) get a private copy of a block where they diverge. The whole
-// block -- 16 slots x all kv heads, filled or not -- is copied in both caches, bit for bit.
+// block -- 16 slots x all kv heads, filled or not -- is copied in both caches, bit for bit (16-bit
+// or E4M3 elements alike).
 //
 // Grid: x = pair, y = 16 KiB piece of the block, z = cache (0: K, 1: V). Each thread moves four
 // 16-byte vectors, issuing all four loads before the stores.
@@ -50,7 +51,7 @@ hipError_t launch_copy_blocks(const CacheDims &c, void *k_cache, void *v_cache,
 {
     if (num_pairs == 0)
         return hipSuccess;
-    const int32_t vec_per_block = c.num_kv_heads * kBlock * c.head_dim / 8;
+    const int32_t vec_per_block = c.num_kv_heads * kBlock * c.head_dim * (c.fp8 ? 1 : 2) / 16;
     const int32_t pieces = (vec_per_block + kVecPerWg - 1) / kVecPerWg;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, pieces, 2), dim3(kThreads), 0, stream,
                        (uint4 *)k_cache, (uint4 *)v_cache, block_mapping, c.num_blocks,

@@ -18,6 +18,11 @@
 // classes are merged once at the end of the unit. The next tile's loads are issued before the
 // current tile is consumed.
 //
+// E4M3 caches (lecture 34 "vLLM 生产级系统架构全景剖析" §4.4): the same kernel with one byte per
+// element, so a lane's 16-byte piece holds 16 dims; keys are widened to 16-bit pairs
+// (v_cvt_scalef32_pk_*_fp8) for the dot products and values to float32 (v_cvt_pk_f32_fp8), exact
+// conversions; k_scale is folded into the score scale and v_scale into the output.
+//
 // Split-K: with partition_size P > 0 the unit covers tokens [part*P, (part+1)*P) and writes its
 // unnormalised accumulator, max and sum (log2 domain) to the workspace; a merge kernel rescales the
 // parts of each (sequence, head) to their common maximum and normalises.
@@ -49,7 +54,8 @@ struct DecodeParams {
     int32_t n_sub;        // query-head subgroups per kv head
     int32_t n_units;
     int32_t split;
-    float scale_log2;     // scale * log2(e): scores live in the log2 domain
+    float scale_log2;     // scale * log2(e) (* k_scale for E4M3 caches): scores in the log2 domain
+    float v_scale;        // E4M3 caches: value scale, applied to the accumulated output
     // Shared-prefix (cascade) support; zero / null for a plain decode.
     const int32_t *__restrict__ seq_starts;   // [num_seqs] first position of a unit's range
     const int32_t *__restrict__ group_starts; // [num_groups + 1] members of prefix group g
@@ -66,12 +72,16 @@ __device__ __forceinline__ int unit_start(const DecodeParams &p, int seq, int L)
     return p.seq_starts ? min(max(p.seq_starts[seq], 0), L) : 0;
 }
 
-template <bool BF, int D, int GK>
+// F8: the caches hold E4M3 codes (one byte per element) instead of 16-bit elements.
+template <bool BF, bool F8, int D, int GK>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
 {
-    constexpr int RL = D / 8;            // lanes per token row (8 elements = 16 bytes each)
+    constexpr int EPL = F8 ? 16 : 8;     // cache elements per 16-byte piece = dims per lane
+    constexpr int RL = D / EPL;          // lanes per token row
     constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
     constexpr int NCH = kBlock / ROWS;   // loads per (block, kv head) tile
+    constexpr int QV = EPL / 8;          // 16-byte query pieces per lane and head
+    constexpr int ESZ = F8 ? 1 : 2;      // bytes per cache element
     const int lane = threadIdx.x;
     const int r = lane / RL;
 
@@ -92,25 +102,30 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
         return;  // a part with no tokens: the merge never reads it
     const int t1 = min(L, t0 + p.part_tokens);
 
-    uint4 q[GK];
+    uint4 q[GK][QV];
 #pragma unroll
     for (int h = 0; h < GK; ++h)
-        q[h] = *(const uint4 *)(p.query + ((size_t)seq * p.num_q_heads + h0 + h) * D +
-                                (lane % RL) * 8);
+#pragma unroll
+        for (int k = 0; k < QV; ++k)
+            q[h][k] = *(const uint4 *)(p.query + ((size_t)seq * p.num_q_heads + h0 + h) * D +
+                                       (lane % RL) * EPL + k * 8);
 
-    float m[GK], l[GK], acc[GK][8];
+    float m[GK], l[GK], acc[GK][EPL];
 #pragma unroll
     for (int h = 0; h < GK; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < EPL; ++j)
             acc[h][j] = 0.0f;
     }
 
     const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
-    const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D;
-    const size_t tile_off = (size_t)kvh * kBlock * D + lane * 8;
+    const uint8_t *kbase = (const uint8_t *)p.k_cache;
+    const uint8_t *vbase = (const uint8_t *)p.v_cache;
+    // byte offsets: lane l reads piece l % RL of row l / RL of each 1 KiB load
+    const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D * ESZ;
+    const size_t tile_off = ((size_t)kvh * kBlock * D + lane * EPL) * ESZ;
 
     for (int bb = t0 / kBlock; bb * kBlock < t1; bb += kWave) {
         const int nb = min(kWave, (t1 - bb * kBlock + kBlock - 1) / kBlock);
@@ -119,12 +134,12 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
         auto load = [&](int k, uint4(&kk)[NCH], uint4(&vv)[NCH]) {
             int blk = __builtin_amdgcn_readlane(my_blk, k);
             blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
-            const uint16_t *kp = p.k_cache + blk * block_stride + tile_off;
-            const uint16_t *vp = p.v_cache + blk * block_stride + tile_off;
+            const uint8_t *kp = kbase + blk * block_stride + tile_off;
+            const uint8_t *vp = vbase + blk * block_stride + tile_off;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                kk[i] = load_nt(kp + i * ROWS * D);
-                vv[i] = load_nt(vp + i * ROWS * D);
+                kk[i] = load_nt(kp + i * 1024);
+                vv[i] = load_nt(vp + i * 1024);
             }
         };
 
@@ -136,8 +151,14 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
 #pragma unroll
             for (int h = 0; h < GK; ++h)
 #pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    s[h][i] = group_sum<RL>(dot8<BF>(q[h], kk[i])) * p.scale_log2;
+                for (int i = 0; i < NCH; ++i) {
+                    float d;
+                    if constexpr (F8)
+                        d = dot16_e4m3<BF>(q[h], kk[i]);
+                    else
+                        d = dot8<BF>(q[h][0], kk[i]);
+                    s[h][i] = group_sum<RL>(d) * p.scale_log2;
+                }
             if (!(good_blk && base >= t0 && base + kBlock <= t1)) {  // an edge block or a bad id
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
@@ -169,7 +190,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
                 l[h] = l[h] * alpha + psum;
                 m[h] = mn;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < EPL; ++j)
                     acc[h][j] *= alpha;
             }
 #pragma unroll
@@ -177,11 +198,21 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
                 const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float v0 = lo_f32<BF>(w[j]), v1 = hi_f32<BF>(w[j]);
+                    if constexpr (F8) {
+                        float v[4];
+                        e4m3x4_to_f32(w[j], v);
 #pragma unroll
-                    for (int h = 0; h < GK; ++h) {
-                        acc[h][2 * j] += pr[h][i] * v0;
-                        acc[h][2 * j + 1] += pr[h][i] * v1;
+                        for (int h = 0; h < GK; ++h)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[h][4 * j + e] += pr[h][i] * v[e];
+                    } else {
+                        const float v0 = lo_f32<BF>(w[j]), v1 = hi_f32<BF>(w[j]);
+#pragma unroll
+                        for (int h = 0; h < GK; ++h) {
+                            acc[h][2 * j] += pr[h][i] * v0;
+                            acc[h][2 * j + 1] += pr[h][i] * v1;
+                        }
                     }
                 }
             }
@@ -214,12 +245,12 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
         for (int off = RL; off < kWave; off <<= 1)
             lh += xor_shfl(lh, off);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < EPL; ++j) {
             float a = acc[h][j] * f;
 #pragma unroll
             for (int off = RL; off < kWave; off <<= 1)
                 a += xor_shfl(a, off);
-            acc[h][j] = a;
+            acc[h][j] = F8 ? a * p.v_scale : a;
         }
         m[h] = M;
         l[h] = lh;
@@ -231,19 +262,24 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
             const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
             if (p.split) {
                 const size_t slot = row * p.ws_slots + p.slot_base + part;
-                float *wa = p.ws_acc + slot * D + lane * 8;
-                *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-                *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                float *wa = p.ws_acc + slot * D + lane * EPL;
+#pragma unroll
+                for (int j = 0; j < EPL; j += 4)
+                    *(float4 *)(wa + j) =
+                        make_float4(acc[h][j], acc[h][j + 1], acc[h][j + 2], acc[h][j + 3]);
                 if (lane == 0)
                     *(float2 *)(p.ws_ml + slot * 2) = make_float2(m[h], l[h]);
             } else {
                 const float inv = l[h] > 0.0f ? 1.0f / l[h] : 0.0f;
-                uint4 o;
-                o.x = pack2<BF>(acc[h][0] * inv, acc[h][1] * inv);
-                o.y = pack2<BF>(acc[h][2] * inv, acc[h][3] * inv);
-                o.z = pack2<BF>(acc[h][4] * inv, acc[h][5] * inv);
-                o.w = pack2<BF>(acc[h][6] * inv, acc[h][7] * inv);
-                *(uint4 *)(p.out + row * D + lane * 8) = o;
+#pragma unroll
+                for (int j = 0; j < EPL; j += 8) {
+                    uint4 o;
+                    o.x = pack2<BF>(acc[h][j] * inv, acc[h][j + 1] * inv);
+                    o.y = pack2<BF>(acc[h][j + 2] * inv, acc[h][j + 3] * inv);
+                    o.z = pack2<BF>(acc[h][j + 4] * inv, acc[h][j + 5] * inv);
+                    o.w = pack2<BF>(acc[h][j + 6] * inv, acc[h][j + 7] * inv);
+                    *(uint4 *)(p.out + row * D + lane * EPL + j) = o;
+                }
             }
         }
     }
@@ -646,46 +682,56 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
         *dst = (uint16_t)to_word<BF>(o[0] * inv);
 }
 
-template <bool BF, int D, int GK>
+template <bool BF, bool F8, int D, int GK>
 hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
 {
     const int grid = round_up8(p.n_units);
-    if constexpr (GK >= 4)
+    if constexpr (GK >= 4 && !F8)
         hipLaunchKernelGGL((decode_gqa_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_partition_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0,
+        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>), dim3(grid), dim3(kWave), 0,
                            stream, p);
     return hipGetLastError();
 }
 
-template <bool BF, int D>
+template <bool BF, bool F8, int D>
 hipError_t launch_units_gk(int gk, const DecodeParams &p, hipStream_t stream)
 {
-    switch (gk) {
-    case 8: return launch_units<BF, D, 8>(p, stream);
-    case 4: return launch_units<BF, D, 4>(p, stream);
-    case 2: return launch_units<BF, D, 2>(p, stream);
-    default: return launch_units<BF, D, 1>(p, stream);
+    if constexpr (F8) {  // E4M3 caches: the per-row-class kernel for head groups up to 4
+        switch (gk) {
+        case 4: return launch_units<BF, true, D, 4>(p, stream);
+        case 2: return launch_units<BF, true, D, 2>(p, stream);
+        default: return launch_units<BF, true, D, 1>(p, stream);
+        }
+    } else {
+        switch (gk) {
+        case 8: return launch_units<BF, false, D, 8>(p, stream);
+        case 4: return launch_units<BF, false, D, 4>(p, stream);
+        case 2: return launch_units<BF, false, D, 2>(p, stream);
+        default: return launch_units<BF, false, D, 1>(p, stream);
+        }
     }
 }
 
-template <bool BF, int D>
+template <bool BF, bool F8, int D>
 hipError_t run_decode(int gk, int gkp, const DecodeParams &p, const DecodeParams *pre,
                       hipStream_t stream)
 {
     hipError_t e;
-    if (pre) {
-        const int grid = round_up8(pre->n_units);
-        if (gkp == 8)
-            hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 8>), dim3(grid), dim3(kWave), 0,
-                               stream, *pre);
-        else
-            hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 4>), dim3(grid), dim3(kWave), 0,
-                               stream, *pre);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
+    if constexpr (!F8) {  // shared-prefix units exist for 16-bit caches only
+        if (pre) {
+            const int grid = round_up8(pre->n_units);
+            if (gkp == 8)
+                hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 8>), dim3(grid), dim3(kWave), 0,
+                                   stream, *pre);
+            else
+                hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 4>), dim3(grid), dim3(kWave), 0,
+                                   stream, *pre);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
     }
-    if ((e = launch_units_gk<BF, D>(gk, p, stream)) != hipSuccess || !p.split)
+    if ((e = launch_units_gk<BF, F8, D>(gk, p, stream)) != hipSuccess || !p.split)
         return e;
     const int rows = p.num_seqs * p.num_q_heads;
     hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
@@ -704,8 +750,10 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (d.num_seqs == 0)
         return hipSuccess;
     const int group = d.num_q_heads / d.c.num_kv_heads;
-    const int gk = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    const int gk = group % 8 == 0 && !d.fp8 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
     const bool cascade = d.group_starts != nullptr && d.num_groups > 0;
+    if (d.fp8 && cascade)
+        return hipErrorInvalidValue;  // no shared-prefix kernel for E4M3 caches
     DecodeParams p = {};
     p.query = (const uint16_t *)d.query;
     p.k_cache = (const uint16_t *)d.k_cache;
@@ -721,7 +769,8 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.num_q_heads = d.num_q_heads;
     p.num_blocks = d.c.num_blocks;
     p.max_seq_len = d.max_seq_len;
-    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    p.scale_log2 = (float)((double)d.scale * (d.fp8 ? (double)d.k_scale : 1.0) * 1.4426950408889634);
+    p.v_scale = d.fp8 ? d.v_scale : 1.0f;
     p.n_sub = group / gk;
     p.split = d.max_parts > 0 ? 1 : 0;
     p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
@@ -756,11 +805,18 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
         return hipErrorInvalidValue;
     p.n_units = (int32_t)units;
     const DecodeParams *pp = cascade ? &pre : nullptr;
+    if (d.fp8) {
+        if (d.c.bf16)
+            return d.c.head_dim == 64 ? run_decode<true, true, 64>(gk, gkp, p, pp, stream)
+                                      : run_decode<true, true, 128>(gk, gkp, p, pp, stream);
+        return d.c.head_dim == 64 ? run_decode<false, true, 64>(gk, gkp, p, pp, stream)
+                                  : run_decode<false, true, 128>(gk, gkp, p, pp, stream);
+    }
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? run_decode<true, 64>(gk, gkp, p, pp, stream)
-                                  : run_decode<true, 128>(gk, gkp, p, pp, stream);
-    return d.c.head_dim == 64 ? run_decode<false, 64>(gk, gkp, p, pp, stream)
-                              : run_decode<false, 128>(gk, gkp, p, pp, stream);
+        return d.c.head_dim == 64 ? run_decode<true, false, 64>(gk, gkp, p, pp, stream)
+                                  : run_decode<true, false, 128>(gk, gkp, p, pp, stream);
+    return d.c.head_dim == 64 ? run_decode<false, false, 64>(gk, gkp, p, pp, stream)
+                              : run_decode<false, false, 128>(gk, gkp, p, pp, stream);
 }
 
 }  // namespace pa

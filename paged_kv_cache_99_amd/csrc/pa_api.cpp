@@ -42,11 +42,16 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
         REQUIRE(aligned16(p), "%s is not 16-byte aligned", name);                         \
     } while (0)
 
+// allow_fp8: dtype may name E4M3 caches (an operation that only moves cache bytes).
 pa_status_t check_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
-                        int32_t head_dim, pa::CacheDims *c)
+                        int32_t head_dim, pa::CacheDims *c, bool allow_fp8 = false)
 {
-    REQUIRE(dtype == PA_DTYPE_F16 || dtype == PA_DTYPE_BF16, "dtype %d is not F16 or BF16",
-            (int)dtype);
+    if (allow_fp8)
+        REQUIRE(dtype == PA_DTYPE_F16 || dtype == PA_DTYPE_BF16 || dtype == PA_DTYPE_FP8_E4M3,
+                "dtype %d is not F16, BF16 or FP8_E4M3", (int)dtype);
+    else
+        REQUIRE(dtype == PA_DTYPE_F16 || dtype == PA_DTYPE_BF16, "dtype %d is not F16 or BF16",
+                (int)dtype);
     REQUIRE(num_blocks >= 0, "num_blocks %d < 0", num_blocks);
     REQUIRE(num_kv_heads > 0, "num_kv_heads %d <= 0", num_kv_heads);
     if (head_dim != 64 && head_dim != 128)
@@ -57,8 +62,11 @@ pa_status_t check_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_hea
     c->num_kv_heads = num_kv_heads;
     c->head_dim = head_dim;
     c->bf16 = dtype == PA_DTYPE_BF16;
+    c->fp8 = dtype == PA_DTYPE_FP8_E4M3;
     return PA_OK;
 }
+
+bool good_scale(float x) { return x > 0.0f && x < 3.0e38f; }
 
 pa_status_t launched(hipError_t e, const char *what)
 {
@@ -114,12 +122,40 @@ pa_status_t pa_reshape_and_cache(pa_dtype_t dtype, int32_t num_blocks, int32_t n
                     "reshape_and_cache");
 }
 
+pa_status_t pa_reshape_and_cache_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                     int32_t head_dim, const void *key, const void *value,
+                                     void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                     int32_t num_tokens, float k_scale, float v_scale,
+                                     void *stream)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    c.fp8 = true;
+    REQUIRE(num_tokens >= 0, "num_tokens %d < 0", num_tokens);
+    REQUIRE(good_scale(k_scale) && good_scale(v_scale),
+            "k_scale %g / v_scale %g is not a finite positive number", (double)k_scale,
+            (double)v_scale);
+    if (num_tokens == 0)
+        return ok();
+    REQUIRE_PTR(key, "key");
+    REQUIRE_PTR(value, "value");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(slot_mapping != nullptr, "slot_mapping is NULL");
+    return launched(pa::launch_reshape_and_cache_fp8(c, key, value, k_cache, v_cache, slot_mapping,
+                                                     num_tokens, k_scale, v_scale,
+                                                     (hipStream_t)stream),
+                    "reshape_and_cache_fp8");
+}
+
 pa_status_t pa_copy_blocks(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
                            int32_t head_dim, void *k_cache, void *v_cache,
                            const int32_t *block_mapping, int32_t num_pairs, void *stream)
 {
     pa::CacheDims c;
-    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c, true);
     if (s != PA_OK)
         return s;
     REQUIRE(num_pairs >= 0, "num_pairs %d < 0", num_pairs);
@@ -142,13 +178,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
     return (size_t)num_seqs * num_q_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
-pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
-                      int32_t head_dim, void *out, const void *query, const void *k_cache,
-                      const void *v_cache, const int32_t *block_tables,
-                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
-                      int32_t max_seq_len, int32_t num_q_heads, float scale,
-                      int32_t partition_size, void *workspace, size_t workspace_bytes,
-                      void *stream)
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, void *out, const void *query, const void *k_cache,
+                        const void *v_cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                        int32_t max_seq_len, int32_t num_q_heads, float scale,
+                        int32_t partition_size, void *workspace, size_t workspace_bytes,
+                        void *stream, bool fp8, float k_scale, float v_scale)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -165,6 +205,10 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
     REQUIRE(partition_size >= 0 && partition_size % PA_BLOCK_SIZE == 0 && partition_size <= 1024,
             "partition_size %d is not 0 or a multiple of 16 up to 1024", partition_size);
     REQUIRE(scale > 0.0f && scale < 3.0e38f, "scale %g is not a finite positive number", (double)scale);
+    if (fp8)
+        REQUIRE(good_scale(k_scale) && good_scale(v_scale),
+                "k_scale %g / v_scale %g is not a finite positive number", (double)k_scale,
+                (double)v_scale);
     if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
                     num_q_heads / num_kv_heads);
@@ -207,7 +251,43 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
     d.ws_acc = (float *)workspace;
     d.ws_ml = need ? (float *)workspace + (size_t)num_seqs * num_q_heads * d.max_parts * head_dim
                    : nullptr;
-    return launched(pa::launch_decode(d, (hipStream_t)stream), "decode");
+    d.fp8 = fp8;
+    d.c.fp8 = fp8;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    return launched(pa::launch_decode(d, (hipStream_t)stream), fp8 ? "decode_fp8" : "decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                      int32_t head_dim, void *out, const void *query, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    return decode_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                       num_q_heads, scale, partition_size, workspace, workspace_bytes, stream,
+                       false, 1.0f, 1.0f);
+}
+
+pa_status_t pa_decode_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, void *out, const void *query, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                          int32_t max_seq_len, int32_t num_q_heads, float scale, float k_scale,
+                          float v_scale, int32_t partition_size, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    return decode_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                       num_q_heads, scale, partition_size, workspace, workspace_bytes, stream,
+                       true, k_scale, v_scale);
 }
 
 size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,

@@ -80,6 +80,46 @@ __device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b)
     return dot2<BF>(a.w, b.w, s);
 }
 
+// ------------------------------------------------------------------ FP8 (E4M3) cache elements
+// gfx950's FP8 conversions read and write the OCP E4M3 format (bias 7, no infinities, largest 448).
+// Every E4M3 value is exactly an f16, a bf16 and a float32 value.
+
+// Codes in bytes 0,1 (HI = false) or 2,3 (HI = true) of w as two 16-bit elements, low half first
+// (v_cvt_scalef32_pk_{f16,bf16}_fp8 with scale 1: exact).
+template <bool BF, bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_pk16(uint32_t w)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// Dot product of 16 16-bit query elements (q[0]: elements 0..7, q[1]: 8..15) with the 16 E4M3
+// codes of k (byte j = element j).
+template <bool BF>
+__device__ __forceinline__ float dot16_e4m3(const uint4 (&q)[2], const uint4 &k)
+{
+    const uint4 a = make_uint4(e4m3x2_to_pk16<BF, false>(k.x), e4m3x2_to_pk16<BF, true>(k.x),
+                               e4m3x2_to_pk16<BF, false>(k.y), e4m3x2_to_pk16<BF, true>(k.y));
+    const uint4 b = make_uint4(e4m3x2_to_pk16<BF, false>(k.z), e4m3x2_to_pk16<BF, true>(k.z),
+                               e4m3x2_to_pk16<BF, false>(k.w), e4m3x2_to_pk16<BF, true>(k.w));
+    return dot8<BF>(q[0], a) + dot8<BF>(q[1], b);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The four codes of w (byte j = element j) as float32 (v_cvt_pk_f32_fp8: exact).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4])
+{
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+}
+
 // ------------------------------------------------------------------ cross-lane reductions (DPP)
 // DPP controls of GFX9: quad_perm(1,0,3,2) swaps neighbours, quad_perm(2,3,0,1) swaps pairs,
 // row_half_mirror reverses each 8-lane half row, row_mirror reverses each 16-lane row.
@@ -95,14 +135,15 @@ __device__ __forceinline__ float dpp_f(float v, int ctrl_id)
     return __int_as_float(x);
 }
 
-// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group gets the group's sum.
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of a group gets the group's sum.
 template <int N>
 __device__ __forceinline__ float group_sum(float v)
 {
-    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
     v += dpp_f(v, 0);
     v += dpp_f(v, 1);
-    v += dpp_f(v, 2);
+    if constexpr (N >= 8)
+        v += dpp_f(v, 2);
     if constexpr (N == 16)
         v += dpp_f(v, 3);
     return v;
@@ -132,7 +173,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 16-byte load marked nontemporal (global_load_dwordx4 ... nt): for data streamed once, such as
 // the K/V tiles of a decode step; it measurably raises the sustained read rate of scattered
 // 4 KiB tiles on gfx950.
-__device__ __forceinline__ uint4 load_nt(const uint16_t *p)
+__device__ __forceinline__ uint4 load_nt(const void *p)
 {
     const u32x4 t = __builtin_nontemporal_load((const u32x4 *)p);
     return make_uint4(t[0], t[1], t[2], t[3]);

@@ -11,13 +11,19 @@ struct CacheDims {
     int32_t num_blocks;
     int32_t num_kv_heads;
     int32_t head_dim;
-    bool bf16;
+    bool bf16;          // 16-bit element type of queries, keys, values and outputs
+    bool fp8 = false;   // the caches hold E4M3 codes (one byte per element)
 };
 
 // reshape_and_cache.hip
 hipError_t launch_reshape_and_cache(const CacheDims &c, const void *key, const void *value,
                                     void *k_cache, void *v_cache, const int32_t *slot_mapping,
                                     int32_t num_tokens, hipStream_t stream);
+// E4M3 caches: the code of x / k_scale (keys) or x / v_scale (values) goes to the slot.
+hipError_t launch_reshape_and_cache_fp8(const CacheDims &c, const void *key, const void *value,
+                                        void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                        int32_t num_tokens, float k_scale, float v_scale,
+                                        hipStream_t stream);
 
 // copy_blocks.hip
 hipError_t launch_copy_blocks(const CacheDims &c, void *k_cache, void *v_cache,
@@ -47,6 +53,10 @@ struct DecodeLaunch {
     int32_t num_groups;
     int32_t max_group_size;
     int32_t max_prefix_len;
+    // E4M3 caches (c.fp8): element = code value * k_scale / v_scale
+    bool fp8 = false;
+    float k_scale = 1.0f;
+    float v_scale = 1.0f;
 };
 // Group sizes with a dedicated kernel; any other group size runs as several of these.
 bool decode_supported(int32_t head_dim, int32_t group);

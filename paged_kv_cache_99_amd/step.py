@@ -39,17 +39,41 @@ def ints_to_device(a, device) -> torch.Tensor:
 
 
 class GpuStep:
+    """Device buffers of one step and its stages.
+
+    kv_cache="fp8" keeps the caches as E4M3 codes (lecture 34 §4.4) with scales k_scale, v_scale:
+    fp8_pool gives their initial bytes (numpy uint8, the pool layout); without it the 16-bit pool is
+    quantized on the device by the library's own FP8 scatter, each slot being one token. Such a
+    step runs copy, scatter and decode; it has no shared-prefix or prefill stage.
+    """
+
     def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
-                 shared_prefix: bool = False):
+                 shared_prefix: bool = False, kv_cache: str = "auto", k_scale: float = 1.0,
+                 v_scale: float = 1.0, fp8_pool=None):
         self.w = w
         self.device = torch.device(device)
         dt, dev = w.dtype, self.device
         shape = (w.num_blocks, w.H_kv, binding.BLOCK_SIZE, w.D)
-        self.k_cache = words_to_device(w.k_cache, dt, dev).view(shape)
-        self.v_cache = words_to_device(w.v_cache, dt, dev).view(shape)
+        self.fp8 = kv_cache == "fp8"
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.new_key = words_to_device(w.new_key, dt, dev)
         self.new_value = words_to_device(w.new_value, dt, dev)
         self.slot_mapping = ints_to_device(w.slot_mapping, dev)
+        if self.fp8:
+            if shared_prefix:
+                raise ValueError("no shared-prefix decode for E4M3 caches")
+            if fp8_pool is not None:
+                self.k_cache = torch.from_numpy(np.ascontiguousarray(fp8_pool[0], np.uint8)).to(
+                    dev).view(shape)
+                self.v_cache = torch.from_numpy(np.ascontiguousarray(fp8_pool[1], np.uint8)).to(
+                    dev).view(shape)
+            else:
+                self.k_cache = torch.empty(shape, dtype=torch.uint8, device=dev)
+                self.v_cache = torch.empty(shape, dtype=torch.uint8, device=dev)
+                self.quantize_pool_on_device(w)
+        else:
+            self.k_cache = words_to_device(w.k_cache, dt, dev).view(shape)
+            self.v_cache = words_to_device(w.v_cache, dt, dev).view(shape)
         self.copy_pairs = ints_to_device(np.asarray(w.copy_pairs).reshape(-1, 2), dev)
         nd = int(w.n_decode)
         self.n_decode = nd
@@ -88,16 +112,39 @@ class GpuStep:
         cu = np.asarray(w.cu_q_lens)
         self.max_q_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
 
+    def quantize_pool_on_device(self, w):
+        """E4M3 caches holding the codes of the workload's 16-bit pool: every slot of the pool is
+        written as one token by pa_reshape_and_cache_fp8 (slot s = block s / 16, offset s % 16)."""
+        nb, H, D = w.num_blocks, w.H_kv, w.D
+        slots = torch.arange(nb * binding.BLOCK_SIZE, dtype=torch.int32, device=self.device)
+
+        def as_tokens(words):
+            pool = words_to_device(words, w.dtype, self.device).view(nb, H, binding.BLOCK_SIZE, D)
+            return pool.permute(0, 2, 1, 3).contiguous().view(nb * binding.BLOCK_SIZE, H, D)
+
+        binding.reshape_and_cache_fp8(as_tokens(w.k_cache), as_tokens(w.v_cache), self.k_cache,
+                                      self.v_cache, slots, self.k_scale, self.v_scale)
+        torch.cuda.synchronize(self.device)
+
     # ---- stages
     def copy(self, stream=None):
         binding.copy_blocks(self.k_cache, self.v_cache, self.copy_pairs, stream)
 
     def scatter(self, stream=None):
-        binding.reshape_and_cache(self.new_key, self.new_value, self.k_cache, self.v_cache,
-                                  self.slot_mapping, stream)
+        if self.fp8:
+            binding.reshape_and_cache_fp8(self.new_key, self.new_value, self.k_cache, self.v_cache,
+                                          self.slot_mapping, self.k_scale, self.v_scale, stream)
+        else:
+            binding.reshape_and_cache(self.new_key, self.new_value, self.k_cache, self.v_cache,
+                                      self.slot_mapping, stream)
 
     def decode(self, stream=None):
-        if self.n_decode and self.shared_prefix:
+        if self.n_decode and self.fp8:
+            binding.decode_fp8(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
+                               self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,
+                               self.k_scale, self.v_scale, self.partition_size, self.workspace,
+                               stream)
+        elif self.n_decode and self.shared_prefix:
             binding.decode_shared_prefix(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
                                          self.dec_tables, self.dec_lens, self.max_seq_len,
                                          self.group_starts, self.prefix_lens,
@@ -109,6 +156,8 @@ class GpuStep:
                            self.partition_size, self.workspace, stream)
 
     def prefill(self, stream=None):
+        if self.pre_query.shape[0] and self.fp8:
+            raise ValueError("no prefill kernel reads E4M3 caches")
         if self.pre_query.shape[0]:
             binding.prefill_chunk(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
                                   self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,

@@ -121,3 +121,38 @@ def test_scatter_copy_prefill_reject_bad_arguments():
     neg = list(args)
     neg[13] = -1
     assert lib.pa_prefill_chunk(*neg) == INVALID
+
+
+FP8 = 2
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    lib = binding.lib()
+    f = ctypes.c_float
+    # the quantizing scatter: activation dtype F16/BF16 only, positive finite scales
+    ok_args = [F16, 10, 4, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 0, f(0.5), f(0.5), None]
+    assert lib.pa_reshape_and_cache_fp8(*ok_args) == OK
+    for i, bad in ((0, FP8), (10, f(0.0)), (11, f(-1.0)), (10, f(float("inf"))),
+                   (11, f(float("nan")))):
+        a = list(ok_args)
+        a[i] = bad
+        a[9] = 3
+        assert lib.pa_reshape_and_cache_fp8(*a) == INVALID, (i, bad)
+    assert lib.pa_reshape_and_cache_fp8(F16, 10, 4, 96, FAKE, FAKE, FAKE, FAKE, FAKE, 3, f(1.0),
+                                        f(1.0), None) == UNSUPPORTED
+    # the 16-bit entry points do not take E4M3 caches; copy_blocks does
+    assert lib.pa_reshape_and_cache(FP8, 10, 4, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == INVALID
+    assert lib.pa_copy_blocks(FP8, 10, 4, 128, None, None, None, 0, None) == OK
+    assert lib.pa_copy_blocks(FP8, 10, 4, 128, FAKE, None, FAKE, 2, None) == INVALID
+    assert lib.pa_copy_blocks(3, 10, 4, 128, FAKE, FAKE, FAKE, 2, None) == INVALID
+    # decode over E4M3 caches: the checks of pa_decode plus the scales
+    dec = [BF16, 10, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 64, 8, f(0.125), f(0.5),
+           f(0.5), 0, None, 0, None]
+    assert lib.pa_decode_fp8(*[a if i != 11 else 0 for i, a in enumerate(dec)]) == OK
+    for i, bad in ((15, f(0.0)), (16, f(float("inf"))), (0, FP8), (13, 7), (17, 24)):
+        a = list(dec)
+        a[i] = bad
+        assert lib.pa_decode_fp8(*a) == INVALID, (i, bad)
+    small = list(dec)
+    small[12], small[17], small[9] = 4096, 512, 256
+    assert lib.pa_decode_fp8(*small) == WORKSPACE
