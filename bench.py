@@ -15,12 +15,13 @@ Prints ONE JSON line:
                when it was taken on the current decode source, else null;
   cpu_baseline the CPU oracle (float64) timed on this host over the full decode of the workload.
 
-Algorithmic bytes (what the method must move, per stage):
-  decode   sum_s L_s * 2 * H_kv * D * 2 (each valid token's K and V row once) + query + output;
+Algorithmic bytes (what the method must move, per stage; E = 2 bytes per cache element, 1 with
+--kv-cache fp8, whose caches hold E4M3 codes):
+  decode   sum_s L_s * 2 * H_kv * D * E (each valid token's K and V row once) + query + output;
            with shared-prefix groups read once, a group's common blocks count once for the group
            (the per-sequence count is reported as decode_logical_bytes);
-  scatter  T * H_kv * D * 2 * 2 read + the same written;
-  copy     pairs * 2 caches * (16 * H_kv * D * 2) read + the same written;
+  scatter  2 * T * H_kv * D * 2 read + 2 * T * H_kv * D * E written;
+  copy     pairs * 2 caches * (16 * H_kv * D * E) read + the same written;
   prefill  K/V rows of the context once + query + output (its roofline is MFMA: 4*D*H_q*sum(p+1)).
 """
 import argparse
@@ -42,9 +43,9 @@ DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_99_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_traffic.json")
 
 
-def decode_bytes(w):
+def decode_bytes(w, esize=2):
     nd = w.n_decode
-    kv = int(np.sum(w.seq_lens[:nd].astype(np.int64))) * 2 * w.H_kv * w.D * 2
+    kv = int(np.sum(w.seq_lens[:nd].astype(np.int64))) * 2 * w.H_kv * w.D * esize
     return kv + 2 * nd * w.H_q * w.D * 2
 
 
@@ -62,12 +63,12 @@ def decode_unique_bytes(w):
     return tokens * 2 * w.H_kv * w.D * 2 + 2 * nd * w.H_q * w.D * 2
 
 
-def scatter_bytes(w):
-    return 4 * len(w.slot_mapping) * w.H_kv * w.D * 2
+def scatter_bytes(w, esize=2):
+    return 2 * len(w.slot_mapping) * w.H_kv * w.D * (2 + esize)
 
 
-def copy_bytes(w):
-    return 4 * len(w.copy_pairs) * 16 * w.H_kv * w.D * 2
+def copy_bytes(w, esize=2):
+    return 4 * len(w.copy_pairs) * 16 * w.H_kv * w.D * esize
 
 
 def prefill_bytes_flops(w):
@@ -104,11 +105,17 @@ def committed_traffic(per_launch_algorithmic):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, max_seconds):
-    """Time the float64 oracle over the workload's decode (a bounded sample when it is long)."""
+def cpu_baseline(w, max_seconds, fp8=None):
+    """Time the float64 oracle over the workload's decode (a bounded sample when it is long).
+    fp8 = (k_scale, v_scale): the oracle's E4M3 decode over its own quantization of the pool."""
     import oracle
     nd = w.n_decode
     threads = oracle.max_threads()
+    esize = 2
+    if fp8 is not None:
+        esize = 1
+        k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, fp8[0])
+        v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, fp8[1])
     order = np.arange(nd)
     # grow the sample by whole sequences until the next one would pass max_seconds of wall time
     done_tokens, elapsed, n_seq = 0, 0.0, 0
@@ -116,18 +123,24 @@ def cpu_baseline(w, max_seconds):
     while n_seq < nd:
         take = order[n_seq:n_seq + max(1, nd // 8)]
         pairs = np.array([(s, h) for s in take for h in range(w.H_q)], np.int32)
-        oracle.decode(w.query_decode, w.k_cache, w.v_cache, w.block_tables[:nd], w.seq_lens[:nd],
-                      w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, pairs=pairs,
-                      nthreads=threads)
+        if fp8 is None:
+            oracle.decode(w.query_decode, w.k_cache, w.v_cache, w.block_tables[:nd],
+                          w.seq_lens[:nd], w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                          pairs=pairs, nthreads=threads)
+        else:
+            oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd],
+                              w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, fp8[0], fp8[1],
+                              pairs=pairs, nthreads=threads)
         n_seq += len(take)
         done_tokens += int(np.sum(w.seq_lens[take]))
         elapsed = time.perf_counter() - t0
         if elapsed > max_seconds:
             break
-    nbytes = done_tokens * 2 * w.H_kv * w.D * 2 + 2 * n_seq * w.H_q * w.D * 2
+    nbytes = done_tokens * 2 * w.H_kv * w.D * esize + 2 * n_seq * w.H_q * w.D * 2
+    what = "E4M3 decode" if fp8 is not None else "decode"
     return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"float64 oracle decode of {n_seq} of {nd} sequences x {w.H_q} query heads "
+            "sample": f"float64 oracle {what} of {n_seq} of {nd} sequences x {w.H_q} query heads "
                       f"({done_tokens} context tokens, {nbytes / 1e9:.3f} GB of K/V) in "
                       f"{elapsed:.2f} s, pool before the step's scatter",
             "seconds": round(elapsed, 3)}
@@ -162,6 +175,11 @@ def main():
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode shared-prefix groups per sequence instead of reading each "
                          "group's common blocks once")
+    ap.add_argument("--kv-cache", choices=["auto", "fp8"], default="auto",
+                    help="fp8: E4M3 caches (quantizing scatter, E4M3 decode); decode-only "
+                         "workloads")
+    ap.add_argument("--k-scale", type=float, default=0.03, help="E4M3 key scale")
+    ap.add_argument("--v-scale", type=float, default=0.02, help="E4M3 value scale")
     ap.add_argument("--print-decode-src-hash", action="store_true",
                     help="print the hash of the decode sources (recorded with counter summaries)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
@@ -189,7 +207,15 @@ def main():
     w = W.named(args.workload)
     print(f"[bench] workload {w.name}: {len(w.seq_lens)} sequences, pool {w.num_blocks} blocks, "
           f"built in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    g = GpuStep(w, partition_size=args.partition, shared_prefix=not args.no_shared_prefix)
+    fp8 = args.kv_cache == "fp8"
+    if fp8 and len(w.cu_q_lens) > 1 and int(w.cu_q_lens[-1]) > 0:
+        print("bench.py --kv-cache fp8 runs decode-only workloads (no prefill kernel reads E4M3 "
+              "caches)", file=sys.stderr)
+        sys.exit(2)
+    esize = 1 if fp8 else 2
+    g = GpuStep(w, partition_size=args.partition,
+                shared_prefix=not args.no_shared_prefix and not fp8,
+                kv_cache=args.kv_cache, k_scale=args.k_scale, v_scale=args.v_scale)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -223,13 +249,13 @@ def main():
     if args.copy_calibration:
         calibration_copy(g, args.copy_calibration)
 
-    d_bytes = decode_bytes(w)
+    d_bytes = decode_bytes(w, esize)
     u_bytes = decode_unique_bytes(w) if g.shared_prefix else d_bytes
     p_bytes, p_flops = prefill_bytes_flops(w)
-    step_bytes = u_bytes + scatter_bytes(w) + copy_bytes(w) + p_bytes
+    step_bytes = u_bytes + scatter_bytes(w, esize) + copy_bytes(w, esize) + p_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_gbs = u_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0
-    traffic = committed_traffic(d_bytes) if w.name == "llama2_7b_decode" else None
+    traffic = committed_traffic(d_bytes) if w.name == "llama2_7b_decode" and not fp8 else None
     out = {
         "metric": "pa_decode HBM GB/s (% of 8 TB/s peak) + decode tokens/s, 7B-shaped layer",
         "value": round(value, 2),
@@ -256,6 +282,7 @@ def main():
             "scatter_tokens": int(len(w.slot_mapping)),
             "prefill_rows": int(g.pre_query.shape[0]),
             "shared_prefix_read_once": bool(g.shared_prefix),
+            "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
         },
         "decode_tokens_per_s": round(w.n_decode / (ms_per_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 5),
@@ -263,7 +290,8 @@ def main():
         "pct_of_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (partition + merge kernels)",
+            "kernel": "pa_decode_fp8 (partition + merge kernels)" if fp8
+                      else "pa_decode (partition + merge kernels)",
             "achieved": round(dec_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -280,7 +308,8 @@ def main():
         out["prefill_TFLOPs"] = round(p_flops / (pre_ms * 1e-3) / 1e12, 2)
         out["prefill_mfma_frac"] = round(p_flops / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
+                                           (args.k_scale, args.v_scale) if fp8 else None)
     print(json.dumps(out), flush=True)
 
 
