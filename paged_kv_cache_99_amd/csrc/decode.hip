@@ -285,291 +285,331 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
     }
 }
 
-// ------------------------------------------------------------------ head groups of 4 and 8
-// The kernel above computes every score in all 16 lanes of a token row and repeats the softmax
-// there, once per query head: for GQA groups that redundancy, not HBM, bounds it. Here each
-// (block, kv head) K tile is staged in LDS and re-read in a scoring layout where GK lanes own one
-// token (lane j covers dims [j*D/GK, (j+1)*D/GK) for all GK heads). A transpose-reduce over those
-// GK lanes leaves lane j with the full score of head j, so the exponential and the running sum are
-// computed once per (token, head). The softmax reference point m is wave-uniform per head and
-// moves only when a score exceeds it by more than 2^kLazy (then the accumulators are rescaled): all
-// tokens of a head share one m, so P*V may use any lane layout. Probabilities reach the P*V lanes
-// (the coalesced V layout of the kernel above) through a 16 x GK float buffer in LDS.
-constexpr float kLazy = 8.0f;  // log2 units: partial sums stay below 2^8 times their true scale
+// Lazy reference point of the MFMA units below: a column's running maximum moves (and its sums
+// are rescaled) only when a score passes it by more than 2^kLazy, so partial sums stay below 2^8
+// times their true scale and most steps skip the rescale.
+constexpr float kLazy = 8.0f;  // log2 units
 
-// Sum the GK values x[0..GK) of each lane over aligned groups of GK lanes, leaving lane j of a
-// group with the group's total of x[j]. Stage s pairs lanes that differ in bit s of j (for GK = 8,
-// bit 2 via row_half_mirror, which reverses each group of 8): each lane keeps the half of its values
-// selected by that bit and adds the partner's copy of the same half.
-template <int GK>
-__device__ __forceinline__ float transpose_reduce(float (&x)[GK], int j)
-{
-    if constexpr (GK == 8) {
-        const bool b2 = (j >> 2) & 1;
-        float y[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float keep = b2 ? x[4 + k] : x[k], send = b2 ? x[k] : x[4 + k];
-            y[k] = keep + dpp_f(send, 2);  // row_half_mirror: lane j <-> 7 - j
-        }
-        const bool b1 = (j >> 1) & 1;
-        float z[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float keep = b1 ? y[2 + k] : y[k], send = b1 ? y[k] : y[2 + k];
-            z[k] = keep + dpp_f(send, 1);  // j <-> j ^ 2
-        }
-        const bool b0 = j & 1;
-        const float keep = b0 ? z[1] : z[0], send = b0 ? z[0] : z[1];
-        return keep + dpp_f(send, 0);  // j <-> j ^ 1
-    } else {
-        static_assert(GK == 4, "groups of 4 or 8");
-        const bool b1 = (j >> 1) & 1;
-        float z[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float keep = b1 ? x[2 + k] : x[k], send = b1 ? x[k] : x[2 + k];
-            z[k] = keep + dpp_f(send, 1);
-        }
-        const bool b0 = j & 1;
-        const float keep = b0 ? z[1] : z[0], send = b0 ? z[0] : z[1];
-        return keep + dpp_f(send, 0);
-    }
-}
+// ------------------------------------------------------------------ head groups on MFMA
+// Up to 16 query rows that read one (kv head, token range) -- the query heads of a GQA group, or the
+// (member, query head) pairs of a shared-prefix group -- are the 16 columns of
+// v_mfma_f32_16x16x32_{f16,bf16}; a step covers two blocks (32 tokens):
+//   S[t][j]  = sum_d K[t][d] Q[j][d]   A = K, 16 tokens x 32 dims, loaded from HBM straight into
+//                                       the operand layout (lane l: token l % 16; plain loads, since
+//                                       one instruction covers half of each 128-byte line and the
+//                                       next the other half); B = Q in registers
+//   O[d][j] += sum_t V[t][d] P[t][j]   A = V^T, 16 dims x 32 tokens, read from row-major V in LDS
+//                                       with ds_read_b64_tr_b16; B = P, taken from the S accumulators
+//                                       where it already sits in the operand layout.
+// Lane l owns column j = l % 16 and row group g = l / 16: its S values are tokens 4g..4g+3 of each
+// block, its O values dims 16c + 4g..4g+3 of each 16-dim tile c. The score scale and the running
+// reference point are per column, kept equal across the 4 row groups; like the kernel above the
+// reference moves only when a score passes it by more than 2^kLazy. Token order inside the PV
+// contraction: operand slot 8g + e is token 4g + e of the first block (e < 4) or 4g + e - 4 of the
+// second, for both operands. bf16 probabilities go in as a hi + lo pair (about 16 significant bits).
+// E4M3 caches: K bytes are widened to 16-bit pairs in registers, V bytes on their way into LDS.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// XOR swizzle of the 16-byte pieces of K row `row` in LDS: the coalesced writes fill whole rows;
-// the scoring reads (16 lanes = 16/GK*... rows x pieces) then fall on distinct banks.
-template <int D, int GK>
-__device__ __forceinline__ int kswz(int row)
+constexpr int kCols = 16;  // query rows per MFMA unit
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma16(const uint4 &a, const uint4 &b, const f32x4 &c)
 {
-    if constexpr (D == 128)
-        return row & (16 / GK - 1);
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     else
-        return (row >> 1) & (8 / GK - 1);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// One unit over positions [t0, t1) of the table `table` and kv head kvh, for GK query rows qrow[h]
-// (rows of query / out / workspace; -1 = no query). Split units write slot `slot` of each row.
-template <bool BF, int D, int GK>
-__device__ __forceinline__ void gqa_unit(const DecodeParams &p, const int (&qrow)[GK],
-                                         const int32_t *table, int kvh, int t0, int t1, int slot,
-                                         bool split)
+// First of the 8 dims that row group g holds in QK k-chunk c. 16-bit caches: chunk c is dims
+// 32c..32c+31. E4M3 caches: a lane's 16-byte load holds 16 dims, the halves of which feed chunks
+// 2c2 and 2c2+1 (any dim order serves, as long as K and Q agree).
+template <bool F8>
+__device__ __forceinline__ int qk_dim(int c, int g)
 {
-    constexpr int RL = D / 8;            // P*V layout: lanes per token row
-    constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
-    constexpr int NCH = kBlock / ROWS;   // loads per (block, kv head) tile
-    constexpr int TPP = kWave / GK;      // tokens scored per pass
-    constexpr int NPASS = kBlock / TPP;  // passes per block
-    constexpr int CPL = D / GK / 8;      // 16-byte pieces of a K row per scoring lane
-    constexpr int ROWB = D * 2;
-    __shared__ __align__(16) uint8_t k_lds[kBlock * ROWB];
-    __shared__ __align__(16) float p_lds[kBlock * GK];
+    return F8 ? 16 * (g + 4 * (c >> 1)) + 8 * (c & 1) : 32 * c + 8 * g;
+}
+
+// XOR swizzle of the 16-byte pieces of V row r in LDS (rows of D 16-bit elements): the 16 rows
+// one transposed read touches start on distinct pieces.
+template <int D>
+__device__ __forceinline__ int vswz(int r)
+{
+    return D == 128 ? (r & 15) : (r & 7);
+}
+
+template <bool BF, bool F8, int D>
+__device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const int32_t *table,
+                                          int kvh, int t0, int t1, int slot, bool split)
+{
+    constexpr int NC = D / 32;              // QK k-chunks
+    constexpr int NT = D / 16;              // PV output tiles
+    constexpr int ESZ = F8 ? 1 : 2;
+    constexpr int TILE = kBlock * D * ESZ;  // bytes of a (block, kv head) tile
+    constexpr int NV = TILE / 1024;         // 1 KiB V loads per block
+    constexpr int KL = F8 ? NC / 2 : NC;    // 16-byte K loads per lane per block
+    constexpr int ROWB = D * 2;             // bytes of a 16-bit V row in LDS
+    __shared__ __align__(16) uint8_t v_lds[2 * kBlock * ROWB];
 
     const int lane = threadIdx.x;
-    const int r = lane / RL, c = lane % RL;  // P*V layout
-    const int ts = lane / GK, j = lane % GK; // scoring layout: token slot, dim slice = own head
+    const int j = lane & 15, g = lane >> 4;
 
-    // queries in the scoring layout: dims [j*D/GK, (j+1)*D/GK) of every head of the group
-    uint4 q[GK][CPL];
+    uint4 q[NC];
 #pragma unroll
-    for (int h = 0; h < GK; ++h)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-            q[h][k] = qrow[h] >= 0 ? *(const uint4 *)(p.query + (size_t)qrow[h] * D + (j * CPL + k) * 8)
-                                   : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c)
+        q[c] = qrow >= 0 ? *(const uint4 *)(p.query + (size_t)qrow * D + qk_dim<F8>(c, g))
+                         : make_uint4(0, 0, 0, 0);
 
-    float m_own = -INFINITY, l_own = 0.0f;  // reference point and partial sum of head j
-    float acc[GK][8];
+    f32x4 o[NT];
 #pragma unroll
-    for (int h = 0; h < GK; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[h][e] = 0.0f;
+    for (int t = 0; t < NT; ++t)
+        o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY, l = 0.0f;
 
-    const size_t block_stride = (size_t)p.num_kv_heads * kBlock * D;
-    const size_t tile_off = (size_t)kvh * kBlock * D + lane * 8;
+    const uint8_t *kbase = (const uint8_t *)p.k_cache + (size_t)kvh * TILE;
+    const uint8_t *vbase = (const uint8_t *)p.v_cache + (size_t)kvh * TILE;
+    const size_t block_stride = (size_t)p.num_kv_heads * TILE;
+
+    // transposed-read addresses: source lane s = 4k + qd of a row group points at row 4g + k (first
+    // block; + 16 for the second), dims 16c + 4qd .. +3
+    const int tr_k = (lane & 15) >> 2, tr_q = lane & 3;
 
     for (int bb = t0 / kBlock; bb * kBlock < t1; bb += kWave) {
         const int nb = min(kWave, (t1 - bb * kBlock + kBlock - 1) / kBlock);
         const int my_blk = lane < nb ? table[bb + lane] : 0;
+        const int nsteps = (nb + 1) / 2;
 
-        auto load = [&](int k, uint4(&kk)[NCH], uint4(&vv)[NCH]) {
-            int blk = __builtin_amdgcn_readlane(my_blk, k);
-            blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
-            const uint16_t *kp = p.k_cache + blk * block_stride + tile_off;
-            const uint16_t *vp = p.v_cache + blk * block_stride + tile_off;
+        auto blk_of = [&](int k) {  // block id of the window's k-th block (k < nb), 0 if bad
+            const int blk = __builtin_amdgcn_readlane(my_blk, k);
+            return (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+        };
+        // a second block past the window's end (odd nb) is not loaded: its operands are zero
+        auto load_k = [&](int st, uint4(&kk)[2][KL]) {
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                kk[i] = load_nt(kp + i * ROWS * D);
-                vv[i] = load_nt(vp + i * ROWS * D);
+            for (int b = 0; b < 2; ++b) {
+                const int k = 2 * st + b;
+                if (k < nb) {
+                    const uint8_t *kt = kbase + (size_t)blk_of(k) * block_stride;
+#pragma unroll
+                    for (int c = 0; c < KL; ++c)  // plain loads: each covers half lines
+                        kk[b][c] = F8 ? *(const uint4 *)(kt + j * D + 16 * (g + 4 * c))
+                                      : *(const uint4 *)(kt + (j * D + 32 * c + 8 * g) * 2);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < KL; ++c)
+                        kk[b][c] = make_uint4(0, 0, 0, 0);
+                }
+            }
+        };
+        auto load_v = [&](int st, uint4(&vv)[2][NV]) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int k = 2 * st + b;
+                if (k < nb) {
+                    const uint8_t *vt = vbase + (size_t)blk_of(k) * block_stride;
+#pragma unroll
+                    for (int i = 0; i < NV; ++i)
+                        vv[b][i] = load_nt(vt + 1024 * i + 16 * lane);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i)
+                        vv[b][i] = make_uint4(0, 0, 0, 0);
+                }
             }
         };
 
-        auto consume = [&](int k, const uint4(&kk)[NCH], uint4(&vv)[NCH]) {
-            const int base = (bb + k) * kBlock;
-            const int raw = __builtin_amdgcn_readlane(my_blk, k);
-            const bool good_blk = (unsigned)raw < (unsigned)p.num_blocks;
-            const bool whole = good_blk && base >= t0 && base + kBlock <= t1;
-
-            // stage the K tile: row ROWS*i + r, piece c (swizzled)
+        // validity of the step's 32 tokens: block ids in the pool and positions in [t0, t1)
+        auto tok_ok = [&](int st, int b, int r) {
+            const int k = 2 * st + b;
+            const int raw = __builtin_amdgcn_readlane(my_blk, k < nb ? k : 0);
+            const int tok = (bb + k) * kBlock + r;
+            return k < nb && (unsigned)raw < (unsigned)p.num_blocks && tok >= t0 && tok < t1;
+        };
+        auto whole_step = [&](int st) {
+            bool w = 2 * st + 1 < nb && (bb + 2 * st) * kBlock >= t0 &&
+                     (bb + 2 * st + 2) * kBlock <= t1;
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int row = ROWS * i + r;
-                *(uint4 *)(k_lds + row * ROWB + ((c ^ kswz<D, GK>(row)) << 4)) = kk[i];
+            for (int b = 0; b < 2; ++b) {
+                const int raw = __builtin_amdgcn_readlane(my_blk, w ? 2 * st + b : 0);
+                w = w && (unsigned)raw < (unsigned)p.num_blocks;
             }
+            return w;
+        };
 
-            // scores of head j for tokens ts + TPP*pass
-            float sc[NPASS];
+        // V of a step into LDS as 16-bit rows 0..31 (masked rows zeroed: they may hold any bits)
+        auto stage = [&](int st, bool whole, const uint4(&vv)[2][NV]) {
 #pragma unroll
-            for (int ps = 0; ps < NPASS; ++ps) {
-                const int row = ps * TPP + ts;
-                uint4 kr[CPL];
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int k2 = 0; k2 < CPL; ++k2)
-                    kr[k2] = *(const uint4 *)(k_lds + row * ROWB +
-                                              (((j * CPL + k2) ^ kswz<D, GK>(row)) << 4));
-                float part_sum[GK];
-#pragma unroll
-                for (int h = 0; h < GK; ++h) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int k2 = 0; k2 < CPL; ++k2)
-                        a += dot8<BF>(q[h][k2], kr[k2]);
-                    part_sum[h] = a;
-                }
-                float x = transpose_reduce<GK>(part_sum, j) * p.scale_log2;
-                if (!whole && !(good_blk && base + row >= t0 && base + row < t1))
-                    x = -INFINITY;
-                sc[ps] = x;
-            }
-
-            // lazy reference point: move it (and rescale) only when a score passes it by 2^kLazy
-            float over = sc[0] - m_own;
-#pragma unroll
-            for (int ps = 1; ps < NPASS; ++ps)
-                over = fmaxf(over, sc[ps] - m_own);
-            if (!__all(!(over > kLazy))) {
-                float mx = sc[0];
-#pragma unroll
-                for (int ps = 1; ps < NPASS; ++ps)
-                    mx = fmaxf(mx, sc[ps]);
-#pragma unroll
-                for (int off = GK; off < kWave; off <<= 1)
-                    mx = fmaxf(mx, xor_shfl(mx, off));  // max over the token slots of head j
-                const float mn = fmaxf(m_own, mx);
-                const float alpha = fast_exp2(m_own - mn);  // 0 on the first block
-                m_own = mn;
-                l_own *= alpha;
-#pragma unroll
-                for (int h = 0; h < GK; ++h) {
-                    const float ah = __int_as_float(
-                        __builtin_amdgcn_readlane(__float_as_int(alpha), h));  // lane h has head h
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[h][e] *= ah;
-                }
-            }
-
-            // probabilities: own head, own tokens; to LDS as p[token][head]
-#pragma unroll
-            for (int ps = 0; ps < NPASS; ++ps) {
-                const float pr = fast_exp2(sc[ps] - m_own);  // masked: exp2(-inf) = 0
-                l_own += pr;
-                p_lds[(ps * TPP + ts) * GK + j] = pr;
-            }
-
-            // P*V in the coalesced layout: lane (r, c) holds tokens ROWS*i + r, dims c*8..c*8+7
-            if (!whole) {
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    const int tok = base + ROWS * i + r;
-                    const bool ok = good_blk && tok >= t0 && tok < t1;
-                    vv[i] = ok ? vv[i] : make_uint4(0, 0, 0, 0);  // masked rows may hold NaN bits
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                float pv[GK];
-#pragma unroll
-                for (int h4 = 0; h4 < GK; h4 += 4) {
-                    const float4 t = *(const float4 *)(p_lds + (ROWS * i + r) * GK + h4);
-                    pv[h4] = t.x;
-                    pv[h4 + 1] = t.y;
-                    pv[h4 + 2] = t.z;
-                    pv[h4 + 3] = t.w;
-                }
-                const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v0 = lo_f32<BF>(w[e]), v1 = hi_f32<BF>(w[e]);
-#pragma unroll
-                    for (int h = 0; h < GK; ++h) {
-                        acc[h][2 * e] += pv[h] * v0;
-                        acc[h][2 * e + 1] += pv[h] * v1;
+                for (int i = 0; i < NV; ++i) {
+                    const int byte = 1024 * i + 16 * lane;       // in the tile
+                    const int r = byte / (D * ESZ);               // row in the block
+                    const int e0 = (byte % (D * ESZ)) / ESZ;      // first element
+                    uint4 x = vv[b][i];
+                    if (!whole && !tok_ok(st, b, r))
+                        x = make_uint4(0, 0, 0, 0);
+                    const int R = kBlock * b + r;
+                    uint8_t *row = v_lds + R * ROWB;
+                    if constexpr (F8) {
+                        const uint4 lo = make_uint4(e4m3x2_to_pk16<BF, false>(x.x),
+                                                    e4m3x2_to_pk16<BF, true>(x.x),
+                                                    e4m3x2_to_pk16<BF, false>(x.y),
+                                                    e4m3x2_to_pk16<BF, true>(x.y));
+                        const uint4 hi = make_uint4(e4m3x2_to_pk16<BF, false>(x.z),
+                                                    e4m3x2_to_pk16<BF, true>(x.z),
+                                                    e4m3x2_to_pk16<BF, false>(x.w),
+                                                    e4m3x2_to_pk16<BF, true>(x.w));
+                        const int pc = e0 / 8;
+                        *(uint4 *)(row + ((pc ^ vswz<D>(R)) << 4)) = lo;
+                        *(uint4 *)(row + (((pc + 1) ^ vswz<D>(R)) << 4)) = hi;
+                    } else {
+                        *(uint4 *)(row + (((e0 / 8) ^ vswz<D>(R)) << 4)) = x;
                     }
                 }
+        };
+
+        auto scores = [&](int st, bool whole, const uint4(&kk)[2][KL], float(&sv)[8]) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    uint4 a;
+                    if constexpr (F8) {
+                        const uint4 &raw = kk[b][c >> 1];
+                        const uint32_t w0 = (c & 1) ? raw.z : raw.x;
+                        const uint32_t w1 = (c & 1) ? raw.w : raw.y;
+                        a = make_uint4(e4m3x2_to_pk16<BF, false>(w0), e4m3x2_to_pk16<BF, true>(w0),
+                                       e4m3x2_to_pk16<BF, false>(w1), e4m3x2_to_pk16<BF, true>(w1));
+                    } else {
+                        a = kk[b][c];
+                    }
+                    acc = mfma16<BF>(a, q[c], acc);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float x = acc[v] * p.scale_log2;
+                    if (!whole && !tok_ok(st, b, 4 * g + v))
+                        x = -INFINITY;
+                    sv[4 * b + v] = x;
+                }
             }
         };
 
-        uint4 ka[NCH], va[NCH], kn[NCH], vn[NCH];
-        load(0, ka, va);
-        for (int k = 0; k < nb; ++k) {
-            if (k + 1 < nb)
-                load(k + 1, kn, vn);
-            consume(k, ka, va);
+        auto accumulate = [&](const float(&sv)[8]) {
+            float over = sv[0] - m;
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                ka[i] = kn[i];
-                va[i] = vn[i];
+            for (int e = 1; e < 8; ++e)
+                over = fmaxf(over, sv[e] - m);
+            if (!__all(!(over > kLazy))) {
+                float mx = sv[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e)
+                    mx = fmaxf(mx, sv[e]);
+                mx = fmaxf(mx, xor_shfl(mx, 16));
+                mx = fmaxf(mx, xor_shfl(mx, 32));  // column max over the 4 row groups
+                if (mx > m) {
+                    const float alpha = fast_exp2(m - mx);  // 0 while m = -inf
+                    l *= alpha;
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        o[t] *= alpha;
+                    m = mx;
+                }
             }
+            const float ms = m == -INFINITY ? 0.0f : m;
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pr[e] = fast_exp2(sv[e] - ms);  // masked: exp2(-inf) = 0
+                l += pr[e];
+            }
+            uint4 pb, pl;
+            uint32_t *hw = &pb.x, *lw = &pl.x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hw[e] = pack2<BF>(pr[2 * e], pr[2 * e + 1]);
+                if constexpr (BF)
+                    lw[e] = pack2<BF>(pr[2 * e] - lo_f32<BF>(hw[e]),
+                                      pr[2 * e + 1] - hi_f32<BF>(hw[e]));
+            }
+
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int pc = 2 * t + (tr_q >> 1), half = (tr_q & 1) * 8;
+                const int r1 = 4 * g + tr_k, r2 = r1 + kBlock;
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16 *)(v_lds + r1 * ROWB + ((pc ^ vswz<D>(r1)) << 4) + half));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16 *)(v_lds + r2 * ROWB + ((pc ^ vswz<D>(r2)) << 4) + half));
+                const uint4 a = make_uint4(__builtin_bit_cast(uint2, lo4).x,
+                                           __builtin_bit_cast(uint2, lo4).y,
+                                           __builtin_bit_cast(uint2, hi4).x,
+                                           __builtin_bit_cast(uint2, hi4).y);
+                o[t] = mfma16<BF>(a, pb, o[t]);
+                if constexpr (BF)
+                    o[t] = mfma16<BF>(a, pl, o[t]);
+            }
+        };
+
+        // One set of operand registers: V of step st+1 is loaded as soon as V of step st sits in
+        // LDS, K of step st+1 as soon as the scores of step st are out; both then stream in while
+        // the rest of step st runs.
+        uint4 ka[2][KL], va[2][NV];
+        load_k(0, ka);
+        load_v(0, va);
+        for (int st = 0; st < nsteps; ++st) {
+            const bool whole = whole_step(st);
+            __syncthreads();  // the previous step's transposed reads are done
+            stage(st, whole, va);
+            if (st + 1 < nsteps)
+                load_v(st + 1, va);
+            __syncthreads();
+            float sv[8];
+            scores(st, whole, ka, sv);
+            if (st + 1 < nsteps)
+                load_k(st + 1, ka);
+            accumulate(sv);
         }
     }
 
-    // totals: l of head j over its token slots; acc over the row classes (one m per head: no
-    // rescaling needed)
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    if (qrow < 0)
+        return;
+    const float vs = F8 ? p.v_scale : 1.0f;
+    if (split) {
+        const size_t sl = (size_t)qrow * p.ws_slots + slot;
+        float *wa = p.ws_acc + sl * D + 4 * g;
 #pragma unroll
-    for (int off = GK; off < kWave; off <<= 1)
-        l_own += xor_shfl(l_own, off);
+        for (int t = 0; t < NT; ++t)
+            *(float4 *)(wa + 16 * t) = make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs,
+                                                   o[t][3] * vs);
+        if (g == 0)
+            *(float2 *)(p.ws_ml + sl * 2) = make_float2(m, l);
+    } else {
+        const float inv = l > 0.0f ? vs / l : 0.0f;
+        uint16_t *dst = p.out + (size_t)qrow * D + 4 * g;
 #pragma unroll
-    for (int h = 0; h < GK; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = acc[h][e];
-#pragma unroll
-            for (int off = RL; off < kWave; off <<= 1)
-                a += xor_shfl(a, off);
-            acc[h][e] = a;
-        }
-
-#pragma unroll
-    for (int h = 0; h < GK; ++h) {
-        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_own), h));
-        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_own), h));
-        if (lane < RL && qrow[h] >= 0) {
-            const size_t row = (size_t)qrow[h];
-            if (split) {
-                const size_t sl = row * p.ws_slots + slot;
-                float *wa = p.ws_acc + sl * D + lane * 8;
-                *(float4 *)wa = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-                *(float4 *)(wa + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-                if (lane == 0)
-                    *(float2 *)(p.ws_ml + sl * 2) = make_float2(mh, lh);
-            } else {
-                const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-                uint4 o;
-                o.x = pack2<BF>(acc[h][0] * inv, acc[h][1] * inv);
-                o.y = pack2<BF>(acc[h][2] * inv, acc[h][3] * inv);
-                o.z = pack2<BF>(acc[h][4] * inv, acc[h][5] * inv);
-                o.w = pack2<BF>(acc[h][6] * inv, acc[h][7] * inv);
-                *(uint4 *)(p.out + row * D + lane * 8) = o;
-            }
-        }
+        for (int t = 0; t < NT; ++t)
+            *(uint2 *)(dst + 16 * t) =
+                make_uint2(pack2<BF>(o[t][0] * inv, o[t][1] * inv),
+                           pack2<BF>(o[t][2] * inv, o[t][3] * inv));
     }
 }
 
-// Plain decode unit for a head group of GK: (sequence, kv head, subgroup, part).
-template <bool BF, int D, int GK>
-__global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
+// Plain decode of head groups of 3 or more: (sequence, kv head, subgroup of 16 query heads, part).
+// Three waves per SIMD (at most 168 registers): the unit holds one step of K and V operands in
+// flight, so the number of resident waves sets the bytes in flight per CU.
+template <bool BF, bool F8, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
+    DecodeParams p)
 {
     const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
     if (unit >= p.n_units)
@@ -585,21 +625,21 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(DecodeParams p)
     if (p.split && t0 >= L)
         return;
     const int t1 = min(L, t0 + p.part_tokens);
-    int qrow[GK];
-#pragma unroll
-    for (int h = 0; h < GK; ++h)
-        qrow[h] = seq * p.num_q_heads + (kvh * p.n_sub + sub) * GK + h;
-    gqa_unit<BF, D, GK>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
-                        p.slot_base + part, p.split != 0);
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int h = sub * kCols + (threadIdx.x & 15);
+    const int qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
+    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
+                         p.slot_base + part, p.split != 0);
 }
 
-// Shared-prefix unit: (prefix group g, kv head, subgroup of GK (member, query head) pairs, part).
+// Shared-prefix unit: (prefix group g, kv head, subgroup of 16 (member, query head) pairs, part).
 // The members of group g are sequences group_starts[g] .. group_starts[g+1]-1; they share the
 // blocks of positions [0, seq_starts[first member]), read here once through the first member's
 // table for all of them (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are
 // stored once). Pair v of the group is member v / G, query head kvh*G + v % G.
-template <bool BF, int D, int GK>
-__global__ __launch_bounds__(64) void decode_prefix_kernel(DecodeParams p)
+template <bool BF, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void
+decode_prefix_mfma_kernel(DecodeParams p)
 {
     const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
     if (unit >= p.n_units)
@@ -610,12 +650,11 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(DecodeParams p)
     const int kvh = rest % p.num_kv_heads;
     rest /= p.num_kv_heads;
     const int part = rest % p.max_parts;
-    const int g = rest / p.max_parts;
-    const int first = min(max(p.group_starts[g], 0), p.num_seqs);
-    const int n_mem = min(max(p.group_starts[g + 1], first), p.num_seqs) - first;
+    const int grp = rest / p.max_parts;
+    const int first = min(max(p.group_starts[grp], 0), p.num_seqs);
+    const int n_mem = min(max(p.group_starts[grp + 1], first), p.num_seqs) - first;
     const int G = p.num_q_heads / p.num_kv_heads;
-    const int v0 = vsub * GK;
-    if (n_mem == 0 || v0 >= n_mem * G)
+    if (n_mem == 0 || vsub * kCols >= n_mem * G)
         return;
     const int L0 = min(max(p.seq_lens[first], 0), p.max_seq_len);
     const int prefix = min(max(p.seq_starts[first], 0), L0);
@@ -623,14 +662,10 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(DecodeParams p)
     if (t0 >= prefix)
         return;
     const int t1 = min(prefix, t0 + p.part_tokens);
-    int qrow[GK];
-#pragma unroll
-    for (int h = 0; h < GK; ++h) {
-        const int v = v0 + h;
-        qrow[h] = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
-    }
-    gqa_unit<BF, D, GK>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1, part,
-                        true);
+    const int v = vsub * kCols + (threadIdx.x & 15);
+    const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
+    mfma_unit<BF, false, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1,
+                            part, true);
 }
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
@@ -686,52 +721,31 @@ template <bool BF, bool F8, int D, int GK>
 hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
 {
     const int grid = round_up8(p.n_units);
-    if constexpr (GK >= 4 && !F8)
-        hipLaunchKernelGGL((decode_gqa_kernel<BF, D, GK>), dim3(grid), dim3(kWave), 0, stream, p);
+    if constexpr (GK == kCols)
+        hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D>), dim3(grid), dim3(kWave), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>), dim3(grid), dim3(kWave), 0,
                            stream, p);
     return hipGetLastError();
 }
 
+// gk: query rows per unit -- 1 or 2 (one row class per lane, vector ALU) or kCols (MFMA columns)
 template <bool BF, bool F8, int D>
-hipError_t launch_units_gk(int gk, const DecodeParams &p, hipStream_t stream)
-{
-    if constexpr (F8) {  // E4M3 caches: the per-row-class kernel for head groups up to 4
-        switch (gk) {
-        case 4: return launch_units<BF, true, D, 4>(p, stream);
-        case 2: return launch_units<BF, true, D, 2>(p, stream);
-        default: return launch_units<BF, true, D, 1>(p, stream);
-        }
-    } else {
-        switch (gk) {
-        case 8: return launch_units<BF, false, D, 8>(p, stream);
-        case 4: return launch_units<BF, false, D, 4>(p, stream);
-        case 2: return launch_units<BF, false, D, 2>(p, stream);
-        default: return launch_units<BF, false, D, 1>(p, stream);
-        }
-    }
-}
-
-template <bool BF, bool F8, int D>
-hipError_t run_decode(int gk, int gkp, const DecodeParams &p, const DecodeParams *pre,
-                      hipStream_t stream)
+hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hipStream_t stream)
 {
     hipError_t e;
     if constexpr (!F8) {  // shared-prefix units exist for 16-bit caches only
         if (pre) {
-            const int grid = round_up8(pre->n_units);
-            if (gkp == 8)
-                hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 8>), dim3(grid), dim3(kWave), 0,
-                                   stream, *pre);
-            else
-                hipLaunchKernelGGL((decode_prefix_kernel<BF, D, 4>), dim3(grid), dim3(kWave), 0,
-                                   stream, *pre);
+            hipLaunchKernelGGL((decode_prefix_mfma_kernel<BF, D>), dim3(round_up8(pre->n_units)),
+                               dim3(kWave), 0, stream, *pre);
             if ((e = hipGetLastError()) != hipSuccess)
                 return e;
         }
     }
-    if ((e = launch_units_gk<BF, F8, D>(gk, p, stream)) != hipSuccess || !p.split)
+    e = gk == kCols ? launch_units<BF, F8, D, kCols>(p, stream)
+        : gk == 2   ? launch_units<BF, F8, D, 2>(p, stream)
+                    : launch_units<BF, F8, D, 1>(p, stream);
+    if (e != hipSuccess || !p.split)
         return e;
     const int rows = p.num_seqs * p.num_q_heads;
     hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
@@ -750,7 +764,9 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (d.num_seqs == 0)
         return hipSuccess;
     const int group = d.num_q_heads / d.c.num_kv_heads;
-    const int gk = group % 8 == 0 && !d.fp8 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    // groups of 1 and 2: one unit per query head pair on the vector ALU; larger groups: up to 16
+    // query heads per unit on MFMA
+    const int gk = group <= 2 ? group : kCols;
     const bool cascade = d.group_starts != nullptr && d.num_groups > 0;
     if (d.fp8 && cascade)
         return hipErrorInvalidValue;  // no shared-prefix kernel for E4M3 caches
@@ -771,7 +787,7 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.max_seq_len = d.max_seq_len;
     p.scale_log2 = (float)((double)d.scale * (d.fp8 ? (double)d.k_scale : 1.0) * 1.4426950408889634);
     p.v_scale = d.fp8 ? d.v_scale : 1.0f;
-    p.n_sub = group / gk;
+    p.n_sub = (group + gk - 1) / gk;
     p.split = d.max_parts > 0 ? 1 : 0;
     p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
     if (p.part_tokens < kBlock)
@@ -780,7 +796,6 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.ws_slots = p.max_parts;
 
     DecodeParams pre;
-    int gkp = 8;
     if (cascade) {
         // slots [0, pre_parts) of every row hold shared-prefix parts, the rest its own parts
         const int pre_parts = (d.max_prefix_len + d.partition_size - 1) / d.partition_size;
@@ -792,8 +807,7 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
         pre.group_starts = d.group_starts;
         pre.num_groups = d.num_groups;
         const int pairs = d.max_group_size * group;  // (member, query head) pairs per kv head
-        gkp = pairs >= 8 ? 8 : 4;
-        pre.n_vsub = (pairs + gkp - 1) / gkp;
+        pre.n_vsub = (pairs + kCols - 1) / kCols;
         pre.max_parts = pre_parts;
         const int64_t pre_units = (int64_t)d.num_groups * pre_parts * d.c.num_kv_heads * pre.n_vsub;
         if (pre_units > 0x7ffffff0)
@@ -807,16 +821,16 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     const DecodeParams *pp = cascade ? &pre : nullptr;
     if (d.fp8) {
         if (d.c.bf16)
-            return d.c.head_dim == 64 ? run_decode<true, true, 64>(gk, gkp, p, pp, stream)
-                                      : run_decode<true, true, 128>(gk, gkp, p, pp, stream);
-        return d.c.head_dim == 64 ? run_decode<false, true, 64>(gk, gkp, p, pp, stream)
-                                  : run_decode<false, true, 128>(gk, gkp, p, pp, stream);
+            return d.c.head_dim == 64 ? run_decode<true, true, 64>(gk, p, pp, stream)
+                                      : run_decode<true, true, 128>(gk, p, pp, stream);
+        return d.c.head_dim == 64 ? run_decode<false, true, 64>(gk, p, pp, stream)
+                                  : run_decode<false, true, 128>(gk, p, pp, stream);
     }
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? run_decode<true, false, 64>(gk, gkp, p, pp, stream)
-                                  : run_decode<true, false, 128>(gk, gkp, p, pp, stream);
-    return d.c.head_dim == 64 ? run_decode<false, false, 64>(gk, gkp, p, pp, stream)
-                              : run_decode<false, false, 128>(gk, gkp, p, pp, stream);
+        return d.c.head_dim == 64 ? run_decode<true, false, 64>(gk, p, pp, stream)
+                                  : run_decode<true, false, 128>(gk, p, pp, stream);
+    return d.c.head_dim == 64 ? run_decode<false, false, 64>(gk, p, pp, stream)
+                              : run_decode<false, false, 128>(gk, p, pp, stream);
 }
 
 }  // namespace pa
