@@ -19,8 +19,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor argument is a DEVICE pointer owned by the caller, row-major and contiguous, and
- *    aligned to 16 bytes. The library allocates no memory, keeps no state between calls (apart from
- *    a thread-local error message) and may be called from several threads.
+ *    aligned to 16 bytes. These entry points allocate no memory, keep no state between calls (apart
+ *    from a thread-local error message) and may be called from several threads. (The host-side
+ *    block manager of pa_block_manager.h, also in this library, is the one stateful part.)
  *  - 16-bit element type: PA_DTYPE_F16 (IEEE binary16) or PA_DTYPE_BF16 (bfloat16). Queries, keys,
  *    values, caches and outputs all share it. Arithmetic is float32; outputs are rounded to nearest
  *    even.
@@ -47,7 +48,8 @@
  *    faults.
  *  - Errors: PA_ERR_INVALID_ARG (bad pointer, alignment, count or size), PA_ERR_UNSUPPORTED (a
  *    head_dim or head-group size with no kernel), PA_ERR_WORKSPACE (workspace too small),
- *    PA_ERR_HIP (a launch failed). pa_last_error() gives the calling thread's last message.
+ *    PA_ERR_HIP (a launch failed), PA_ERR_NO_BLOCKS (block manager only). pa_last_error() gives
+ *    the calling thread's last message.
  */
 #ifndef PA_H
 #define PA_H
@@ -66,7 +68,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1,
     PA_ERR_UNSUPPORTED = 2,
     PA_ERR_WORKSPACE = 3,
-    PA_ERR_HIP = 4
+    PA_ERR_HIP = 4,
+    PA_ERR_NO_BLOCKS = 5 /* the block manager's free queue is too short (pa_block_manager.h) */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F16 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_dtype_t;

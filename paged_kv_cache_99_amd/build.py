@@ -1,6 +1,6 @@
 """Build the HIP library libpa.so (C ABI of include/pa.h) for gfx950 with hipcc.
 
-Every .hip source and the host-side pa_api.cpp are compiled in parallel to objects under
+Every .hip source and the host-side .cpp sources (the C ABI, the block manager) are compiled in parallel to objects under
 _build/, then linked into paged_kv_cache_99_amd/libpa.so next to this file.
 """
 import concurrent.futures
@@ -36,7 +36,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "pa_api.cpp")]
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     cmd = ["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] + objs

@@ -10,8 +10,10 @@
 #include "pa_internal.h"
 
 namespace {
-
 thread_local char g_error[512] = "";
+}  // namespace
+
+namespace pa {
 
 pa_status_t fail(pa_status_t s, const char *fmt, ...)
 {
@@ -27,6 +29,13 @@ pa_status_t ok()
     g_error[0] = '\0';
     return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -94,6 +103,7 @@ const char *pa_status_string(pa_status_t status)
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: no kernel for this shape";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks in the pool";
     }
     return "unknown pa_status_t";
 }

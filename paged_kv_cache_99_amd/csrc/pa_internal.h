@@ -5,7 +5,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Set the calling thread's pa_last_error() message and return s (pa_api.cpp).
+pa_status_t fail(pa_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the message and return PA_OK.
+pa_status_t ok();
 
 struct CacheDims {
     int32_t num_blocks;
