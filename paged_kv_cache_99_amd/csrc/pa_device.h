@@ -6,6 +6,9 @@
 
 namespace pa {
 
+// Marks a lambda always inlined (arrays it takes by reference then stay in registers).
+#define PA_INLINE __attribute__((always_inline))
+
 constexpr int kBlock = 16;  // tokens per physical block
 constexpr int kWave = 64;
 
@@ -152,6 +155,23 @@ __device__ __forceinline__ float group_sum(float v)
 __device__ __forceinline__ float xor_shfl(float v, int mask)
 {
     return __shfl_xor(v, mask, kWave);
+}
+
+// Lanes l and l ^ 32 combined (v_permlane32_swap_b32 with both operands = v gives, at every lane,
+// v of lanes l % 32 and 32 + l % 32 -- the lane and its partner, in lane order, so both partners
+// compute the same result bit for bit).
+__device__ __forceinline__ float pair_max(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_max(float v)

@@ -28,7 +28,17 @@
 // The causal mask is applied only on tiles that reach past the workgroup's first position. Keys
 // beyond the context are never loaded; LDS starts zeroed, so such slots hold finite stale values that
 // meet zero probabilities (no NaN reaches an MFMA).
+//
+// Two tile loops. Where every row of the workgroup attends at least kOnePartKeys keys, the loop is
+// software-pipelined so that the matrix cores and the vector ALUs work at once: while the softmax
+// of tile t runs on the VALU, the MFMAs of S^T for tile t+1 and of O^T += V^T P^T for tile t-1 are
+// in flight (K and V have separate double buffers: K runs two tiles ahead of V). P is rounded to
+// the 16-bit type in one part there. Rows with fewer keys -- the first rows of a prompt, where a
+// handful of keys can dominate and cancel -- take the plain loop, which splits a bfloat16 P into
+// hi + lo parts.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -72,8 +82,14 @@ struct PrefillParams {
     float scale_log2;
 };
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kPairs = kWaves * 32;      // (row, head) pairs per workgroup
 constexpr int kKeys = 64;  // keys per tile
+// A workgroup whose first row attends at least this many keys rounds P to the 16-bit type in one
+// part: a bfloat16 probability keeps 8 significant bits, and over L keys of comparable weight the
+// rounding errors add up to about 2^-9 |v| / sqrt(L) (below 1e-4 here), far inside the 2e-3 gate.
+constexpr int kOnePartKeys = 512;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -92,18 +108,22 @@ __device__ __forceinline__ int swz(int r)
 }
 
 template <bool BF, int D, int GK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 {
-    constexpr int R = 128 / GK;                     // query rows per workgroup
+    constexpr int R = kPairs / GK;                  // query rows per workgroup
     constexpr int DC = D / 16;                      // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;                      // 32-dim tiles of O^T
     constexpr int ROWB = D * 2;                     // bytes per LDS row (no padding)
     constexpr int CPR = D / 8;                      // 16-byte pieces per row
     constexpr int TILEB = kKeys * ROWB;             // bytes of one K or V tile
     constexpr int NLOAD = TILEB / (kThreads * 16);  // direct-to-LDS loads per thread per tile
-    __shared__ __align__(16) uint8_t smem[2][2][TILEB];  // [buffer][0 = K, 1 = V]
+    // Two K and two V tile buffers, each its own LDS object: the compiler can then tell that a
+    // direct-to-LDS load into one buffer leaves the others alone, and lets the reads of the tile
+    // being computed run while the next tiles are in flight.
+    __shared__ __align__(16) uint8_t k_lds0[TILEB], k_lds1[TILEB], v_lds0[TILEB], v_lds1[TILEB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
 
     const int item = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -123,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
     const int row_base = tile_r * R;
     if (row_base >= q_len)
         return;
-    const int L = min(max(p.seq_lens[seq], 0), p.max_blocks * kBlock);
+    const int L = p.num_blocks > 0 ? min(max(p.seq_lens[seq], 0), p.max_blocks * kBlock) : 0;
     const int first_pos = L - q_len;  // position of the chunk's row 0
 
     // this lane's (row, head) pair: column n of the wave's S^T / O^T tiles
@@ -147,31 +167,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
     const int unmasked_below = first_pos + row_base;  // every row of the group sees keys <= this
     const bool ragged_rows = row_base + R > q_len;
 
-    const int32_t *table = p.block_tables + (size_t)seq * p.max_blocks;
+    // the sequence's block table, read with scalar loads (it is read-only while the kernel runs)
+    typedef const __attribute__((address_space(4))) int32_t *ctable_t;
+    const ctable_t table = (ctable_t)(p.block_tables + (size_t)seq * p.max_blocks);
     const size_t blk_stride = (size_t)p.num_kv_heads * kBlock * D;
 
     // LDS starts zeroed: slots of keys that are never loaded then hold finite values
-#pragma unroll
-    for (int i = tid; i < 4 * TILEB / 16; i += kThreads)
-        ((uint4 *)&smem[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < TILEB / 16; i += kThreads) {
+        ((uint4 *)k_lds0)[i] = make_uint4(0, 0, 0, 0);
+        ((uint4 *)k_lds1)[i] = make_uint4(0, 0, 0, 0);
+        ((uint4 *)v_lds0)[i] = make_uint4(0, 0, 0, 0);
+        ((uint4 *)v_lds1)[i] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
 
-    // Direct-to-LDS loads of tile t into buffer b: load j of the wave covers LDS bytes
-    // [(j*4 + wave) * 1 KiB, +1 KiB); lane i writes the 16-byte piece at offset 16*i of that range.
-    // Those rows all lie in one paged block, so the block id and the source base are wave-uniform;
-    // the lane's offset inside the (block, kv head) tile -- its row, and the swizzled piece it
-    // stores -- is the same for every tile and every load.
-    // Block ids come from a register window: lane i holds table entry 64*w + i of window w (16
-    // tiles). The next window is fetched one window ahead, so no tile waits on a table read.
+    // Direct-to-LDS loads of tile t of one cache into buf: load j of the wave covers LDS bytes
+    // [(j * kWaves + wave) * 1 KiB, +1 KiB); lane i writes the 16-byte piece at offset 16*i of that
+    // range. Those rows all lie in one paged block, so the block id and the source base are
+    // wave-uniform; the lane's offset inside the (block, kv head) tile -- its row, and the
+    // swizzled piece it stores -- is the same for every tile and every load.
     const int lane_row = lane / CPR;
     const int lane_piece = lane % CPR;
-    const int n_blocks = (L + kBlock - 1) / kBlock;
-    auto table_window = [&](int w) {
-        const int i = w * kWave + lane;
-        return i < n_blocks ? table[i] : -1;
-    };
-    int win_cur = table_window(0), win_next = table_window(1);
-    auto issue = [&](int t, int b) {
+    auto issue_one = [&](const uint16_t *cache, uint8_t *buf, int t) PA_INLINE {
         const bool whole = (t + 1) * kKeys <= L;  // no key of this tile lies past the context
 #pragma unroll
         for (int j = 0; j < NLOAD; ++j) {
@@ -179,23 +196,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
             const int key0 = t * kKeys + first_row;
             if (key0 >= L)
                 continue;
-            const int bi = (key0 / kBlock) & (kWave - 1);  // slot in the window of tile t
-            const int blk = __builtin_amdgcn_readlane(win_cur, bi);
+            const int blk = table[key0 / kBlock];
             if ((unsigned)blk >= (unsigned)p.num_blocks)
                 continue;
             const size_t off = (size_t)blk * blk_stride +
                                ((size_t)kvh * kBlock + (key0 % kBlock) + lane_row) * D +
                                (lane_piece ^ swz<D>(first_row + lane_row)) * 8;
             const int lds_off = (j * kThreads + wave * kWave) * 16;
-            if (whole || key0 + lane_row < L) {
-                __builtin_amdgcn_global_load_lds(p.k_cache + off, (lds_void *)(&smem[b][0][lds_off]),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(p.v_cache + off, (lds_void *)(&smem[b][1][lds_off]),
-                                                 16, 0, 0);
-            }
+            if (whole || key0 + lane_row < L)
+                __builtin_amdgcn_global_load_lds(cache + off, (lds_void *)(buf + lds_off), 16, 0,
+                                                 0);
         }
     };
-    constexpr int kTilesPerWindow = kWave * kBlock / kKeys;  // 16
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 o[DT];
@@ -212,21 +224,242 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
     const int v_half = g16 >> 1;                     // lane half h of the destination lanes
     const int v_dim = (g16 & 1) * 16 + 4 * v_q;      // dim within a 32-dim tile
 
-    if (n_tiles > 0)
+    // a bfloat16 P needs its hi + lo split only while some row sees few keys (see kOnePartKeys)
+    const bool one_part = !BF || first_pos + row_base + 1 >= kOnePartKeys;
+    if (one_part && n_tiles > 0) {
+        // ---------------------------------------------------------------- pipelined loop
+        // Iteration t issues K tile t+2 (into K buffer t & 1) and V tile t (into V buffer t & 1)
+        // and computes PV(t-1), QK(t+1) and the softmax of tile t; both reads hit the other
+        // buffers. The buffer of an iteration is fixed at compile time (parity P = t & 1).
+        auto kbuf = [&](auto par) PA_INLINE -> uint8_t * {
+            if constexpr (decltype(par)::value == 0)
+                return k_lds0;
+            else
+                return k_lds1;
+        };
+        auto vbuf = [&](auto par) PA_INLINE -> uint8_t * {
+            if constexpr (decltype(par)::value == 0)
+                return v_lds0;
+            else
+                return v_lds1;
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+
+        // S^T = K Q^T of one tile into s, k-steps [C0, C1) (k-step 0 starts from zero)
+        auto qk = [&](auto c0, auto c1, f32x16 (&s)[2], const uint8_t *kb) PA_INLINE {
+            const f32x16 zero = {};
+#pragma unroll
+            for (int c = decltype(c0)::value; c < decltype(c1)::value; ++c)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const uint4 a = *(const uint4 *)(kb + (kt * 32 + n) * ROWB +
+                                                     (((2 * c + hh) ^ k_sw) * 16));
+                    s[kt] = mfma32<BF>(a, qv[c], c == 0 ? zero : s[kt]);
+                }
+        };
+        // O^T += V^T P^T for the 16 keys of step c4 of one tile
+        auto pv = [&](auto c4c, const uint4 (&pt)[4], const uint8_t *vb) PA_INLINE {
+            constexpr int c4 = decltype(c4c)::value;
+            const int r1 = c4 * 16 + 4 * v_half + v_k, r2 = r1 + 8;
+            uint4 a[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int dim = dt * 32 + v_dim;
+                const int off1 = r1 * ROWB + (((dim >> 3) ^ swz<D>(r1)) << 4) + (dim & 7) * 2;
+                const int off2 = r2 * ROWB + (((dim >> 3) ^ swz<D>(r2)) << 4) + (dim & 7) * 2;
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off1));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off2));
+                a[dt].x = __builtin_bit_cast(uint2, lo4).x;
+                a[dt].y = __builtin_bit_cast(uint2, lo4).y;
+                a[dt].z = __builtin_bit_cast(uint2, hi4).x;
+                a[dt].w = __builtin_bit_cast(uint2, hi4).y;
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = mfma32<BF>(a[dt], pt[c4], o[dt]);
+        };
+        // invalid rows (past the chunk) have zero queries and are never stored: no mask for them
+        const int pos_p = row_ok ? pos : 0x3fffffff;
+        // Online softmax of the tile in s, in three parts: the maximum (and the mask), the
+        // exponentials of values [I0, I1) (value i = s[i / 16][i % 16]), and the packing of P.
+        float ms = 0.0f, psum = 0.0f;
+        auto sm_max = [&](auto masked, f32x16 (&s)[2], int t) PA_INLINE -> float {
+            if constexpr (decltype(masked)::value) {
+                const int last = pos_p - t * kKeys - 4 * hh;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        s[kt][v] = kt * 32 + 8 * (v >> 2) + (v & 3) <= last ? s[kt][v] : -INFINITY;
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    mx = fmaxf(mx, s[kt][v]);
+            mx = pair_max(mx) * p.scale_log2;  // scale > 0 keeps the order
+            const float mn = fmaxf(m_run, mx);
+            ms = mn == -INFINITY ? 0.0f : mn;
+            const float alpha = fast_exp2(m_run - ms);
+            m_run = mn;
+            psum = 0.0f;
+            return alpha;
+        };
+        auto sm_exp = [&](auto i0, auto i1, f32x16 (&s)[2]) PA_INLINE {
+#pragma unroll
+            for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i) {
+                s[i >> 4][i & 15] = fast_exp2(fmaf(s[i >> 4][i & 15], p.scale_log2, -ms));
+                psum += s[i >> 4][i & 15];
+            }
+        };
+        auto sm_pack = [&](auto c4c, const f32x16 (&s)[2], uint4 (&pt)[4]) PA_INLINE {
+            constexpr int c4 = decltype(c4c)::value, kt = c4 >> 1, b = 8 * (c4 & 1);
+            pt[c4].x = pack2<BF>(s[kt][b + 0], s[kt][b + 1]);
+            pt[c4].y = pack2<BF>(s[kt][b + 2], s[kt][b + 3]);
+            pt[c4].z = pack2<BF>(s[kt][b + 4], s[kt][b + 5]);
+            pt[c4].w = pack2<BF>(s[kt][b + 6], s[kt][b + 7]);
+        };
+        // The work of one iteration in four chunks; the compiler interleaves within a chunk and
+        // never moves work across chunk boundaries, which bounds the operands in flight.
+        auto region = [&](auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
+                          const uint4 (&p_in)[4], uint4 (&p_out)[4], const uint8_t *kb,
+                          const uint8_t *vb) PA_INLINE -> float {
+            using C = std::integral_constant<int, 0>;
+            pv(std::integral_constant<int, 0>{}, p_in, vb);
+            qk(C{}, std::integral_constant<int, DC / 4>{}, s_out, kb);
+            const float alpha = sm_max(masked, s_in, t);
+            __builtin_amdgcn_sched_barrier(0);
+            pv(std::integral_constant<int, 1>{}, p_in, vb);
+            qk(std::integral_constant<int, DC / 4>{}, std::integral_constant<int, DC / 2>{}, s_out, kb);
+            sm_exp(C{}, std::integral_constant<int, 11>{}, s_in);
+            sm_pack(std::integral_constant<int, 0>{}, s_in, p_out);
+            __builtin_amdgcn_sched_barrier(0);
+            pv(std::integral_constant<int, 2>{}, p_in, vb);
+            qk(std::integral_constant<int, DC / 2>{}, std::integral_constant<int, 3 * DC / 4>{}, s_out, kb);
+            sm_exp(std::integral_constant<int, 11>{}, std::integral_constant<int, 22>{}, s_in);
+            sm_pack(std::integral_constant<int, 1>{}, s_in, p_out);
+            __builtin_amdgcn_sched_barrier(0);
+            pv(std::integral_constant<int, 3>{}, p_in, vb);
+            qk(std::integral_constant<int, 3 * DC / 4>{}, std::integral_constant<int, DC>{}, s_out, kb);
+            sm_exp(std::integral_constant<int, 22>{}, std::integral_constant<int, 32>{}, s_in);
+            sm_pack(std::integral_constant<int, 2>{}, s_in, p_out);
+            sm_pack(std::integral_constant<int, 3>{}, s_in, p_out);
+            l_run = l_run * alpha + psum;
+            // P is complete here: keeps the compiler from sinking the softmax into the next
+            // iteration, past its rescale branch, where it would no longer overlap these MFMAs
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                asm volatile("" : "+v"(p_out[c4].x), "+v"(p_out[c4].y), "+v"(p_out[c4].z),
+                                  "+v"(p_out[c4].w));
+            __builtin_amdgcn_sched_barrier(0);
+            return alpha;
+        };
+
+        // tiles from t_mask on reach past the first row's position
+        const int t_mask = min(n_tiles, max(0, (first_pos + row_base + 1) / kKeys));
+        f32x16 sa[2], sb[2];
+        uint4 pa[4], pb[4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+            pb[c4] = make_uint4(0, 0, 0, 0);  // "tile -1": zero probabilities
+        float alpha_prev = 1.0f;
+        bool rescale = false;
+
+        issue_one(p.k_cache, k_lds0, 0);
+        if (n_tiles > 1)
+            issue_one(p.k_cache, k_lds1, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        qk(std::integral_constant<int, 0>{}, std::integral_constant<int, DC>{}, sa, k_lds0);
+
+        // One iteration of parity P = t & 1: s_in holds S of tile t, s_out receives S of tile
+        // t+1, p_in is P of tile t-1. After the loads are issued it is straight-line code, so the
+        // scheduler can interleave the MFMAs of pv and qk with the vector work of the softmax.
+        auto iter = [&](auto par, auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
+                        const uint4 (&p_in)[4], uint4 (&p_out)[4]) PA_INLINE {
+            constexpr int P = decltype(par)::value;
+            __builtin_amdgcn_s_waitcnt(0);  // K tile t+1 and V tile t-1 have landed
+            __syncthreads();                // and every wave is done with iteration t-1
+            if (t + 2 < n_tiles)
+                issue_one(p.k_cache, kbuf(par), t + 2);  // K buffer P held tile t, done
+            issue_one(p.v_cache, vbuf(par), t);          // V buffer P held tile t-2, done
+            if (rescale) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        o[dt][v] *= alpha_prev;
+            }
+            // K tile t+1 (past the last tile: stale, finite) and V tile t-1 (before the first:
+            // zeros) are in the buffers of the other parity
+            const float alpha = region(masked, t, s_in, s_out, p_in, p_out,
+                                       kbuf(std::integral_constant<int, 1 - P>{}),
+                                       vbuf(std::integral_constant<int, 1 - P>{}));
+            rescale = !__all(alpha == 1.0f);
+            alpha_prev = alpha;
+        };
+        // Tiles [t, t_end) with or without the mask, two per trip (even t first) so that S and P
+        // alternate between their two register sets without copies. At entry and exit S of tile t
+        // is in sa and P of tile t-1 in pb.
+        int t = 0;
+        auto swap_sets = [&]() PA_INLINE {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                sa[kt] = sb[kt];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                pb[c4] = pa[c4];
+        };
+        auto run = [&](auto masked, int t_end) PA_INLINE {
+            if ((t & 1) && t < t_end) {
+                iter(P1{}, masked, t, sa, sb, pb, pa);
+                ++t;
+                swap_sets();
+            }
+            for (; t + 1 < t_end; t += 2) {
+                iter(P0{}, masked, t, sa, sb, pb, pa);
+                iter(P1{}, masked, t + 1, sb, sa, pa, pb);
+            }
+            if (t < t_end) {
+                iter(P0{}, masked, t, sa, sb, pb, pa);
+                ++t;
+                swap_sets();
+            }
+        };
+        run(std::false_type{}, t_mask);
+        run(std::true_type{}, n_tiles);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (rescale) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    o[dt][v] *= alpha_prev;
+        }
+        const uint8_t *v_last = ((n_tiles - 1) & 1) ? v_lds1 : v_lds0;
+        pv(std::integral_constant<int, 0>{}, pb, v_last);
+        pv(std::integral_constant<int, 1>{}, pb, v_last);
+        pv(std::integral_constant<int, 2>{}, pb, v_last);
+        pv(std::integral_constant<int, 3>{}, pb, v_last);
+    }
+
+    // ---------------------------------------------------------------- plain loop (split P)
+    auto issue = [&](int t, int b) PA_INLINE {
+        issue_one(p.k_cache, b ? k_lds1 : k_lds0, t);
+        issue_one(p.v_cache, b ? v_lds1 : v_lds0, t);
+    };
+    if (!one_part && n_tiles > 0)
         issue(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int t = 0; !one_part && t < n_tiles; ++t) {
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed in LDS
         __syncthreads();                // everyone's have; everyone is done with tile t-1
-        if (t + 1 < n_tiles) {
-            if ((t + 1) % kTilesPerWindow == 0) {  // tile t+1 opens the next window
-                win_cur = win_next;
-                win_next = table_window((t + 1) / kTilesPerWindow + 1);
-            }
+        if (t + 1 < n_tiles)
             issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
-        }
-        const uint8_t *kb = &smem[t & 1][0][0];
-        const uint8_t *vb = &smem[t & 1][1][0];
-
+        const uint8_t *kb = (t & 1) ? k_lds1 : k_lds0;
+        const uint8_t *vb = (t & 1) ? v_lds1 : v_lds0;
         // the two 32-key halves are independent accumulator chains: interleave them so that no
         // MFMA waits on the one issued just before it
         f32x16 s[2];
@@ -328,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
         }
     }
 
-    l_run += xor_shfl(l_run, 32);
+    l_run = pair_sum(l_run);
     if (!row_ok)
         return;
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -391,7 +624,7 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
     p.num_blocks = d.c.num_blocks;
     p.n_sub = group / gk;
     p.total_q = d.total_q;
-    const int rows_per_wg = 128 / gk;
+    const int rows_per_wg = kPairs / gk;
     p.row_tiles = (d.max_q_len + rows_per_wg - 1) / rows_per_wg;
     const int64_t items = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.row_tiles;
     if (items > 0x7ffffff0)
