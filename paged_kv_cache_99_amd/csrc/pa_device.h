@@ -199,6 +199,33 @@ __device__ __forceinline__ uint4 load_nt(const void *p)
     return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
+// 16-byte direct-to-LDS load (global_load_lds_dwordx4, scalar-base form): lane i reads the 16
+// bytes at sbase + voff_i and writes them to LDS address lds + 16 * i; sbase and lds are
+// wave-uniform. M0 carries the LDS address and needs one wait state (s_nop 0) before the load
+// reads it. Issued from inline assembly so that the compiler does not model the LDS write: it then
+// inserts no wait for it before LDS reads of other buffers. The caller orders it -- s_waitcnt
+// vmcnt and a barrier -- before its data is read or its buffer reused.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const lds_u8 *)p;
+}
+
+// 16-byte LDS read at byte address addr (ds_read_b128).
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr)
+{
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)addr;
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void dma16_to_lds(uint32_t voff, const void *sbase, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ float fast_exp2(float x)
 {
     return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0

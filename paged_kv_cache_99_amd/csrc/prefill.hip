@@ -117,10 +117,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     constexpr int CPR = D / 8;                      // 16-byte pieces per row
     constexpr int TILEB = kKeys * ROWB;             // bytes of one K or V tile
     constexpr int NLOAD = TILEB / (kThreads * 16);  // direct-to-LDS loads per thread per tile
-    // Two K and two V tile buffers, each its own LDS object: the compiler can then tell that a
-    // direct-to-LDS load into one buffer leaves the others alone, and lets the reads of the tile
-    // being computed run while the next tiles are in flight.
-    __shared__ __align__(16) uint8_t k_lds0[TILEB], k_lds1[TILEB], v_lds0[TILEB], v_lds1[TILEB];
+    // Four K slots and four V slots of one 64-key tile each: 64-key tile j of the K cache lives in
+    // bytes [(j % 4) * TILEB, +TILEB), of the V cache from (4 + j % 4) * TILEB on. The direct-to-LDS loads are
+    // issued so that the compiler does not track them (dma16_to_lds): reads of the tiles being
+    // computed run while later tiles are in flight, and every wait for a load is explicit below.
+    __shared__ __align__(1024) uint8_t lds[8 * TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,41 +174,56 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const size_t blk_stride = (size_t)p.num_kv_heads * kBlock * D;
 
     // LDS starts zeroed: slots of keys that are never loaded then hold finite values
-    for (int i = tid; i < TILEB / 16; i += kThreads) {
-        ((uint4 *)k_lds0)[i] = make_uint4(0, 0, 0, 0);
-        ((uint4 *)k_lds1)[i] = make_uint4(0, 0, 0, 0);
-        ((uint4 *)v_lds0)[i] = make_uint4(0, 0, 0, 0);
-        ((uint4 *)v_lds1)[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = tid; i < 8 * TILEB / 16; i += kThreads)
+        ((uint4 *)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    // Direct-to-LDS loads of tile t of one cache into buf: load j of the wave covers LDS bytes
-    // [(j * kWaves + wave) * 1 KiB, +1 KiB); lane i writes the 16-byte piece at offset 16*i of that
-    // range. Those rows all lie in one paged block, so the block id and the source base are
-    // wave-uniform; the lane's offset inside the (block, kv head) tile -- its row, and the
-    // swizzled piece it stores -- is the same for every tile and every load.
+    // Direct-to-LDS loads of the SPAN * 64 keys from key t * 64 * SPAN of one cache into buf: load
+    // j of the wave covers LDS bytes [(j * kWaves + wave) * 1 KiB, +1 KiB); lane i writes the
+    // 16-byte piece at offset 16*i of that range. Those rows all lie in one paged block, so the
+    // source base (block, kv head) is wave-uniform. The lane's byte offset inside the (block, kv
+    // head) tile -- its row, and the swizzled piece it stores -- is the same for every load: the
+    // first row of a load is a multiple of 16 plus a wave constant. The block ids are fetched
+    // first (scalar loads, one wait), then the loads go out. Returns how many load instructions
+    // this wave issued: one per load whose first row lies in the context (a load whose block id
+    // is outside the pool is skipped, and then the counted waits may end early -- such tables give
+    // unspecified results, never a fault).
     const int lane_row = lane / CPR;
     const int lane_piece = lane % CPR;
-    auto issue_one = [&](const uint16_t *cache, uint8_t *buf, int t) PA_INLINE {
-        const bool whole = (t + 1) * kKeys <= L;  // no key of this tile lies past the context
+    const int row0 = (wave * kWave / CPR) % kBlock;  // first row of every load of this wave, mod 16
+    const uint32_t dma_voff =
+        (uint32_t)(((row0 + lane_row) * D + (lane_piece ^ swz<D>(row0 + lane_row)) * 8) * 2);
+    const size_t blk_bytes = blk_stride * 2;
+    const size_t kvh_bytes = (size_t)kvh * kBlock * D * 2;
+    auto issue_span = [&](auto span, const uint16_t *cache, uint8_t *buf, int t) PA_INLINE -> int {
+        constexpr int SPAN = decltype(span)::value, NL = NLOAD * SPAN, KEYS = kKeys * SPAN;
+        const bool whole = (t + 1) * KEYS <= L;  // no key of these tiles lies past the context
+        int blk[NL];
 #pragma unroll
-        for (int j = 0; j < NLOAD; ++j) {
+        for (int j = 0; j < NL; ++j) {
+            const int key0 = t * KEYS + (j * kThreads + wave * kWave) / CPR;
+            blk[j] = key0 < L ? table[key0 / kBlock] : -1;
+        }
+        int issued = 0;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
             const int first_row = (j * kThreads + wave * kWave) / CPR;  // wave-uniform
-            const int key0 = t * kKeys + first_row;
+            const int key0 = t * KEYS + first_row;
             if (key0 >= L)
                 continue;
-            const int blk = table[key0 / kBlock];
-            if ((unsigned)blk >= (unsigned)p.num_blocks)
+            ++issued;
+            if ((unsigned)blk[j] >= (unsigned)p.num_blocks)
                 continue;
-            const size_t off = (size_t)blk * blk_stride +
-                               ((size_t)kvh * kBlock + (key0 % kBlock) + lane_row) * D +
-                               (lane_piece ^ swz<D>(first_row + lane_row)) * 8;
-            const int lds_off = (j * kThreads + wave * kWave) * 16;
+            const char *sbase = (const char *)cache + kvh_bytes + (size_t)blk[j] * blk_bytes;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                lds_address(buf + (j * kThreads + wave * kWave) * 16));
             if (whole || key0 + lane_row < L)
-                __builtin_amdgcn_global_load_lds(cache + off, (lds_void *)(buf + lds_off), 16, 0,
-                                                 0);
+                dma16_to_lds(dma_voff, sbase, dst);
         }
+        return issued;
     };
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 o[DT];
@@ -228,48 +244,67 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const bool one_part = !BF || first_pos + row_base + 1 >= kOnePartKeys;
     if (one_part && n_tiles > 0) {
         // ---------------------------------------------------------------- pipelined loop
-        // Iteration t issues K tile t+2 (into K buffer t & 1) and V tile t (into V buffer t & 1)
-        // and computes PV(t-1), QK(t+1) and the softmax of tile t; both reads hit the other
-        // buffers. The buffer of an iteration is fixed at compile time (parity P = t & 1).
-        auto kbuf = [&](auto par) PA_INLINE -> uint8_t * {
-            if constexpr (decltype(par)::value == 0)
-                return k_lds0;
-            else
-                return k_lds1;
-        };
-        auto vbuf = [&](auto par) PA_INLINE -> uint8_t * {
-            if constexpr (decltype(par)::value == 0)
-                return v_lds0;
-            else
-                return v_lds1;
-        };
+        // Step t computes PV(t-1), QK(t+1) and the softmax of tile t. Tiles are loaded in pairs:
+        // odd steps t = 2u+1 wait for the loads of step t-2, pass a barrier and issue K tiles
+        // 2u+4, 2u+5 (into the slots of K tiles 2u, 2u+1, which QK read in steps 2u-1 and 2u)
+        // and V tiles 2u+2, 2u+3 (into the slots of V tiles 2u-2, 2u-1, read by PV in steps
+        // 2u-1 and 2u): every load gets two steps to land.
+        auto kslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (j & 3) * TILEB; };
+        auto vslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (4 + (j & 3)) * TILEB; };
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
+        // wait until at most n of this wave's loads are in flight (and LDS/scalar reads are done)
+        auto wait_loads = [&](int n) PA_INLINE {
+            switch (n) {
+            case 0: __builtin_amdgcn_s_waitcnt(0x70); break;
+            case 1: __builtin_amdgcn_s_waitcnt(0x71); break;
+            case 2: __builtin_amdgcn_s_waitcnt(0x72); break;
+            case 3: __builtin_amdgcn_s_waitcnt(0x73); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0x74); break;
+            case 5: __builtin_amdgcn_s_waitcnt(0x75); break;
+            case 6: __builtin_amdgcn_s_waitcnt(0x76); break;
+            case 7: __builtin_amdgcn_s_waitcnt(0x77); break;
+            default: __builtin_amdgcn_s_waitcnt(0x78); break;
+            }
+        };
+        static_assert(4 * NLOAD <= 8, "wait_loads covers a K pair and a V pair");
 
-        // S^T = K Q^T of one tile into s, k-steps [C0, C1) (k-step 0 starts from zero)
-        auto qk = [&](auto c0, auto c1, f32x16 (&s)[2], const uint8_t *kb) PA_INLINE {
+        // LDS read addresses, computed per step from one lane base per cache (no per-slot
+        // registers). K operand of k-step c, rows kt*32 + n: piece (2c + hh) ^ swz(n) of the row,
+        // i.e. byte (32 c) ^ 16 (hh ^ swz(n)). V operand of 32-dim tile dt, key rows r1 = 16 c4 +
+        // 4 v_half + v_k and r2 = r1 + 8: piece (dim / 8) ^ swz(r), i.e. byte (64 dt) ^ 16 w for a
+        // lane constant w, and swz(r2) differs from swz(r1) in one bit (X2). Slot bases are
+        // multiples of 8 KiB and the lane bases stay below 8 KiB, so the XORs and the slot offset
+        // never interact.
+        const uint32_t lds0 = lds_address(lds);
+        const int k_lane = n * ROWB + 16 * (hh ^ k_sw);
+        const int r1b = 4 * v_half + v_k;
+        const int v_lane = r1b * ROWB + 16 * ((v_dim >> 3) ^ swz<D>(r1b)) + (v_dim & 7) * 2;
+        constexpr int X2 = D == 128 ? 16 : 64;
+
+        // S^T = K Q^T of one tile into s, k-steps [C0, C1) (k-step 0 starts from zero); ka is the
+        // lane's K base in the tile's slot
+        auto qk = [&](auto c0, auto c1, f32x16 (&s)[2], uint32_t ka) PA_INLINE {
             const f32x16 zero = {};
 #pragma unroll
             for (int c = decltype(c0)::value; c < decltype(c1)::value; ++c)
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    const uint4 a = *(const uint4 *)(kb + (kt * 32 + n) * ROWB +
-                                                     (((2 * c + hh) ^ k_sw) * 16));
+                    const uint32_t addr = (ka ^ (32 * c)) + kt * 32 * ROWB;
+                    const uint4 a = lds_read16(addr);
                     s[kt] = mfma32<BF>(a, qv[c], c == 0 ? zero : s[kt]);
                 }
         };
-        // O^T += V^T P^T for the 16 keys of step c4 of one tile
-        auto pv = [&](auto c4c, const uint4 (&pt)[4], const uint8_t *vb) PA_INLINE {
+        // O^T += V^T P^T for the 16 keys of step c4 of one tile; va is the lane's V base
+        auto pv = [&](auto c4c, const uint4 (&pt)[4], uint32_t va) PA_INLINE {
             constexpr int c4 = decltype(c4c)::value;
-            const int r1 = c4 * 16 + 4 * v_half + v_k, r2 = r1 + 8;
             uint4 a[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int dim = dt * 32 + v_dim;
-                const int off1 = r1 * ROWB + (((dim >> 3) ^ swz<D>(r1)) << 4) + (dim & 7) * 2;
-                const int off2 = r2 * ROWB + (((dim >> 3) ^ swz<D>(r2)) << 4) + (dim & 7) * 2;
-                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off1));
-                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + off2));
+                const uint32_t a1 = (va ^ (64 * dt)) + c4 * 16 * ROWB;
+                const uint32_t a2 = (va ^ (64 * dt) ^ X2) + (c4 * 16 + 8) * ROWB;
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)a1);
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)a2);
                 a[dt].x = __builtin_bit_cast(uint2, lo4).x;
                 a[dt].y = __builtin_bit_cast(uint2, lo4).y;
                 a[dt].z = __builtin_bit_cast(uint2, hi4).x;
@@ -324,8 +359,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         // The work of one iteration in four chunks; the compiler interleaves within a chunk and
         // never moves work across chunk boundaries, which bounds the operands in flight.
         auto region = [&](auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
-                          const uint4 (&p_in)[4], uint4 (&p_out)[4], const uint8_t *kb,
-                          const uint8_t *vb) PA_INLINE -> float {
+                          const uint4 (&p_in)[4], uint4 (&p_out)[4], uint32_t kb,
+                          uint32_t vb) PA_INLINE -> float {
             using C = std::integral_constant<int, 0>;
             pv(std::integral_constant<int, 0>{}, p_in, vb);
             qk(C{}, std::integral_constant<int, DC / 4>{}, s_out, kb);
@@ -367,24 +402,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         float alpha_prev = 1.0f;
         bool rescale = false;
 
-        issue_one(p.k_cache, k_lds0, 0);
-        if (n_tiles > 1)
-            issue_one(p.k_cache, k_lds1, 1);
-        __builtin_amdgcn_s_waitcnt(0);
+        // K tiles 0..3 and V tiles 0, 1 before step 0; QK(0) needs K tiles 0, 1 only
+        (void)issue_span(Two{}, p.k_cache, kslot(0), 0);
+        const int c1 = n_tiles > 2 ? issue_span(Two{}, p.k_cache, kslot(2), 1) : 0;
+        const int c2 = issue_span(Two{}, p.v_cache, vslot(0), 0);
+        wait_loads(c1 + c2);
         __syncthreads();
-        qk(std::integral_constant<int, 0>{}, std::integral_constant<int, DC>{}, sa, k_lds0);
+        qk(std::integral_constant<int, 0>{}, std::integral_constant<int, DC>{}, sa,
+           lds0 + k_lane);
 
-        // One iteration of parity P = t & 1: s_in holds S of tile t, s_out receives S of tile
-        // t+1, p_in is P of tile t-1. After the loads are issued it is straight-line code, so the
-        // scheduler can interleave the MFMAs of pv and qk with the vector work of the softmax.
+        // One step, t % 2 == P: s_in holds S of tile t, s_out receives S of tile t+1, p_in is P
+        // of tile t-1. After the loads are issued it is straight-line code, so the scheduler can
+        // interleave the MFMAs of pv and qk with the vector work of the softmax.
         auto iter = [&](auto par, auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
                         const uint4 (&p_in)[4], uint4 (&p_out)[4]) PA_INLINE {
-            constexpr int P = decltype(par)::value;
-            __builtin_amdgcn_s_waitcnt(0);  // K tile t+1 and V tile t-1 have landed
-            __syncthreads();                // and every wave is done with iteration t-1
-            if (t + 2 < n_tiles)
-                issue_one(p.k_cache, kbuf(par), t + 2);  // K buffer P held tile t, done
-            issue_one(p.v_cache, vbuf(par), t);          // V buffer P held tile t-2, done
+            if constexpr (decltype(par)::value == 1) {
+                const int u = t >> 1;  // t = 2u + 1
+                wait_loads(0);         // K tiles 2u+2, 2u+3 and V tiles 2u, 2u+1 landed
+                __syncthreads();       // for every wave; every wave is done with step t-1
+                if (2 * u + 4 < n_tiles)
+                    (void)issue_span(Two{}, p.k_cache, kslot(2 * u + 4), u + 2);
+                if (2 * u + 2 < n_tiles)
+                    (void)issue_span(Two{}, p.v_cache, vslot(2 * u + 2), u + 1);
+            }
             if (rescale) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
@@ -393,16 +433,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                         o[dt][v] *= alpha_prev;
             }
             // K tile t+1 (past the last tile: stale, finite) and V tile t-1 (before the first:
-            // zeros) are in the buffers of the other parity
-            const float alpha = region(masked, t, s_in, s_out, p_in, p_out,
-                                       kbuf(std::integral_constant<int, 1 - P>{}),
-                                       vbuf(std::integral_constant<int, 1 - P>{}));
+            // slot 3, still zero)
+            const uint32_t kb = lds0 + ((t + 1) & 3) * TILEB + k_lane;
+            const uint32_t vb = lds0 + (4 + ((t - 1) & 3)) * TILEB + v_lane;
+            const float alpha = region(masked, t, s_in, s_out, p_in, p_out, kb, vb);
             rescale = !__all(alpha == 1.0f);
             alpha_prev = alpha;
         };
-        // Tiles [t, t_end) with or without the mask, two per trip (even t first) so that S and P
-        // alternate between their two register sets without copies. At entry and exit S of tile t
-        // is in sa and P of tile t-1 in pb.
+        // Steps [t, t_end) with or without the mask, two per trip (even t first) so that S and P
+        // alternate between their two register sets without copies. At entry and exit S of tile
+        // t is in sa and P of tile t-1 in pb.
         int t = 0;
         auto swap_sets = [&]() PA_INLINE {
 #pragma unroll
@@ -430,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         };
         run(std::false_type{}, t_mask);
         run(std::true_type{}, n_tiles);
-        __builtin_amdgcn_s_waitcnt(0);
+        wait_loads(0);
         __syncthreads();
         if (rescale) {
 #pragma unroll
@@ -439,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                 for (int v = 0; v < 16; ++v)
                     o[dt][v] *= alpha_prev;
         }
-        const uint8_t *v_last = ((n_tiles - 1) & 1) ? v_lds1 : v_lds0;
+        const uint32_t v_last = lds0 + (4 + ((n_tiles - 1) & 3)) * TILEB + v_lane;
         pv(std::integral_constant<int, 0>{}, pb, v_last);
         pv(std::integral_constant<int, 1>{}, pb, v_last);
         pv(std::integral_constant<int, 2>{}, pb, v_last);
@@ -448,8 +488,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 
     // ---------------------------------------------------------------- plain loop (split P)
     auto issue = [&](int t, int b) PA_INLINE {
-        issue_one(p.k_cache, b ? k_lds1 : k_lds0, t);
-        issue_one(p.v_cache, b ? v_lds1 : v_lds0, t);
+        (void)issue_span(One{}, p.k_cache, lds + b * TILEB, t);
+        (void)issue_span(One{}, p.v_cache, lds + (4 + b) * TILEB, t);
     };
     if (!one_part && n_tiles > 0)
         issue(0, 0);
@@ -458,8 +498,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         __syncthreads();                // everyone's have; everyone is done with tile t-1
         if (t + 1 < n_tiles)
             issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
-        const uint8_t *kb = (t & 1) ? k_lds1 : k_lds0;
-        const uint8_t *vb = (t & 1) ? v_lds1 : v_lds0;
+        const uint8_t *kb = lds + (t & 1) * TILEB;
+        const uint8_t *vb = lds + (4 + (t & 1)) * TILEB;
         // the two 32-key halves are independent accumulator chains: interleave them so that no
         // MFMA waits on the one issued just before it
         f32x16 s[2];
