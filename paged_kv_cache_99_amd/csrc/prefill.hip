@@ -116,7 +116,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     constexpr int ROWB = D * 2;                     // bytes per LDS row (no padding)
     constexpr int CPR = D / 8;                      // 16-byte pieces per row
     constexpr int TILEB = kKeys * ROWB;             // bytes of one K or V tile
-    constexpr int NLOAD = TILEB / (kThreads * 16);  // direct-to-LDS loads per thread per tile
     // Four K slots and four V slots of one 64-key tile each: 64-key tile j of the K cache lives in
     // bytes [(j % 4) * TILEB, +TILEB), of the V cache from (4 + j % 4) * TILEB on. The direct-to-LDS loads are
     // issued so that the compiler does not track them (dma16_to_lds): reads of the tiles being
@@ -178,47 +177,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         ((uint4 *)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    // Direct-to-LDS loads of the SPAN * 64 keys from key t * 64 * SPAN of one cache into buf: load
-    // j of the wave covers LDS bytes [(j * kWaves + wave) * 1 KiB, +1 KiB); lane i writes the
-    // 16-byte piece at offset 16*i of that range. Those rows all lie in one paged block, so the
-    // source base (block, kv head) is wave-uniform. The lane's byte offset inside the (block, kv
-    // head) tile -- its row, and the swizzled piece it stores -- is the same for every load: the
-    // first row of a load is a multiple of 16 plus a wave constant. The block ids are fetched
-    // first (scalar loads, one wait), then the loads go out. Returns how many load instructions
-    // this wave issued: one per load whose first row lies in the context (a load whose block id
-    // is outside the pool is skipped, and then the counted waits may end early -- such tables give
-    // unspecified results, never a fault).
+    // Direct-to-LDS loads of the SPAN * 64 keys from key t * 64 * SPAN of one cache into buf. Wave
+    // w loads paged block w of the span (16 rows, one block id, one source base): PER_BLK loads of
+    // RPI rows each; lane i of load k writes the 16-byte piece at LDS offset 16*i of rows
+    // [16 w + k RPI, +RPI). Its source is row k RPI + i / CPR of the (block, kv head) tile, piece
+    // (i % CPR) ^ swz(row) -- the same for every block, so the lane offsets are computed once.
+    // Returns how many load instructions this wave issued (the counted waits below rely on it; a
+    // block id outside the pool skips its loads but still counts them, so such tables make those
+    // waits end early -- unspecified results, never a fault). A load instruction is issued exactly
+    // when its first row lies in the context, so at least one of its lanes is active.
+    constexpr int RPI = kWave * 16 / ROWB;       // rows per load instruction
+    constexpr int PER_BLK = kBlock / RPI;        // load instructions per block
     const int lane_row = lane / CPR;
     const int lane_piece = lane % CPR;
-    const int row0 = (wave * kWave / CPR) % kBlock;  // first row of every load of this wave, mod 16
-    const uint32_t dma_voff =
-        (uint32_t)(((row0 + lane_row) * D + (lane_piece ^ swz<D>(row0 + lane_row)) * 8) * 2);
+    uint32_t dma_voff[PER_BLK];
+#pragma unroll
+    for (int k = 0; k < PER_BLK; ++k) {
+        const int r = k * RPI + lane_row;
+        dma_voff[k] = (uint32_t)((r * D + (lane_piece ^ swz<D>(r)) * 8) * 2);
+    }
     const size_t blk_bytes = blk_stride * 2;
     const size_t kvh_bytes = (size_t)kvh * kBlock * D * 2;
     auto issue_span = [&](auto span, const uint16_t *cache, uint8_t *buf, int t) PA_INLINE -> int {
-        constexpr int SPAN = decltype(span)::value, NL = NLOAD * SPAN, KEYS = kKeys * SPAN;
-        const bool whole = (t + 1) * KEYS <= L;  // no key of these tiles lies past the context
-        int blk[NL];
+        constexpr int KEYS = kKeys * decltype(span)::value, NBLK = KEYS / kBlock;
+        static_assert(NBLK <= kWaves, "one block per wave");
+        const int key0 = t * KEYS + wave * kBlock;  // first key of this wave's block
+        if (wave >= NBLK || key0 >= L)
+            return 0;
+        const int blk = table[key0 / kBlock];
+        if ((unsigned)blk >= (unsigned)p.num_blocks)
+            return PER_BLK;
+        const char *sbase = (const char *)cache + kvh_bytes + (size_t)blk * blk_bytes;
+        const uint32_t dst0 = lds_address(buf + wave * kBlock * ROWB);
+        if (key0 + kBlock <= L) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int key0 = t * KEYS + (j * kThreads + wave * kWave) / CPR;
-            blk[j] = key0 < L ? table[key0 / kBlock] : -1;
+            for (int k = 0; k < PER_BLK; ++k)
+                dma16_to_lds(dma_voff[k], sbase, dst0 + k * RPI * ROWB);
+            return PER_BLK;
         }
+        // the context's last block: rows past it are not loaded, and a load none of whose rows
+        // lies in the context is not issued (nor counted)
         int issued = 0;
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int first_row = (j * kThreads + wave * kWave) / CPR;  // wave-uniform
-            const int key0 = t * KEYS + first_row;
-            if (key0 >= L)
-                continue;
+        for (int k = 0; k < PER_BLK; ++k) {
+            if (key0 + k * RPI >= L)
+                break;
             ++issued;
-            if ((unsigned)blk[j] >= (unsigned)p.num_blocks)
-                continue;
-            const char *sbase = (const char *)cache + kvh_bytes + (size_t)blk[j] * blk_bytes;
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(
-                lds_address(buf + (j * kThreads + wave * kWave) * 16));
-            if (whole || key0 + lane_row < L)
-                dma16_to_lds(dma_voff, sbase, dst);
+            if (key0 + k * RPI + lane_row < L)
+                dma16_to_lds(dma_voff[k], sbase, dst0 + k * RPI * ROWB);
         }
         return issued;
     };
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             default: __builtin_amdgcn_s_waitcnt(0x78); break;
             }
         };
-        static_assert(4 * NLOAD <= 8, "wait_loads covers a K pair and a V pair");
+        static_assert(2 * PER_BLK <= 8, "wait_loads covers a K pair and a V pair");
 
         // LDS read addresses, computed per step from one lane base per cache (no per-slot
         // registers). K operand of k-step c, rows kt*32 + n: piece (2c + hh) ^ swz(n) of the row,
