@@ -73,8 +73,12 @@ __device__ __forceinline__ int unit_start(const DecodeParams &p, int seq, int L)
 }
 
 // F8: the caches hold E4M3 codes (one byte per element) instead of 16-bit elements.
+// Independent units (one wave each, no LDS, no barrier) per workgroup of the vector-ALU kernel:
+// fewer, larger workgroups keep more waves resident than one-wave workgroups.
+constexpr int kUnitWaves = 2;
+
 template <bool BF, bool F8, int D, int GK>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(DecodeParams p)
 {
     constexpr int EPL = F8 ? 16 : 8;     // cache elements per 16-byte piece = dims per lane
     constexpr int RL = D / EPL;          // lanes per token row
@@ -82,10 +86,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
     constexpr int NCH = kBlock / ROWS;   // loads per (block, kv head) tile
     constexpr int QV = EPL / 8;          // 16-byte query pieces per lane and head
     constexpr int ESZ = F8 ? 1 : 2;      // bytes per cache element
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int r = lane / RL;
 
-    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x) * kUnitWaves + (int)(threadIdx.x / kWave);
     if (unit >= p.n_units)
         return;
     const int seq = unit % p.num_seqs;
@@ -670,11 +674,17 @@ decode_prefix_mfma_kernel(DecodeParams p)
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// A part's accumulator is read as LPP lanes x 4 floats, so one load instruction covers PPI parts
+// (lane group g takes part j + g); U instructions are in flight per wave. The weights of 64 parts
+// at a time sit one per lane and are broadcast with readlane.
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
 {
-    constexpr int DPL = D / kWave;  // dims per lane
+    constexpr int LPP = D / 4;          // lanes per part
+    constexpr int PPI = kWave / LPP;    // parts per load instruction
+    constexpr int U = 8;                // load instructions in flight
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int grp = lane / LPP, sub = lane % LPP;
     const int idx = blockIdx.x * 4 + wave;
     if (idx >= p.num_seqs * p.num_q_heads)
         return;
@@ -687,7 +697,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     const int np = n_pre + n_own;
     auto slot_of = [&](int jj) { return jj < n_pre ? jj : p.pre_slots + (jj - n_pre); };
     const float *ml = p.ws_ml + (size_t)idx * p.ws_slots * 2;
-    const float *ac = p.ws_acc + (size_t)idx * p.ws_slots * D + lane * DPL;
+    const float *ac = p.ws_acc + (size_t)idx * p.ws_slots * D + sub * 4;
 
     float M = -INFINITY;
     for (int jj = lane; jj < np; jj += kWave)
@@ -698,23 +708,49 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
         W += fast_exp2(ml[2 * slot_of(jj)] - M) * ml[2 * slot_of(jj) + 1];
     W = wave_sum(W);
 
-    float o[DPL];
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < np; c0 += kWave) {
+        const int n = min(kWave, np - c0);
+        const float wl = lane < n ? fast_exp2(ml[2 * slot_of(c0 + lane)] - M) : 0.0f;
+        for (int k = 0; k < n; k += U * PPI) {
+            float4 a[U];
+            float wk[U];
 #pragma unroll
-    for (int d = 0; d < DPL; ++d)
-        o[d] = 0.0f;
-    for (int jj = 0; jj < np; ++jj) {
-        const int sl = slot_of(jj);
-        const float w = fast_exp2(ml[2 * sl] - M);
+            for (int u = 0; u < U; ++u) {
+                const int j0 = k + u * PPI;  // first part of instruction u (wave-uniform)
+                float wv = 0.0f;
 #pragma unroll
-        for (int d = 0; d < DPL; ++d)
-            o[d] += w * ac[(size_t)sl * D + d];
+                for (int g = 0; g < PPI; ++g) {
+                    const float x = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(wl), min(j0 + g, kWave - 1)));
+                    wv = grp == g ? x : wv;
+                }
+                const int j = j0 + grp;
+                wk[u] = j < n ? wv : 0.0f;
+                a[u] = j < n ? *(const float4 *)(ac + (size_t)slot_of(c0 + j) * D)
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                o[0] += wk[u] * a[u].x;
+                o[1] += wk[u] * a[u].y;
+                o[2] += wk[u] * a[u].z;
+                o[3] += wk[u] * a[u].w;
+            }
+        }
     }
-    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-    uint16_t *dst = p.out + (size_t)idx * D + lane * DPL;
-    if constexpr (DPL == 2)
-        *(uint32_t *)dst = pack2<BF>(o[0] * inv, o[1] * inv);
-    else
-        *dst = (uint16_t)to_word<BF>(o[0] * inv);
+#pragma unroll
+    for (int off = LPP; off < kWave; off <<= 1)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            o[d] += xor_shfl(o[d], off);
+    if (grp == 0) {
+        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+        uint2 w2;
+        w2.x = pack2<BF>(o[0] * inv, o[1] * inv);
+        w2.y = pack2<BF>(o[2] * inv, o[3] * inv);
+        *(uint2 *)(p.out + (size_t)idx * D + sub * 4) = w2;
+    }
 }
 
 template <bool BF, bool F8, int D, int GK>
@@ -724,8 +760,9 @@ hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
     if constexpr (GK == kCols)
         hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D>), dim3(grid), dim3(kWave), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>), dim3(grid), dim3(kWave), 0,
-                           stream, p);
+        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>),
+                           dim3(round_up8((p.n_units + kUnitWaves - 1) / kUnitWaves)),
+                           dim3(kWave * kUnitWaves), 0, stream, p);
     return hipGetLastError();
 }
 
