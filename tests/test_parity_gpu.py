@@ -234,6 +234,23 @@ def test_prefill_long_chunk_gqa_full():
                            "prefill long chunk", strict=False)
 
 
+@pytest.mark.parametrize("H_q,H_kv,D,dtype", [(8, 8, 128, "f16"), (16, 8, 128, "bf16"),
+                                               (12, 4, 64, "bf16"), (32, 4, 128, "f16"),
+                                               (16, 2, 64, "f16"), (24, 3, 128, "bf16")])
+def test_prefill_pipelined_rows_full(H_q, H_kv, D, dtype):
+    """Chunks whose every row attends at least 512 keys (the software-pipelined loop): ragged row
+    tiles, chunks starting mid-block and mid-tile, an odd and an even number of 64-key tiles, and
+    several diagonal (masked) tiles per workgroup; every row compared in full."""
+    lens = [1500, 900, 777, 2049]
+    q_lens = [300, 257, 129, 64]     # first rows at positions 1200, 643, 648, 1985
+    w = poisoned(W.build(lens, H_q, H_kv, D, dtype, seed=130 + H_q + D, n_decode=0,
+                         q_lens=q_lens))
+    g = run_on_gpu(w, stages=("scatter", "prefill"))
+    kc, vc = oracle_pool_after_step(w)
+    assert_attention_close(words_from_device(g.pre_out), oracle_prefill(w, kc, vc), dtype,
+                           f"pipelined prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}")
+
+
 def test_prefill_single_row_chunks_match_decode():
     """A chunk of one row is a decode step: both kernels agree within the gate of each."""
     lens = [5, 600, 1500]
