@@ -209,8 +209,7 @@ pa_status_t pa_reshape_and_cache_fp8(pa_dtype_t dtype, int32_t num_blocks, int32
 /*
  * pa_decode_fp8 -- pa_decode over E4M3 caches ([V1] §4.4): keys and values are read as code value
  * times k_scale / v_scale, everything else as in pa_decode (query and out of `dtype`, the same
- * workspace size function, partition_size rules and errors). Head groups of any size run; there is
- * no shared-prefix variant for E4M3 caches.
+ * workspace size function, partition_size rules and errors). Head groups of any size run.
  */
 pa_status_t pa_decode_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
                           int32_t head_dim, void *out, const void *query, const void *k_cache,
@@ -219,6 +218,25 @@ pa_status_t pa_decode_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_h
                           int32_t max_seq_len, int32_t num_q_heads, float scale, float k_scale,
                           float v_scale, int32_t partition_size, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_shared_prefix_fp8 -- pa_decode_shared_prefix over E4M3 caches ([V1] §4.4 with §2.2):
+ * keys and values are read as code value times k_scale / v_scale; groups, prefix lengths, the
+ * workspace size function (pa_decode_shared_prefix_workspace_size), partition_size rules and
+ * errors are those of pa_decode_shared_prefix. out equals pa_decode_fp8's result for the same
+ * sequences: the shared blocks are read once per group instead of once per member.
+ */
+pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
+                                        int32_t num_kv_heads, int32_t head_dim, void *out,
+                                        const void *query, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                                        int32_t num_seqs, int32_t max_seq_len,
+                                        const int32_t *group_starts, const int32_t *prefix_lens,
+                                        int32_t num_groups, int32_t max_group_size,
+                                        int32_t max_prefix_len, int32_t num_q_heads, float scale,
+                                        float k_scale, float v_scale, int32_t partition_size,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *pa_status_string(pa_status_t status);

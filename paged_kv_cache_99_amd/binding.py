@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_shared_prefix.restype = _i
         L.pa_decode_shared_prefix.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i,
                                               _p, _p, _i, _i, _i, _i, _f, _i, _p, _sz, _p]
+        L.pa_decode_shared_prefix_fp8.restype = _i
+        L.pa_decode_shared_prefix_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i,
+                                                  _i, _p, _p, _i, _i, _i, _i, _f, _f, _f, _i, _p,
+                                                  _sz, _p]
         L.pa_reshape_and_cache_fp8.restype = _i
         L.pa_reshape_and_cache_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _f, _f, _p]
         L.pa_decode_fp8.restype = _i
@@ -198,16 +202,18 @@ def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim, max_seq
                                                             partition_size))
 
 
-def decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
-                         group_starts, prefix_lens, max_group_size: int, max_prefix_len: int,
-                         scale: float, partition_size: int = 512,
-                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """pa_decode_shared_prefix: pa_decode whose groups of sequences (group_starts [G+1], int32)
-    read their common leading blocks (prefix_lens [B], int32) once."""
-    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+def _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
+                        group_starts, prefix_lens, max_group_size, max_prefix_len,
+                        partition_size, workspace, fp8):
+    """Checked arguments of pa_decode_shared_prefix{,_fp8} up to num_q_heads, and the workspace
+    (pointer, bytes)."""
+    _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=fp8)
+    dt = _act_dtype(query, "query")
+    if not fp8 and query.dtype != k_cache.dtype:
+        raise ValueError("query dtype differs from the caches'")
     B, hq = int(query.shape[0]), int(query.shape[1])
     for t, n in ((query, "query"), (out, "out")):
-        _gpu(t, n, k_cache.dtype)
+        _gpu(t, n, query.dtype)
         if tuple(t.shape) != (B, hq, d):
             raise ValueError(f"{n} must be [{B}, {hq}, {d}]")
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
@@ -222,13 +228,39 @@ def decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, m
                                                partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode_shared_prefix(
-        dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), int(block_tables.shape[1]), seq_lens.data_ptr(), B,
-        int(max_seq_len), group_starts.data_ptr(), prefix_lens.data_ptr(), max(G, 0),
-        int(max_group_size), int(max_prefix_len), hq, float(scale), int(partition_size),
-        workspace.data_ptr(), ws_bytes, _stream(stream)))
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    args = (dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
+            seq_lens.data_ptr(), B, int(max_seq_len), group_starts.data_ptr(),
+            prefix_lens.data_ptr(), max(G, 0), int(max_group_size), int(max_prefix_len), hq)
+    return args, ws
+
+
+def decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+                         group_starts, prefix_lens, max_group_size: int, max_prefix_len: int,
+                         scale: float, partition_size: int = 512,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode_shared_prefix: pa_decode whose groups of sequences (group_starts [G+1], int32)
+    read their common leading blocks (prefix_lens [B], int32) once."""
+    args, ws = _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens,
+                                   max_seq_len, group_starts, prefix_lens, max_group_size,
+                                   max_prefix_len, partition_size, workspace, False)
+    _check(lib().pa_decode_shared_prefix(*args, float(scale), int(partition_size), *ws,
+                                         _stream(stream)))
+
+
+def decode_shared_prefix_fp8(out, query, k_cache, v_cache, block_tables, seq_lens,
+                             max_seq_len: int, group_starts, prefix_lens, max_group_size: int,
+                             max_prefix_len: int, scale: float, k_scale: float, v_scale: float,
+                             partition_size: int = 512, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """pa_decode_shared_prefix_fp8: decode_shared_prefix over E4M3 caches (uint8 or
+    float8_e4m3fn; elements = code value * k_scale / v_scale)."""
+    args, ws = _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens,
+                                   max_seq_len, group_starts, prefix_lens, max_group_size,
+                                   max_prefix_len, partition_size, workspace, True)
+    _check(lib().pa_decode_shared_prefix_fp8(*args, float(scale), float(k_scale), float(v_scale),
+                                             int(partition_size), *ws, _stream(stream)))
 
 
 def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,

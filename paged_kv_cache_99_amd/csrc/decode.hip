@@ -641,7 +641,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
 // blocks of positions [0, seq_starts[first member]), read here once through the first member's
 // table for all of them (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are
 // stored once). Pair v of the group is member v / G, query head kvh*G + v % G.
-template <bool BF, int D>
+template <bool BF, bool F8, int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_prefix_mfma_kernel(DecodeParams p)
 {
@@ -668,8 +668,8 @@ decode_prefix_mfma_kernel(DecodeParams p)
     const int t1 = min(prefix, t0 + p.part_tokens);
     const int v = vsub * kCols + (threadIdx.x & 15);
     const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
-    mfma_unit<BF, false, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1,
-                            part, true);
+    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1,
+                         part, true);
 }
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
@@ -771,13 +771,11 @@ template <bool BF, bool F8, int D>
 hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hipStream_t stream)
 {
     hipError_t e;
-    if constexpr (!F8) {  // shared-prefix units exist for 16-bit caches only
-        if (pre) {
-            hipLaunchKernelGGL((decode_prefix_mfma_kernel<BF, D>), dim3(round_up8(pre->n_units)),
-                               dim3(kWave), 0, stream, *pre);
-            if ((e = hipGetLastError()) != hipSuccess)
-                return e;
-        }
+    if (pre) {
+        hipLaunchKernelGGL((decode_prefix_mfma_kernel<BF, F8, D>), dim3(round_up8(pre->n_units)),
+                           dim3(kWave), 0, stream, *pre);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
     }
     e = gk == kCols ? launch_units<BF, F8, D, kCols>(p, stream)
         : gk == 2   ? launch_units<BF, F8, D, 2>(p, stream)
@@ -805,8 +803,6 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     // query heads per unit on MFMA
     const int gk = group <= 2 ? group : kCols;
     const bool cascade = d.group_starts != nullptr && d.num_groups > 0;
-    if (d.fp8 && cascade)
-        return hipErrorInvalidValue;  // no shared-prefix kernel for E4M3 caches
     DecodeParams p = {};
     p.query = (const uint16_t *)d.query;
     p.k_cache = (const uint16_t *)d.k_cache;

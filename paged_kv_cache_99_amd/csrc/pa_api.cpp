@@ -312,16 +312,20 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_he
     return (size_t)num_seqs * num_q_heads * (size_t)(pre + own) * (head_dim + 2) * sizeof(float);
 }
 
-pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
-                                    int32_t head_dim, void *out, const void *query,
-                                    const void *k_cache, const void *v_cache,
-                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                    const int32_t *seq_lens, int32_t num_seqs,
-                                    int32_t max_seq_len, const int32_t *group_starts,
-                                    const int32_t *prefix_lens, int32_t num_groups,
-                                    int32_t max_group_size, int32_t max_prefix_len,
-                                    int32_t num_q_heads, float scale, int32_t partition_size,
-                                    void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+pa_status_t shared_prefix_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                               int32_t head_dim, void *out, const void *query,
+                               const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                               const int32_t *group_starts, const int32_t *prefix_lens,
+                               int32_t num_groups, int32_t max_group_size,
+                               int32_t max_prefix_len, int32_t num_q_heads, float scale,
+                               int32_t partition_size, void *workspace, size_t workspace_bytes,
+                               void *stream, bool fp8, float k_scale, float v_scale)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -344,6 +348,10 @@ pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_
             max_group_size);
     REQUIRE(max_prefix_len >= 0 && max_prefix_len <= max_seq_len,
             "max_prefix_len %d is outside [0, max_seq_len]", max_prefix_len);
+    if (fp8)
+        REQUIRE(good_scale(k_scale) && good_scale(v_scale),
+                "k_scale %g / v_scale %g is not a finite positive number", (double)k_scale,
+                (double)v_scale);
     if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
                     num_q_heads / num_kv_heads);
@@ -364,8 +372,6 @@ pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
     REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
     const int32_t own = max_seq_len > 0 ? (max_seq_len + partition_size - 1) / partition_size : 1;
-    const int32_t pre = (max_prefix_len + partition_size - 1) / partition_size;
-    (void)pre;
     pa::DecodeLaunch d;
     d.c = c;
     d.out = out;
@@ -395,7 +401,53 @@ pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_
     const int32_t slots = (d.max_prefix_len + partition_size - 1) / partition_size + own;
     d.ws_acc = (float *)workspace;
     d.ws_ml = (float *)workspace + (size_t)num_seqs * num_q_heads * slots * head_dim;
-    return launched(pa::launch_decode(d, (hipStream_t)stream), "decode_shared_prefix");
+    d.fp8 = fp8;
+    d.c.fp8 = fp8;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    return launched(pa::launch_decode(d, (hipStream_t)stream),
+                    fp8 ? "decode_shared_prefix_fp8" : "decode_shared_prefix");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, void *out, const void *query,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens, int32_t num_seqs,
+                                    int32_t max_seq_len, const int32_t *group_starts,
+                                    const int32_t *prefix_lens, int32_t num_groups,
+                                    int32_t max_group_size, int32_t max_prefix_len,
+                                    int32_t num_q_heads, float scale, int32_t partition_size,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return shared_prefix_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache,
+                              v_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                              max_seq_len, group_starts, prefix_lens, num_groups, max_group_size,
+                              max_prefix_len, num_q_heads, scale, partition_size, workspace,
+                              workspace_bytes, stream, false, 1.0f, 1.0f);
+}
+
+pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
+                                        int32_t num_kv_heads, int32_t head_dim, void *out,
+                                        const void *query, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                                        int32_t num_seqs, int32_t max_seq_len,
+                                        const int32_t *group_starts, const int32_t *prefix_lens,
+                                        int32_t num_groups, int32_t max_group_size,
+                                        int32_t max_prefix_len, int32_t num_q_heads, float scale,
+                                        float k_scale, float v_scale, int32_t partition_size,
+                                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return shared_prefix_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache,
+                              v_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                              max_seq_len, group_starts, prefix_lens, num_groups, max_group_size,
+                              max_prefix_len, num_q_heads, scale, partition_size, workspace,
+                              workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,

@@ -44,7 +44,7 @@ class GpuStep:
     kv_cache="fp8" keeps the caches as E4M3 codes (lecture 34 §4.4) with scales k_scale, v_scale:
     fp8_pool gives their initial bytes (numpy uint8, the pool layout); without it the 16-bit pool is
     quantized on the device by the library's own FP8 scatter, each slot being one token. Such a
-    step runs copy, scatter and decode; it has no shared-prefix or prefill stage.
+    step runs copy, scatter and decode (plain or shared-prefix); it has no prefill stage.
     """
 
     def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
@@ -60,8 +60,6 @@ class GpuStep:
         self.new_value = words_to_device(w.new_value, dt, dev)
         self.slot_mapping = ints_to_device(w.slot_mapping, dev)
         if self.fp8:
-            if shared_prefix:
-                raise ValueError("no shared-prefix decode for E4M3 caches")
             if fp8_pool is not None:
                 self.k_cache = torch.from_numpy(np.ascontiguousarray(fp8_pool[0], np.uint8)).to(
                     dev).view(shape)
@@ -139,7 +137,13 @@ class GpuStep:
                                       self.slot_mapping, stream)
 
     def decode(self, stream=None):
-        if self.n_decode and self.fp8:
+        if self.n_decode and self.fp8 and self.shared_prefix:
+            binding.decode_shared_prefix_fp8(
+                self.dec_out, self.dec_query, self.k_cache, self.v_cache, self.dec_tables,
+                self.dec_lens, self.max_seq_len, self.group_starts, self.prefix_lens,
+                self.max_group_size, self.max_prefix_len, self.w.scale, self.k_scale,
+                self.v_scale, self.partition_size, self.workspace, stream)
+        elif self.n_decode and self.fp8:
             binding.decode_fp8(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
                                self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,
                                self.k_scale, self.v_scale, self.partition_size, self.workspace,

@@ -144,3 +144,74 @@ def test_decode_is_deterministic():
     g.decode()
     torch.cuda.synchronize()
     assert np.array_equal(first, words_from_device(g.dec_out))
+
+
+# ------------------------------------------------------------- read-once shared prefixes, E4M3
+def run_fp8_shared_prefix(w, ks, vs, partition_size=None):
+    kc, vc = oracle_fp8_pool(w, ks, vs)
+    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(kc, vc),
+                partition_size=partition_size, shared_prefix=True)
+    assert g.shared_prefix
+    print(f"[fp8] shared-prefix decode {w.name}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} "
+          f"partition={g.partition_size} groups={len(g.group_starts) - 1} "
+          f"max_group={g.max_group_size}", flush=True)
+    g.copy()
+    g.scatter()
+    g.decode()
+    torch.cuda.synchronize()
+    kc, vc = oracle_fp8_after_step(w, kc, vc, ks, vs)
+    nd = w.n_decode
+    ref = oracle.decode_fp8(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
+                            w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+    return g, ref
+
+
+def test_shared_prefix_decode_named():
+    """Parallel samples of the 2040-token prompt: 8 members per group read it once, E4M3."""
+    w = W.named("prefix_sharing_2040")
+    g, ref = run_fp8_shared_prefix(w, 0.03, 0.02)
+    assert g.max_group_size == 8
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype,
+                           "fp8 shared-prefix decode prefix_sharing_2040")
+
+
+FP8_SHARED_GROUPS = [
+    (40, [41, 60, 100]),                                        # prompt ends mid-block: CoW
+    (1000, [1001, 1016, 1017, 1500, 2000, 1050, 1100, 1333]),   # 8 members
+    (0, [5, 9]),                                                # nothing shared
+    (16, [17]),                                                 # a group of one
+    (640, [641 + 37 * i for i in range(20)]),                   # 20 members: several subgroups
+]
+
+
+@pytest.mark.parametrize("H_q,H_kv,D,dtype", [(4, 4, 128, "f16"), (8, 2, 128, "bf16"),
+                                              (16, 4, 64, "f16"), (6, 2, 128, "bf16"),
+                                              (2, 2, 64, "bf16")])
+@pytest.mark.parametrize("part,ks,vs", [(16, 0.05, 0.015), (512, 2.0 ** -5, 0.3)])
+def test_shared_prefix_decode_groups(H_q, H_kv, D, dtype, part, ks, vs):
+    w = W.build_shared_groups(FP8_SHARED_GROUPS, H_q, H_kv, D, dtype, seed=640 + H_q + D,
+                              independent=[1, 33, 700])
+    g, ref = run_fp8_shared_prefix(w, ks, vs, partition_size=part)
+    assert_attention_close(words_from_device(g.dec_out), ref, dtype,
+                           f"fp8 shared-prefix decode H_q={H_q} H_kv={H_kv} D={D} {dtype} "
+                           f"part={part}", strict=False)
+
+
+def test_shared_prefix_decode_is_deterministic_and_matches_plain():
+    """Bitwise reproducible; and within the gate of the plain E4M3 decode of the same sequences
+    (which reads the shared blocks once per member)."""
+    w = W.build_shared_groups(FP8_SHARED_GROUPS, 32, 8, 128, "bf16", seed=650)
+    g, ref = run_fp8_shared_prefix(w, 0.03, 0.02, partition_size=256)
+    first = words_from_device(g.dec_out)
+    g.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(first, words_from_device(g.dec_out))
+    plain = torch.empty_like(g.dec_out)
+    binding.decode_fp8(plain, g.dec_query, g.k_cache, g.v_cache, g.dec_tables, g.dec_lens,
+                       g.max_seq_len, w.scale, 0.03, 0.02, 256)
+    torch.cuda.synchronize()
+    # contexts of 5 to 17 tokens give outputs near 1: the elementwise gate (bf16 rounding there
+    # alone is up to 3.9e-3)
+    assert_attention_close(words_from_device(plain), ref, w.dtype, "fp8 plain decode",
+                           strict=False)
+    assert_attention_close(first, ref, w.dtype, "fp8 shared-prefix decode", strict=False)
