@@ -61,6 +61,9 @@ struct DecodeParams {
     const int32_t *__restrict__ group_starts; // [num_groups + 1] members of prefix group g
     int32_t num_groups;
     int32_t ws_slots;     // partial-result slots per (sequence, head) row of the workspace
+    int32_t ws_rows;      // (sequence, head) rows: num_seqs * num_q_heads
+    int32_t wg_parts;     // MFMA kernel: parts merged per workgroup (1 or kMfmaWaves)
+    int32_t slot_tokens;  // tokens of a row's own workspace slot: part_tokens * wg_parts
     int32_t slot_base;    // first slot these units write
     int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix parts (merge)
     int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
             const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
             if (p.split) {
                 const size_t slot = row * p.ws_slots + p.slot_base + part;
-                float *wa = p.ws_acc + slot * D + lane * EPL;
+                float *wa = p.ws_acc + ((size_t)(p.slot_base + part) * p.ws_rows + row) * D +
+                            lane * EPL;
 #pragma unroll
                 for (int j = 0; j < EPL; j += 4)
                     *(float4 *)(wa + j) =
@@ -348,9 +352,28 @@ __device__ __forceinline__ int vswz(int r)
     return D == 128 ? (r & 15) : (r & 7);
 }
 
+// Bytes of LDS one MFMA unit stages V through: two blocks of 16 rows of D 16-bit elements.
+template <int D>
+constexpr int kUnitLds = 2 * kBlock * D * 2;
+
+// Orders this wave's LDS accesses on either side of it for the compiler. The LDS unit performs one
+// wave's accesses in program order, so lanes reading what other lanes of the same wave wrote need
+// no s_barrier: the V staging below is private to its wave.
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Attention of the query rows in one wave's 16 MFMA columns over tokens [t0, t1) of kv head kvh.
+// On return o holds the unnormalised accumulator (lane (j, g): column j, dims 16t + 4g .. +3 of
+// tile t), m the running maximum of column j (log2 domain) and l this lane's share of column j's
+// running sum (the four row groups g add up to it). v_lds is the wave's own staging area
+// (kUnitLds<D> bytes). An empty range leaves o = 0, m = -inf, l = 0.
 template <bool BF, bool F8, int D>
 __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const int32_t *table,
-                                          int kvh, int t0, int t1, int slot, bool split)
+                                          int kvh, int t0, int t1, uint8_t *v_lds,
+                                          f32x4 (&o)[D / 16], float &m, float &l)
 {
     constexpr int NC = D / 32;              // QK k-chunks
     constexpr int NT = D / 16;              // PV output tiles
@@ -359,9 +382,8 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
     constexpr int NV = TILE / 1024;         // 1 KiB V loads per block
     constexpr int KL = F8 ? NC / 2 : NC;    // 16-byte K loads per lane per block
     constexpr int ROWB = D * 2;             // bytes of a 16-bit V row in LDS
-    __shared__ __align__(16) uint8_t v_lds[2 * kBlock * ROWB];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int j = lane & 15, g = lane >> 4;
 
     uint4 q[NC];
@@ -370,11 +392,11 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
         q[c] = qrow >= 0 ? *(const uint4 *)(p.query + (size_t)qrow * D + qk_dim<F8>(c, g))
                          : make_uint4(0, 0, 0, 0);
 
-    f32x4 o[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -INFINITY, l = 0.0f;
+    m = -INFINITY;
+    l = 0.0f;
 
     const uint8_t *kbase = (const uint8_t *)p.k_cache + (size_t)kvh * TILE;
     const uint8_t *vbase = (const uint8_t *)p.v_cache + (size_t)kvh * TILE;
@@ -570,11 +592,11 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
         load_v(0, va);
         for (int st = 0; st < nsteps; ++st) {
             const bool whole = whole_step(st);
-            __syncthreads();  // the previous step's transposed reads are done
+            wave_lds_fence();  // after the previous step's transposed reads
             stage(st, whole, va);
             if (st + 1 < nsteps)
                 load_v(st + 1, va);
-            __syncthreads();
+            wave_lds_fence();
             float sv[8];
             scores(st, whole, ka, sv);
             if (st + 1 < nsteps)
@@ -583,57 +605,146 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
         }
     }
 
-    l += xor_shfl(l, 16);
-    l += xor_shfl(l, 32);
-    if (qrow < 0)
-        return;
-    const float vs = F8 ? p.v_scale : 1.0f;
-    if (split) {
-        const size_t sl = (size_t)qrow * p.ws_slots + slot;
-        float *wa = p.ws_acc + sl * D + 4 * g;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *(float4 *)(wa + 16 * t) = make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs,
-                                                   o[t][3] * vs);
-        if (g == 0)
-            *(float2 *)(p.ws_ml + sl * 2) = make_float2(m, l);
-    } else {
-        const float inv = l > 0.0f ? vs / l : 0.0f;
-        uint16_t *dst = p.out + (size_t)qrow * D + 4 * g;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *(uint2 *)(dst + 16 * t) =
-                make_uint2(pack2<BF>(o[t][0] * inv, o[t][1] * inv),
-                           pack2<BF>(o[t][2] * inv, o[t][3] * inv));
-    }
 }
 
-// Plain decode of head groups of 3 or more: (sequence, kv head, subgroup of 16 query heads, part).
-// Three waves per SIMD (at most 168 registers): the unit holds one step of K and V operands in
-// flight, so the number of resident waves sets the bytes in flight per CU.
-template <bool BF, bool F8, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
-    DecodeParams p)
+// Column sums of the four row groups' running sums (every lane of column j gets column j's).
+__device__ __forceinline__ float column_sum(float l)
 {
-    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
-    if (unit >= p.n_units)
+    l += xor_shfl(l, 16);
+    return l + xor_shfl(l, 32);
+}
+
+// Partial result of query row qrow into workspace slot `slot`: the accumulator times v_scale, the
+// maximum m and the column sum lsum.
+template <bool F8, int D>
+__device__ __forceinline__ void mfma_write_partial(const DecodeParams &p, int qrow, int slot,
+                                                   const f32x4 (&o)[D / 16], float m, float lsum)
+{
+    if (qrow < 0)
         return;
+    const int g = (threadIdx.x & (kWave - 1)) >> 4;
+    const float vs = F8 ? p.v_scale : 1.0f;
+    float *wa = p.ws_acc + ((size_t)slot * p.ws_rows + qrow) * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        *(float4 *)(wa + 16 * t) = make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs,
+                                               o[t][3] * vs);
+    if (g == 0)
+        *(float2 *)(p.ws_ml + ((size_t)qrow * p.ws_slots + slot) * 2) = make_float2(m, lsum);
+}
+
+// Normalised output of query row qrow (a range that is the whole context).
+template <bool BF, bool F8, int D>
+__device__ __forceinline__ void mfma_write_output(const DecodeParams &p, int qrow,
+                                                  const f32x4 (&o)[D / 16], float lsum)
+{
+    if (qrow < 0)
+        return;
+    const int g = (threadIdx.x & (kWave - 1)) >> 4;
+    const float inv = lsum > 0.0f ? (F8 ? p.v_scale : 1.0f) / lsum : 0.0f;
+    uint16_t *dst = p.out + (size_t)qrow * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        *(uint2 *)(dst + 16 * t) = make_uint2(pack2<BF>(o[t][0] * inv, o[t][1] * inv),
+                                              pack2<BF>(o[t][2] * inv, o[t][3] * inv));
+}
+
+// Plain decode of head groups of 3 or more. A workgroup is kMfmaWaves waves, at most three per SIMD
+// (at most 168 registers): each unit holds one step of K and V operands in flight, so the number
+// of resident waves sets the bytes in flight per CU.
+//  * Split (p.wg_parts == kMfmaWaves): workgroup (sequence, slot q, subgroup of 16 query heads,
+//    kv head); wave w computes part kMfmaWaves*q + w on its own, then the workgroup merges its
+//    parts through LDS by rescaling to their common maximum (the same log-sum-exp merge as the
+//    merge kernel's) and writes one partial result per row to slot q. Every part's partial would
+//    otherwise be an fp32 write of D floats per query head, and at G = 8 those writes cost several
+//    times their share of the HBM traffic.
+//  * Otherwise (p.wg_parts == 1): the waves are independent units (sequence, part, subgroup, kv
+//    head) that write their own partial result, or the output when the decode is not split.
+constexpr int kMfmaWaves = 4;
+
+template <bool BF, bool F8, int D>
+__global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3))) void
+decode_mfma_kernel(DecodeParams p)
+{
+    constexpr int NT = D / 16;
+    __shared__ __align__(16) uint8_t lds[kMfmaWaves * kUnitLds<D>];  // V staging; then the merge
+    __shared__ float2 ml_lds[kMfmaWaves][kWave];
+    static_assert(kMfmaWaves * NT * kWave * 16 <= kMfmaWaves * kUnitLds<D>, "merge buffer");
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const bool merged = p.wg_parts == kMfmaWaves;
+    const int unit = merged ? wg : wg * kMfmaWaves + w;
+    if (unit >= p.n_units)
+        return;  // uniform over the workgroup in the merged mode
     const int seq = unit % p.num_seqs;
     int rest = unit / p.num_seqs;
-    const int part = rest % p.max_parts;
-    rest /= p.max_parts;
+    const int n_slot = merged ? p.ws_slots - p.slot_base : p.max_parts;  // slots (parts) per row
+    const int q = rest % n_slot;
+    rest /= n_slot;
     const int sub = rest % p.n_sub;
     const int kvh = rest / p.n_sub;
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
-    const int t0 = unit_start(p, seq, L) + part * p.part_tokens;
-    if (p.split && t0 >= L)
-        return;
+    const int start = unit_start(p, seq, L);
+    const int part = merged ? q * kMfmaWaves + w : q;
+    if (p.split && start + q * p.slot_tokens >= L)
+        return;  // the slot holds no tokens (uniform over the workgroup in the merged mode)
+    const int t0 = min(L, start + part * p.part_tokens);
     const int t1 = min(L, t0 + p.part_tokens);
     const int G = p.num_q_heads / p.num_kv_heads;
-    const int h = sub * kCols + (threadIdx.x & 15);
+    const int h = sub * kCols + (lane & 15);
     const int qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
+    f32x4 o[NT];
+    float m, l;
     mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
-                         p.slot_base + part, p.split != 0);
+                         lds + w * kUnitLds<D>, o, m, l);
+    const float lsum = column_sum(l);
+    if (!p.split) {
+        mfma_write_output<BF, F8, D>(p, qrow, o, lsum);
+        return;
+    }
+    if (!merged) {
+        mfma_write_partial<F8, D>(p, qrow, p.slot_base + part, o, m, lsum);
+        return;
+    }
+    // merge the workgroup's parts: wave w combines output tiles [w*NT/W, (w+1)*NT/W) of all parts
+    __syncthreads();  // every wave is done with its V staging
+    f32x4 *ox = (f32x4 *)lds;  // [wave][tile][lane]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        ox[(w * NT + t) * kWave + lane] = o[t];
+    ml_lds[w][lane] = make_float2(m, lsum);
+    __syncthreads();
+    float2 mls[kMfmaWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kMfmaWaves; ++v) {
+        mls[v] = ml_lds[v][lane];
+        M = fmaxf(M, mls[v].x);
+    }
+    float a[kMfmaWaves], L2 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kMfmaWaves; ++v) {
+        a[v] = mls[v].x == -INFINITY ? 0.0f : fast_exp2(mls[v].x - M);
+        L2 += a[v] * mls[v].y;
+    }
+    if (qrow < 0)
+        return;
+    const int g = lane >> 4;
+    const float vs = F8 ? p.v_scale : 1.0f;
+    const int slot = p.slot_base + q;
+    float *wa = p.ws_acc + ((size_t)slot * p.ws_rows + qrow) * D + 4 * g;
+    constexpr int TPW = NT / kMfmaWaves;  // tiles per wave
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int t = w * TPW + tt;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < kMfmaWaves; ++v)
+            acc += a[v] * ox[(v * NT + t) * kWave + lane];
+        *(float4 *)(wa + 16 * t) = make_float4(acc[0] * vs, acc[1] * vs, acc[2] * vs, acc[3] * vs);
+    }
+    if (w == 0 && g == 0)
+        *(float2 *)(p.ws_ml + ((size_t)qrow * p.ws_slots + slot) * 2) = make_float2(M, L2);
 }
 
 // Shared-prefix unit: (prefix group g, kv head, subgroup of 16 (member, query head) pairs, part).
@@ -668,8 +779,12 @@ decode_prefix_mfma_kernel(DecodeParams p)
     const int t1 = min(prefix, t0 + p.part_tokens);
     const int v = vsub * kCols + (threadIdx.x & 15);
     const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
-    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1,
-                         part, true);
+    __shared__ __align__(16) uint8_t v_lds[kUnitLds<D>];
+    f32x4 o[D / 16];
+    float m, l;
+    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1, v_lds,
+                         o, m, l);
+    mfma_write_partial<F8, D>(p, qrow, part, o, m, column_sum(l));
 }
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
@@ -693,11 +808,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     const int start = unit_start(p, seq, L);
     // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots
     const int n_pre = p.pre_slots > 0 ? (start + p.part_tokens - 1) / p.part_tokens : 0;
-    const int n_own = (L - start + p.part_tokens - 1) / p.part_tokens;
+    const int n_own = (L - start + p.slot_tokens - 1) / p.slot_tokens;
     const int np = n_pre + n_own;
     auto slot_of = [&](int jj) { return jj < n_pre ? jj : p.pre_slots + (jj - n_pre); };
     const float *ml = p.ws_ml + (size_t)idx * p.ws_slots * 2;
-    const float *ac = p.ws_acc + (size_t)idx * p.ws_slots * D + sub * 4;
+    const float *ac = p.ws_acc + (size_t)idx * D + sub * 4;  // + slot * ws_rows * D
 
     float M = -INFINITY;
     for (int jj = lane; jj < np; jj += kWave)
@@ -727,7 +842,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
                 }
                 const int j = j0 + grp;
                 wk[u] = j < n ? wv : 0.0f;
-                a[u] = j < n ? *(const float4 *)(ac + (size_t)slot_of(c0 + j) * D)
+                a[u] = j < n ? *(const float4 *)(ac + (size_t)slot_of(c0 + j) * p.ws_rows * D)
                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
 #pragma unroll
@@ -756,9 +871,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
 template <bool BF, bool F8, int D, int GK>
 hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
 {
-    const int grid = round_up8(p.n_units);
     if constexpr (GK == kCols)
-        hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D>), dim3(grid), dim3(kWave), 0, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D>),
+                           dim3(round_up8(p.wg_parts == kMfmaWaves
+                                              ? p.n_units
+                                              : (p.n_units + kMfmaWaves - 1) / kMfmaWaves)),
+                           dim3(kWave * kMfmaWaves), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>),
                            dim3(round_up8((p.n_units + kUnitWaves - 1) / kUnitWaves)),
@@ -826,7 +944,12 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (p.part_tokens < kBlock)
         p.part_tokens = kBlock;
     p.max_parts = p.split ? d.max_parts : 1;
-    p.ws_slots = p.max_parts;
+    // split MFMA decode: kMfmaWaves consecutive parts per workgroup, merged into one slot
+    p.wg_parts = gk == kCols && p.split ? kMfmaWaves : 1;
+    p.slot_tokens = p.part_tokens * p.wg_parts;
+    const int own_slots = (p.max_parts + p.wg_parts - 1) / p.wg_parts;
+    p.ws_slots = own_slots;
+    p.ws_rows = d.num_seqs * d.num_q_heads;
 
     DecodeParams pre;
     if (cascade) {
@@ -835,7 +958,7 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
         p.seq_starts = d.seq_starts;
         p.pre_slots = pre_parts;
         p.slot_base = pre_parts;
-        p.ws_slots = pre_parts + p.max_parts;
+        p.ws_slots = pre_parts + own_slots;
         pre = p;
         pre.group_starts = d.group_starts;
         pre.num_groups = d.num_groups;
@@ -847,7 +970,9 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
             return hipErrorInvalidValue;
         pre.n_units = (int32_t)pre_units;
     }
-    const int64_t units = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.max_parts;
+    // units: workgroups of merged parts, else waves
+    const int64_t units = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub *
+                          (p.wg_parts == kMfmaWaves ? own_slots : p.max_parts);
     if (units > 0x7ffffff0)
         return hipErrorInvalidValue;
     p.n_units = (int32_t)units;
