@@ -49,18 +49,19 @@ def decode_bytes(w, esize=2):
     return kv + 2 * nd * w.H_q * w.D * 2
 
 
-def decode_unique_bytes(w):
-    """Bytes when every group's common blocks are read once (shared-prefix workloads)."""
+def decode_unique_bytes(w, esize=2):
+    """Bytes when every group's common blocks are read once (shared-prefix workloads); esize:
+    bytes per cached K/V element (2, or 1 for E4M3 caches)."""
     meta = getattr(w, "meta", {}) or {}
     if "group_starts" not in meta:
-        return decode_bytes(w)
+        return decode_bytes(w, esize)
     nd = w.n_decode
     gs = np.asarray(meta["group_starts"])
     pre = np.asarray(meta["shared_prefix"], np.int64)[:nd]
     lens = w.seq_lens[:nd].astype(np.int64)
     shared = int(sum(pre[gs[g]] for g in range(len(gs) - 1) if gs[g + 1] > gs[g]))
     tokens = shared + int(np.sum(lens - pre))
-    return tokens * 2 * w.H_kv * w.D * 2 + 2 * nd * w.H_q * w.D * 2
+    return tokens * 2 * w.H_kv * w.D * esize + 2 * nd * w.H_q * w.D * 2
 
 
 def scatter_bytes(w, esize=2):
@@ -214,7 +215,7 @@ def main():
         sys.exit(2)
     esize = 1 if fp8 else 2
     g = GpuStep(w, partition_size=args.partition,
-                shared_prefix=not args.no_shared_prefix and not fp8,
+                shared_prefix=not args.no_shared_prefix,
                 kv_cache=args.kv_cache, k_scale=args.k_scale, v_scale=args.v_scale)
     stream = torch.cuda.current_stream()
 
@@ -250,7 +251,7 @@ def main():
         calibration_copy(g, args.copy_calibration)
 
     d_bytes = decode_bytes(w, esize)
-    u_bytes = decode_unique_bytes(w) if g.shared_prefix else d_bytes
+    u_bytes = decode_unique_bytes(w, esize) if g.shared_prefix else d_bytes
     p_bytes, p_flops = prefill_bytes_flops(w)
     step_bytes = u_bytes + scatter_bytes(w, esize) + copy_bytes(w, esize) + p_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -290,8 +291,10 @@ def main():
         "pct_of_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode_fp8 (partition + merge kernels)" if fp8
-                      else "pa_decode (partition + merge kernels)",
+            "kernel": ("pa_decode_shared_prefix" if g.shared_prefix else "pa_decode") +
+                      ("_fp8" if fp8 else "") +
+                      (" (prefix + partition + merge kernels)" if g.shared_prefix
+                       else " (partition + merge kernels)"),
             "achieved": round(dec_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

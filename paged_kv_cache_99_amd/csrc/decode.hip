@@ -8,7 +8,10 @@
 // are combined by rescaling to the common maximum (devpress.csdn.net/amd vLLM overview, §9 (4)
 // online softmax; §3 (3) per-block accumulation over the block table).
 //
-// Work unit: one wavefront per (sequence, kv head, query-head subgroup, partition). A (block,
+// Work unit: one workgroup of kUnitWaves wavefronts per (sequence, kv head, query-head subgroup,
+// partition); wave w takes blocks w, w + kUnitWaves, ... of the unit's range, and the waves'
+// results are merged through LDS at the end (a unit then takes a quarter of the time, which
+// shortens the tail of batches with few, uneven units). A (block,
 // kv head) tile is 16 rows x D contiguous 16-bit words (4 KiB at D = 128). Lane l of the wave
 // loads 16 bytes at offset 16*l of each 1 KiB piece of the tile, so every load instruction reads
 // one contiguous KiB, and lane l then holds 8 dims (l % RL)*8.. of token rows (l / RL) + ROWS*i.
@@ -64,6 +67,7 @@ struct DecodeParams {
     int32_t ws_rows;      // (sequence, head) rows: num_seqs * num_q_heads
     int32_t wg_parts;     // MFMA kernel: parts merged per workgroup (1 or kMfmaWaves)
     int32_t slot_tokens;  // tokens of a row's own workspace slot: part_tokens * wg_parts
+    int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: part_tokens * kMfmaWaves
     int32_t slot_base;    // first slot these units write
     int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix parts (merge)
     int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
@@ -76,9 +80,10 @@ __device__ __forceinline__ int unit_start(const DecodeParams &p, int seq, int L)
 }
 
 // F8: the caches hold E4M3 codes (one byte per element) instead of 16-bit elements.
-// Independent units (one wave each, no LDS, no barrier) per workgroup of the vector-ALU kernel:
-// fewer, larger workgroups keep more waves resident than one-wave workgroups.
-constexpr int kUnitWaves = 2;
+// Waves per unit of the vector-ALU kernel. Measured on the 7B-shaped layer and on 256 sequences
+// of U{1..512} tokens: 1 wave per unit (two units per workgroup) 76.7 % / 70.5 % of 8 TB/s, 2 waves
+// 77.3 % / 74.3 %, 4 waves 77.5 % / 76.7 %; 8 waves lost on E4M3 caches (66 %).
+constexpr int kUnitWaves = 4;
 
 template <bool BF, bool F8, int D, int GK>
 __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(DecodeParams p)
@@ -91,10 +96,11 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
     constexpr int ESZ = F8 ? 1 : 2;      // bytes per cache element
     const int lane = threadIdx.x & (kWave - 1);
     const int r = lane / RL;
+    const int w = threadIdx.x / kWave;  // this wave takes blocks w, w + kUnitWaves, ... of the unit
 
-    const int unit = xcd_logical_id(blockIdx.x, gridDim.x) * kUnitWaves + (int)(threadIdx.x / kWave);
+    const int unit = xcd_logical_id(blockIdx.x, gridDim.x);  // one unit per workgroup
     if (unit >= p.n_units)
-        return;
+        return;  // uniform over the workgroup
     const int seq = unit % p.num_seqs;
     int rest = unit / p.num_seqs;
     const int part = rest % p.max_parts;
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int t0 = unit_start(p, seq, L) + part * p.part_tokens;
     if (p.split && t0 >= L)
-        return;  // a part with no tokens: the merge never reads it
+        return;  // a part with no tokens: the merge never reads it (uniform)
     const int t1 = min(L, t0 + p.part_tokens);
 
     uint4 q[GK][QV];
@@ -226,10 +232,11 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
         };
 
         uint4 ka[NCH], va[NCH], kn[NCH], vn[NCH];
-        load(0, ka, va);
-        for (int k = 0; k < nb; ++k) {
-            if (k + 1 < nb)
-                load(k + 1, kn, vn);
+        if (w < nb)
+            load(w, ka, va);
+        for (int k = w; k < nb; k += kUnitWaves) {
+            if (k + kUnitWaves < nb)
+                load(k + kUnitWaves, kn, vn);
             consume(k, ka, va);
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
@@ -261,6 +268,47 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
         }
         m[h] = M;
         l[h] = lh;
+    }
+
+    // merge the waves' results: waves 1.. publish theirs, wave 0 rescales to the common maximum
+    __shared__ float xs[kUnitWaves - 1][GK][RL][EPL + 2];
+    if (w > 0 && lane < RL) {
+#pragma unroll
+        for (int h = 0; h < GK; ++h) {
+#pragma unroll
+            for (int j = 0; j < EPL; ++j)
+                xs[w - 1][h][lane][j] = acc[h][j];
+            xs[w - 1][h][lane][EPL] = m[h];
+            xs[w - 1][h][lane][EPL + 1] = l[h];
+        }
+    }
+    __syncthreads();
+    if (w > 0)
+        return;
+    if (lane < RL) {
+#pragma unroll
+        for (int h = 0; h < GK; ++h) {
+            float M = m[h];
+#pragma unroll
+            for (int v = 0; v < kUnitWaves - 1; ++v)
+                M = fmaxf(M, xs[v][h][lane][EPL]);
+            const float Ms = M == -INFINITY ? 0.0f : M;
+            const float f0 = fast_exp2(m[h] - Ms);
+            float lh = l[h] * f0;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j)
+                acc[h][j] *= f0;
+#pragma unroll
+            for (int v = 0; v < kUnitWaves - 1; ++v) {
+                const float fv = fast_exp2(xs[v][h][lane][EPL] - Ms);
+                lh += xs[v][h][lane][EPL + 1] * fv;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    acc[h][j] += xs[v][h][lane][j] * fv;
+            }
+            m[h] = M;
+            l[h] = lh;
+        }
     }
 
     if (lane < RL) {
@@ -649,6 +697,66 @@ __device__ __forceinline__ void mfma_write_output(const DecodeParams &p, int qro
                                               pack2<BF>(o[t][2] * inv, o[t][3] * inv));
 }
 
+constexpr int kMfmaWaves = 4;  // MFMA units (waves) per workgroup
+
+// LDS of a workgroup of kMfmaWaves MFMA units: each wave's V staging area, reused by the merge.
+template <int D>
+struct MfmaLds {
+    uint8_t stage[kMfmaWaves * kUnitLds<D>];
+    float2 ml[kMfmaWaves][kWave];
+};
+
+// Merge the (m, l, acc) results of the workgroup's kMfmaWaves waves (tokens of disjoint ranges of
+// the same query rows) by rescaling to their common maximum, and write the result as one partial
+// to workspace slot `slot`. Every wave of the workgroup must call it (it holds two barriers); wave w
+// combines output tiles w, w + kMfmaWaves, ... A wave with an empty range contributes m = -inf.
+template <bool F8, int D>
+__device__ __forceinline__ void mfma_workgroup_merge(const DecodeParams &p, int qrow, int slot,
+                                                     const f32x4 (&o)[D / 16], float m, float lsum,
+                                                     MfmaLds<D> &sm)
+{
+    constexpr int NT = D / 16;
+    static_assert(kMfmaWaves * NT * kWave * 16 <= (int)sizeof(sm.stage), "merge buffer");
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    __syncthreads();  // every wave is done with its V staging
+    f32x4 *ox = (f32x4 *)sm.stage;  // [wave][tile][lane]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        ox[(w * NT + t) * kWave + lane] = o[t];
+    sm.ml[w][lane] = make_float2(m, lsum);
+    __syncthreads();
+    float2 mls[kMfmaWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kMfmaWaves; ++v) {
+        mls[v] = sm.ml[v][lane];
+        M = fmaxf(M, mls[v].x);
+    }
+    float a[kMfmaWaves], lm = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kMfmaWaves; ++v) {
+        a[v] = mls[v].x == -INFINITY ? 0.0f : fast_exp2(mls[v].x - M);
+        lm += a[v] * mls[v].y;
+    }
+    if (qrow < 0)
+        return;
+    const int g = lane >> 4;
+    const float vs = F8 ? p.v_scale : 1.0f;
+    float *wa = p.ws_acc + ((size_t)slot * p.ws_rows + qrow) * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t % kMfmaWaves != w)
+            continue;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < kMfmaWaves; ++v)
+            acc += a[v] * ox[(v * NT + t) * kWave + lane];
+        *(float4 *)(wa + 16 * t) = make_float4(acc[0] * vs, acc[1] * vs, acc[2] * vs, acc[3] * vs);
+    }
+    if (w == 0 && g == 0)
+        *(float2 *)(p.ws_ml + ((size_t)qrow * p.ws_slots + slot) * 2) = make_float2(M, lm);
+}
+
 // Plain decode of head groups of 3 or more. A workgroup is kMfmaWaves waves, at most three per SIMD
 // (at most 168 registers): each unit holds one step of K and V operands in flight, so the number
 // of resident waves sets the bytes in flight per CU.
@@ -660,16 +768,13 @@ __device__ __forceinline__ void mfma_write_output(const DecodeParams &p, int qro
 //    times their share of the HBM traffic.
 //  * Otherwise (p.wg_parts == 1): the waves are independent units (sequence, part, subgroup, kv
 //    head) that write their own partial result, or the output when the decode is not split.
-constexpr int kMfmaWaves = 4;
 
 template <bool BF, bool F8, int D>
 __global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_mfma_kernel(DecodeParams p)
 {
     constexpr int NT = D / 16;
-    __shared__ __align__(16) uint8_t lds[kMfmaWaves * kUnitLds<D>];  // V staging; then the merge
-    __shared__ float2 ml_lds[kMfmaWaves][kWave];
-    static_assert(kMfmaWaves * NT * kWave * 16 <= kMfmaWaves * kUnitLds<D>, "merge buffer");
+    __shared__ __align__(16) MfmaLds<D> sm;
     const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
     const bool merged = p.wg_parts == kMfmaWaves;
@@ -696,7 +801,7 @@ decode_mfma_kernel(DecodeParams p)
     f32x4 o[NT];
     float m, l;
     mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
-                         lds + w * kUnitLds<D>, o, m, l);
+                         sm.stage + w * kUnitLds<D>, o, m, l);
     const float lsum = column_sum(l);
     if (!p.split) {
         mfma_write_output<BF, F8, D>(p, qrow, o, lsum);
@@ -706,85 +811,50 @@ decode_mfma_kernel(DecodeParams p)
         mfma_write_partial<F8, D>(p, qrow, p.slot_base + part, o, m, lsum);
         return;
     }
-    // merge the workgroup's parts: wave w combines output tiles [w*NT/W, (w+1)*NT/W) of all parts
-    __syncthreads();  // every wave is done with its V staging
-    f32x4 *ox = (f32x4 *)lds;  // [wave][tile][lane]
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-        ox[(w * NT + t) * kWave + lane] = o[t];
-    ml_lds[w][lane] = make_float2(m, lsum);
-    __syncthreads();
-    float2 mls[kMfmaWaves];
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kMfmaWaves; ++v) {
-        mls[v] = ml_lds[v][lane];
-        M = fmaxf(M, mls[v].x);
-    }
-    float a[kMfmaWaves], L2 = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kMfmaWaves; ++v) {
-        a[v] = mls[v].x == -INFINITY ? 0.0f : fast_exp2(mls[v].x - M);
-        L2 += a[v] * mls[v].y;
-    }
-    if (qrow < 0)
-        return;
-    const int g = lane >> 4;
-    const float vs = F8 ? p.v_scale : 1.0f;
-    const int slot = p.slot_base + q;
-    float *wa = p.ws_acc + ((size_t)slot * p.ws_rows + qrow) * D + 4 * g;
-    constexpr int TPW = NT / kMfmaWaves;  // tiles per wave
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int t = w * TPW + tt;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int v = 0; v < kMfmaWaves; ++v)
-            acc += a[v] * ox[(v * NT + t) * kWave + lane];
-        *(float4 *)(wa + 16 * t) = make_float4(acc[0] * vs, acc[1] * vs, acc[2] * vs, acc[3] * vs);
-    }
-    if (w == 0 && g == 0)
-        *(float2 *)(p.ws_ml + ((size_t)qrow * p.ws_slots + slot) * 2) = make_float2(M, L2);
+    mfma_workgroup_merge<F8, D>(p, qrow, p.slot_base + q, o, m, lsum, sm);
 }
 
-// Shared-prefix unit: (prefix group g, kv head, subgroup of 16 (member, query head) pairs, part).
-// The members of group g are sequences group_starts[g] .. group_starts[g+1]-1; they share the
-// blocks of positions [0, seq_starts[first member]), read here once through the first member's
-// table for all of them (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are
-// stored once). Pair v of the group is member v / G, query head kvh*G + v % G.
+// Shared-prefix units: workgroup (prefix group g, kv head, subgroup of 16 (member, query head)
+// pairs, prefix slot q); wave w takes part kMfmaWaves*q + w of the prefix and the workgroup merges
+// its parts into slot q as decode_mfma_kernel does. The members of group g are sequences
+// group_starts[g] .. group_starts[g+1]-1; they share the blocks of positions
+// [0, seq_starts[first member]), read here once through the first member's table for all of them
+// (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are stored once). Pair v of
+// the group is member v / G, query head kvh*G + v % G.
 template <bool BF, bool F8, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void
+__global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_prefix_mfma_kernel(DecodeParams p)
 {
+    __shared__ __align__(16) MfmaLds<D> sm;
+    const int w = threadIdx.x / kWave;
     const int unit = xcd_logical_id(blockIdx.x, gridDim.x);
     if (unit >= p.n_units)
-        return;
+        return;  // uniform over the workgroup
     int rest = unit;
     const int vsub = rest % p.n_vsub;
     rest /= p.n_vsub;
     const int kvh = rest % p.num_kv_heads;
     rest /= p.num_kv_heads;
-    const int part = rest % p.max_parts;
-    const int grp = rest / p.max_parts;
+    const int q = rest % p.pre_slots;
+    const int grp = rest / p.pre_slots;
     const int first = min(max(p.group_starts[grp], 0), p.num_seqs);
     const int n_mem = min(max(p.group_starts[grp + 1], first), p.num_seqs) - first;
     const int G = p.num_q_heads / p.num_kv_heads;
     if (n_mem == 0 || vsub * kCols >= n_mem * G)
-        return;
+        return;  // uniform
     const int L0 = min(max(p.seq_lens[first], 0), p.max_seq_len);
     const int prefix = min(max(p.seq_starts[first], 0), L0);
-    const int t0 = part * p.part_tokens;
-    if (t0 >= prefix)
-        return;
+    if (q * p.pre_slot_tokens >= prefix)
+        return;  // uniform: the slot holds no prefix tokens
+    const int t0 = min(prefix, (q * kMfmaWaves + w) * p.part_tokens);
     const int t1 = min(prefix, t0 + p.part_tokens);
     const int v = vsub * kCols + (threadIdx.x & 15);
     const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
-    __shared__ __align__(16) uint8_t v_lds[kUnitLds<D>];
     f32x4 o[D / 16];
     float m, l;
-    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1, v_lds,
-                         o, m, l);
-    mfma_write_partial<F8, D>(p, qrow, part, o, m, column_sum(l));
+    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)first * p.max_blocks, kvh, t0, t1,
+                         sm.stage + w * kUnitLds<D>, o, m, l);
+    mfma_workgroup_merge<F8, D>(p, qrow, q, o, m, column_sum(l), sm);
 }
 
 // One wave per (sequence, query head): rescale every part to the common maximum M,
@@ -807,7 +877,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int start = unit_start(p, seq, L);
     // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots
-    const int n_pre = p.pre_slots > 0 ? (start + p.part_tokens - 1) / p.part_tokens : 0;
+    const int n_pre = p.pre_slots > 0 ? (start + p.pre_slot_tokens - 1) / p.pre_slot_tokens : 0;
     const int n_own = (L - start + p.slot_tokens - 1) / p.slot_tokens;
     const int np = n_pre + n_own;
     auto slot_of = [&](int jj) { return jj < n_pre ? jj : p.pre_slots + (jj - n_pre); };
@@ -878,8 +948,7 @@ hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
                                               : (p.n_units + kMfmaWaves - 1) / kMfmaWaves)),
                            dim3(kWave * kMfmaWaves), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>),
-                           dim3(round_up8((p.n_units + kUnitWaves - 1) / kUnitWaves)),
+        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>), dim3(round_up8(p.n_units)),
                            dim3(kWave * kUnitWaves), 0, stream, p);
     return hipGetLastError();
 }
@@ -891,7 +960,7 @@ hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hi
     hipError_t e;
     if (pre) {
         hipLaunchKernelGGL((decode_prefix_mfma_kernel<BF, F8, D>), dim3(round_up8(pre->n_units)),
-                           dim3(kWave), 0, stream, *pre);
+                           dim3(kWave * kMfmaWaves), 0, stream, *pre);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
@@ -953,19 +1022,22 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
 
     DecodeParams pre;
     if (cascade) {
-        // slots [0, pre_parts) of every row hold shared-prefix parts, the rest its own parts
+        // slots [0, pre_slots) of every row hold shared-prefix results (kMfmaWaves parts each),
+        // the rest its own parts
         const int pre_parts = (d.max_prefix_len + d.partition_size - 1) / d.partition_size;
+        const int pre_slots = (pre_parts + kMfmaWaves - 1) / kMfmaWaves;
         p.seq_starts = d.seq_starts;
-        p.pre_slots = pre_parts;
-        p.slot_base = pre_parts;
-        p.ws_slots = pre_parts + own_slots;
+        p.pre_slots = pre_slots;
+        p.pre_slot_tokens = d.partition_size * kMfmaWaves;
+        p.slot_base = pre_slots;
+        p.ws_slots = pre_slots + own_slots;
         pre = p;
         pre.group_starts = d.group_starts;
         pre.num_groups = d.num_groups;
         const int pairs = d.max_group_size * group;  // (member, query head) pairs per kv head
         pre.n_vsub = (pairs + kCols - 1) / kCols;
-        pre.max_parts = pre_parts;
-        const int64_t pre_units = (int64_t)d.num_groups * pre_parts * d.c.num_kv_heads * pre.n_vsub;
+        // workgroups: (group, prefix slot, kv head, pair subgroup)
+        const int64_t pre_units = (int64_t)d.num_groups * pre_slots * d.c.num_kv_heads * pre.n_vsub;
         if (pre_units > 0x7ffffff0)
             return hipErrorInvalidValue;
         pre.n_units = (int32_t)pre_units;

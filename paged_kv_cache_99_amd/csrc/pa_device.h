@@ -199,6 +199,15 @@ __device__ __forceinline__ uint4 load_nt(const void *p)
     return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
+// 16-byte store marked nontemporal (global_store_dwordx4 ... nt), for cache writes that the next
+// kernels of the step do not read back soon: the lines leave the caches with the writing kernel
+// instead of being written back to HBM while a following HBM-bound kernel streams its reads.
+__device__ __forceinline__ void store_nt(void *p, const uint4 &v)
+{
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, (u32x4 *)p);
+}
+
 // 16-byte direct-to-LDS load (global_load_lds_dwordx4, scalar-base form): lane i reads the 16
 // bytes at sbase + voff_i and writes them to LDS address lds + 16 * i; sbase and lds are
 // wave-uniform. M0 carries the LDS address and needs one wait state (s_nop 0) before the load

@@ -7,7 +7,9 @@
 //
 // Layout: key/value [T][H_kv][D]; cache [num_blocks][H_kv][16][D]. One thread moves 16 bytes of K
 // and 16 bytes of V; consecutive threads read consecutive input bytes (coalesced) and write whole
-// 16-byte pieces of a D-element cache row (a 128/256-byte run per head).
+// 16-byte pieces of a D-element cache row (a 128/256-byte run per head), with nontemporal stores
+// (the attention kernels of the step stream their reads while ordinary stores would still be
+// waiting in the caches to be written back).
 //
 // E4M3 caches (lecture 34 "vLLM 生产级系统架构全景剖析" §4.4: one byte per key and value element):
 // a thread reads 16 elements (32 bytes) of K and of V and writes their 16 codes. The code of x is
@@ -37,8 +39,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const int32_t blk = slot / kBlock, off = slot % kBlock;
     const int32_t head = v / vec_per_row, piece = v % vec_per_row;
     const int64_t dst = (((int64_t)blk * num_kv_heads + head) * kBlock + off) * vec_per_row + piece;
-    k_cache[dst] = key[i];
-    v_cache[dst] = value[i];
+    store_nt(&k_cache[dst], key[i]);
+    store_nt(&v_cache[dst], value[i]);
 }
 
 // Codes of the four 16-bit elements of (w0, w1), element j in byte j.
@@ -87,8 +89,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const int32_t blk = slot / kBlock, off = slot % kBlock;
     const int32_t head = v / pieces_per_row, piece = v % pieces_per_row;
     const int64_t dst = (((int64_t)blk * num_kv_heads + head) * kBlock + off) * pieces_per_row + piece;
-    k_cache[dst] = quantize16<BF>(key[2 * i], key[2 * i + 1], k_scale);
-    v_cache[dst] = quantize16<BF>(value[2 * i], value[2 * i + 1], v_scale);
+    store_nt(&k_cache[dst], quantize16<BF>(key[2 * i], key[2 * i + 1], k_scale));
+    store_nt(&v_cache[dst], quantize16<BF>(value[2 * i], value[2 * i + 1], v_scale));
 }
 
 }  // namespace
