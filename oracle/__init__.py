@@ -28,6 +28,7 @@ _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_u64p = np.ctypeslib.ndpointer(dtype=np.uint64, flags="C_CONTIGUOUS")
 _c_int, _c_double = ctypes.c_int, ctypes.c_double
 
 
@@ -52,6 +53,9 @@ def lib():
         L.oracle_prefill.argtypes = [_u16p, _u16p, _u16p, _i32p, _c_int, _i32p, _i32p, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_double,
                                      ctypes.c_void_p, _c_int, _c_int, _f64p]
+        L.oracle_prefill_tree.argtypes = [_u16p, _u16p, _u16p, _i32p, _c_int, _i32p, _i32p,
+                                          _u64p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_double, _c_int, _f64p]
         L.oracle_split_merge.argtypes = [_f64p, _f64p, _f64p, _c_int, _c_int, _c_double, _c_int,
                                          _f64p]
         L.oracle_poison_free_slots.restype = ctypes.c_long
@@ -197,6 +201,22 @@ def prefill(query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens, H_q, H_k
                               _i32(seq_lens), cu, S, H_q, H_kv, D, num_blocks, _DTYPES[dtype],
                               scale, rp, n, nthreads, out)
     _check(rc, "prefill")
+    return out
+
+
+def prefill_tree(query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens, tree_mask, H_q, H_kv,
+                 D, num_blocks, dtype, scale, nthreads=0):
+    """T1: paged prefill of drafted-token trees (at most 64 rows per sequence): row i of a sequence
+    sees its context and chunk rows j <= i whose bit j is set in tree_mask[row] (uint64 [total_q]).
+    query [total_q][H_q][D] words. Returns float64 [total_q][H_q][D]."""
+    bt = _i32(block_tables)
+    cu = _i32(cu_q_lens)
+    tm = np.ascontiguousarray(tree_mask, dtype=np.uint64)
+    out = np.zeros((int(cu[-1]), H_q, D), dtype=np.float64)
+    rc = lib().oracle_prefill_tree(_u16(query), _u16(k_cache), _u16(v_cache), bt, bt.shape[1],
+                                   _i32(seq_lens), cu, tm, bt.shape[0], H_q, H_kv, D, num_blocks,
+                                   _DTYPES[dtype], scale, nthreads, out)
+    _check(rc, "prefill_tree")
     return out
 
 

@@ -16,7 +16,9 @@
  *   [OV]   devpress.csdn.net/amd vLLM overview: §3 PagedAttention (3) pseudo-code (per-block
  *          accumulation over the block table), §9 FlashAttention (4) online softmax (running max
  *          and running sum of exponentials, rescaled at the end).
- *   [V1]   lilinji.mintlify.site lecture 34, "vLLM 生产级系统架构全景剖析…": §4.4 FP8 KV cache.
+ *   [V1]   lilinji.mintlify.site lecture 34, "vLLM 生产级系统架构全景剖析…": §4.4 FP8 KV cache;
+ *          §5.3 draft trees (EAGLE): a tree of drafted tokens is verified by the target model in
+ *          one pass, each drafted token seeing the context and its own ancestors.
  *   [OFP8] the OCP 8-bit floating point specification (not one of the pages): the E4M3 format.
  *
  * Cache layout (an interface fact, fixed by the library's header, restated here on its own):
@@ -502,6 +504,88 @@ int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_
                 free(V);
                 free(q);
             }
+        }
+        if (rc != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            status = rc;
+        }
+    }
+    return status;
+}
+
+
+/* ---------------------------------------------------------------- T1: tree-masked prefill */
+/* [V1] §5.3 (a draft tree checked in one target pass) with [PD] §5.4 (k drafted tokens verified
+ * together): the q_len rows of sequence s are the drafted tokens at positions first .. L-1,
+ * first = L - q_len, and row i sees every context position 0..first-1 plus chunk row j (position
+ * first + j) exactly when j <= i and bit j of tree_mask[cu_q_lens[s] + i] is set. The visible rows
+ * are gathered in position order and given to O5. q_len <= 64 (one 64-bit mask per row). */
+int oracle_prefill_tree(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
+                        const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                        const int32_t *cu_q_lens, const uint64_t *tree_mask, int S, int H_q,
+                        int H_kv, int D, int num_blocks, int dtype, double scale, int nthreads,
+                        double *out)
+{
+    if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
+        return OR_BAD_ARG;
+    for (int s = 0; s < S; ++s)
+        if (cu_q_lens[s + 1] - cu_q_lens[s] > 64 || cu_q_lens[s + 1] < cu_q_lens[s])
+            return OR_BAD_ARG;
+    int total_q = cu_q_lens[S];
+    int n = total_q * H_q;
+    int group = H_q / H_kv;
+    int status = OR_OK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int idx = 0; idx < n; ++idx) {
+        int r = idx / H_q, h = idx % H_q;
+        int rc = OR_OK;
+        int s = -1;
+        for (int j = 0; j < S; ++j)
+            if (cu_q_lens[j] <= r && r < cu_q_lens[j + 1])
+                s = j;
+        int q_len = cu_q_lens[s + 1] - cu_q_lens[s];
+        int i = r - cu_q_lens[s];
+        int first = seq_lens[s] - q_len;
+        int p = first + i;
+        if (first < 0 || seq_lens[s] > max_blocks * OR_BLOCK) {
+            rc = OR_BAD_INDEX;
+        } else {
+            int L = p + 1;
+            double *K = (double *)malloc(sizeof(double) * (size_t)L * D);
+            double *V = (double *)malloc(sizeof(double) * (size_t)L * D);
+            double *q = (double *)malloc(sizeof(double) * (size_t)D);
+            if (!K || !V || !q) {
+                rc = OR_NO_MEM;
+            } else {
+                const int32_t *row = block_tables + (size_t)s * max_blocks;
+                rc = oracle_gather(k_cache, row, L, h / group, num_blocks, H_kv, D, dtype, K);
+                if (rc == OR_OK)
+                    rc = oracle_gather(v_cache, row, L, h / group, num_blocks, H_kv, D, dtype, V);
+                /* keep the visible positions, in order */
+                int kept = 0;
+                for (int pos = 0; rc == OR_OK && pos < L; ++pos) {
+                    int j = pos - first;
+                    int visible = j < 0 || ((tree_mask[r] >> j) & 1u);
+                    if (!visible)
+                        continue;
+                    memmove(K + (size_t)kept * D, K + (size_t)pos * D, sizeof(double) * D);
+                    memmove(V + (size_t)kept * D, V + (size_t)pos * D, sizeof(double) * D);
+                    ++kept;
+                }
+                for (int d = 0; d < D; ++d)
+                    q[d] = oracle_to_double(query[((size_t)r * H_q + h) * D + d], dtype);
+                if (rc == OR_OK)
+                    rc = oracle_attention(q, K, V, kept, D, scale, out + (size_t)idx * D);
+            }
+            free(K);
+            free(V);
+            free(q);
         }
         if (rc != OR_OK) {
 #ifdef _OPENMP
