@@ -193,6 +193,29 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
                              int32_t num_q_heads, float scale, void *stream);
 
 /*
+ * pa_prefill_chunk_tree -- pa_prefill_chunk for chunks that hold a tree of drafted tokens.
+ * [V1] §5.3: a draft tree (EAGLE) is checked by the target model in one pass, every drafted token
+ * seeing the context and the drafted tokens on its own path from the root; [PD] §5.4: the k drafts
+ * are verified together. The chunk rows of sequence s are the drafted tokens, stored at positions
+ * first_s .. seq_lens[s]-1 (first_s = seq_lens[s] - q_len_s) in tree order (a node after its
+ * parent). Row i (position first_s + i) attends every position 0..first_s-1 and chunk row j
+ * exactly when j <= i and bit j of tree_mask[cu_q_lens[s] + i] is set -- the mask of a node is
+ * usually its ancestors and itself. A row that attends no position is written as zeros.
+ *   tree_mask     [total_q] uint64, device memory, 8-byte aligned; bits j > i are ignored.
+ *   max_q_len     at most 64 (PA_ERR_INVALID_ARG otherwise); q_len_s <= max_q_len and
+ *                 q_len_s <= seq_lens[s] are the caller's contract.
+ * Everything else -- layouts, the other arguments, errors -- as in pa_prefill_chunk.
+ */
+pa_status_t pa_prefill_chunk_tree(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                  int32_t head_dim, void *out, const void *query,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                  const uint64_t *tree_mask, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_q_len, int32_t num_q_heads, float scale,
+                                  void *stream);
+
+/*
  * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into E4M3 caches ([V1] §4.4).
  * key and value are [num_tokens][num_kv_heads][head_dim] elements of `dtype` (F16 or BF16). The
  * byte written for element x is the E4M3 code of x / k_scale (keys) or x / v_scale (values): the

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_fp8.restype = _i
         L.pa_decode_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _f,
                                     _f, _i, _p, _sz, _p]
+        L.pa_prefill_chunk_tree.restype = _i
+        L.pa_prefill_chunk_tree.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p,
+                                            _i, _i, _i, _i, _f, _p]
         L.pa_prefill_chunk.restype = _i
         L.pa_prefill_chunk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _i,
                                        _i, _f, _p]
@@ -264,9 +267,10 @@ def decode_shared_prefix_fp8(out, query, k_cache, v_cache, block_tables, seq_len
 
 
 def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,
-                  max_q_len: int, scale: float, stream=None) -> None:
+                  max_q_len: int, scale: float, stream=None, tree_mask=None) -> None:
     """pa_prefill_chunk: out/query [total_q, H_q, D]; cu_q_lens [S+1]; seq_lens [S]; tables
-    [S, max_blocks]."""
+    [S, max_blocks]. With tree_mask (int64 or uint64 [total_q], the 64-bit mask of each row)
+    pa_prefill_chunk_tree: chunks of drafted-token trees, at most 64 rows each."""
     dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
     tq, hq = int(query.shape[0]), int(query.shape[1])
     for t, n in ((query, "query"), (out, "out")):
@@ -278,6 +282,17 @@ def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_len
     S = int(seq_lens.shape[0])
     if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q_lens.shape != (S + 1,):
         raise ValueError("block_tables must be [S, max_blocks] and cu_q_lens [S + 1]")
+    if tree_mask is not None:
+        if not (tree_mask.is_cuda and tree_mask.is_contiguous()) or \
+                tree_mask.dtype not in (torch.int64, torch.uint64) or tuple(tree_mask.shape) != (tq,):
+            raise ValueError(f"tree_mask must be a contiguous int64/uint64 GPU tensor [{tq}]")
+        _check(lib().pa_prefill_chunk_tree(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
+                                           k_cache.data_ptr(), v_cache.data_ptr(),
+                                           block_tables.data_ptr(), int(block_tables.shape[1]),
+                                           seq_lens.data_ptr(), cu_q_lens.data_ptr(),
+                                           tree_mask.data_ptr(), S, tq, int(max_q_len), hq,
+                                           float(scale), _stream(stream)))
+        return
     _check(lib().pa_prefill_chunk(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
                                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
                                   int(block_tables.shape[1]), seq_lens.data_ptr(),

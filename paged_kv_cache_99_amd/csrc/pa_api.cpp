@@ -450,13 +450,17 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
                               workspace_bytes, stream, true, k_scale, v_scale);
 }
 
-pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
-                             int32_t head_dim, void *out, const void *query,
-                             const void *k_cache, const void *v_cache,
-                             const int32_t *block_tables, int32_t max_blocks_per_seq,
-                             const int32_t *seq_lens, const int32_t *cu_q_lens,
-                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                             int32_t num_q_heads, float scale, void *stream)
+}  // extern "C"
+
+namespace {
+
+pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, void *out, const void *query, const void *k_cache,
+                         const void *v_cache, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                         const int32_t *cu_q_lens, const uint64_t *tree_mask, bool tree,
+                         int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                         int32_t num_q_heads, float scale, void *stream)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -465,6 +469,8 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
     REQUIRE(num_seqs >= 0, "num_seqs %d < 0", num_seqs);
     REQUIRE(total_q >= 0, "total_q %d < 0", total_q);
     REQUIRE(max_q_len >= 0, "max_q_len %d < 0", max_q_len);
+    if (tree)
+        REQUIRE(max_q_len <= 64, "max_q_len %d > 64: a tree mask covers at most 64 rows", max_q_len);
     REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
             "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
             num_kv_heads);
@@ -482,6 +488,10 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
     REQUIRE(block_tables != nullptr, "block_tables is NULL");
     REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
     REQUIRE(cu_q_lens != nullptr, "cu_q_lens is NULL");
+    if (tree) {
+        REQUIRE(tree_mask != nullptr, "tree_mask is NULL");
+        REQUIRE(((uintptr_t)tree_mask & 7) == 0, "tree_mask is not 8-byte aligned");
+    }
     pa::PrefillLaunch p;
     p.c = c;
     p.out = out;
@@ -497,7 +507,40 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
     p.max_q_len = max_q_len;
     p.num_q_heads = num_q_heads;
     p.scale = scale;
-    return launched(pa::launch_prefill(p, (hipStream_t)stream), "prefill_chunk");
+    p.tree_mask = tree ? tree_mask : nullptr;
+    return launched(pa::launch_prefill(p, (hipStream_t)stream),
+                    tree ? "prefill_chunk_tree" : "prefill_chunk");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, void *out, const void *query,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, const int32_t *cu_q_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, float scale, void *stream)
+{
+    return prefill_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                        block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, nullptr, false,
+                        num_seqs, total_q, max_q_len, num_q_heads, scale, stream);
+}
+
+pa_status_t pa_prefill_chunk_tree(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                  int32_t head_dim, void *out, const void *query,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                  const uint64_t *tree_mask, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_q_len, int32_t num_q_heads, float scale,
+                                  void *stream)
+{
+    return prefill_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                        block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, tree_mask, true,
+                        num_seqs, total_q, max_q_len, num_q_heads, scale, stream);
 }
 
 }  // extern "C"

@@ -80,6 +80,7 @@ struct PrefillLaunch {
     int32_t max_blocks;
     const int32_t *seq_lens;
     const int32_t *cu_q_lens;
+    const uint64_t *tree_mask = nullptr;  // drafted-token trees: one mask per query row
     int32_t num_seqs;
     int32_t total_q;
     int32_t max_q_len;

@@ -69,6 +69,7 @@ struct PrefillParams {
     const int32_t *__restrict__ block_tables;
     const int32_t *__restrict__ seq_lens;
     const int32_t *__restrict__ cu_q_lens;
+    const uint64_t *__restrict__ tree_mask;  // null: causal; else one mask per query row
     uint16_t *__restrict__ out;
     int32_t max_blocks;
     int32_t num_seqs;
@@ -107,7 +108,7 @@ __device__ __forceinline__ int swz(int r)
         return (r >> 1) & 7;
 }
 
-template <bool BF, int D, int GK>
+template <bool BF, int D, int GK, bool TREE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 {
     constexpr int R = kPairs / GK;                  // query rows per workgroup
@@ -161,11 +162,51 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                                           c * 16 + hh * 8)
                        : make_uint4(0, 0, 0, 0);
 
+    // TREE (drafted-token trees): the row sees chunk row j (position first_pos + j, j <= row) only
+    // when bit j of its mask p.tree_mask[row] is set; every position before the chunk stays visible
+    constexpr bool tree = TREE;
+
     const int last_row = min(row_base + R, q_len) - 1;
     const int key_end = max(0, min(L, first_pos + last_row + 1));
     const int n_tiles = (key_end + kKeys - 1) / kKeys;
-    const int unmasked_below = first_pos + row_base;  // every row of the group sees keys <= this
+    // every row of the group sees the keys <= this
+    const int unmasked_below = tree ? first_pos - 1 : first_pos + row_base;
     const bool ragged_rows = row_base + R > q_len;
+    // visibility bits of the lane's keys in tile t, bit kr for key t*64 + 4*hh + kr (kr < 64)
+    auto tree_bits = [&](int t) PA_INLINE -> uint64_t {
+        // read where needed (masked tiles only): no register holds it through the tile loop
+        const uint64_t tmask = row_ok ? p.tree_mask[q0 + row] : ~0ull;
+        const int jb = t * kKeys + 4 * hh - first_pos;  // chunk row of kr = 0
+        if (jb >= 64)
+            return 0;
+        if (jb >= 0)
+            return tmask >> jb;
+        if (jb > -64)
+            return (tmask << -jb) | ((1ull << -jb) - 1);
+        return ~0ull;
+    };
+    // the causal mask of tile t (keys past the row's position), and the tree mask when given
+    auto apply_mask = [&](f32x16 (&s)[2], int t, int row_pos) PA_INLINE {
+        const int last = row_pos - t * kKeys - 4 * hh;  // key kr must be <= last
+        if constexpr (tree) {
+            const uint64_t bits = tree_bits(t);
+            const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kr = kt * 32 + 8 * (v >> 2) + (v & 3);
+                    const bool seen = ((kr < 32 ? lo >> kr : hi >> (kr - 32)) & 1u) != 0;
+                    s[kt][v] = kr <= last && seen ? s[kt][v] : -INFINITY;
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    s[kt][v] = kt * 32 + 8 * (v >> 2) + (v & 3) <= last ? s[kt][v] : -INFINITY;
+        }
+    };
 
     // the sequence's block table, read with scalar loads (it is read-only while the kernel runs)
     typedef const __attribute__((address_space(4))) int32_t *ctable_t;
@@ -247,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const int v_dim = (g16 & 1) * 16 + 4 * v_q;      // dim within a 32-dim tile
 
     // a bfloat16 P needs its hi + lo split only while some row sees few keys (see kOnePartKeys)
-    const bool one_part = !BF || first_pos + row_base + 1 >= kOnePartKeys;
+    const bool one_part = !BF || unmasked_below + 1 >= kOnePartKeys;
     if (one_part && n_tiles > 0) {
         // ---------------------------------------------------------------- pipelined loop
         // Step t computes PV(t-1), QK(t+1) and the softmax of tile t. Tiles are loaded in pairs:
@@ -326,14 +367,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         // exponentials of values [I0, I1) (value i = s[i / 16][i % 16]), and the packing of P.
         float ms = 0.0f, psum = 0.0f;
         auto sm_max = [&](auto masked, f32x16 (&s)[2], int t) PA_INLINE -> float {
-            if constexpr (decltype(masked)::value) {
-                const int last = pos_p - t * kKeys - 4 * hh;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        s[kt][v] = kt * 32 + 8 * (v >> 2) + (v & 3) <= last ? s[kt][v] : -INFINITY;
-            }
+            if constexpr (decltype(masked)::value)
+                apply_mask(s, t, pos_p);
             float mx = s[0][0];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -398,8 +433,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             return alpha;
         };
 
-        // tiles from t_mask on reach past the first row's position
-        const int t_mask = min(n_tiles, max(0, (first_pos + row_base + 1) / kKeys));
+        // tiles from t_mask on hold keys that some row of the group does not see
+        const int t_mask = min(n_tiles, max(0, (unmasked_below + 1) / kKeys));
         f32x16 sa[2], sb[2];
         uint4 pa[4], pb[4];
 #pragma unroll
@@ -525,14 +560,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 
         const int k0 = t * kKeys;
         const bool need_mask = ragged_rows || k0 + kKeys - 1 > unmasked_below;
-        if (need_mask) {
-            const int last = pos - k0 - 4 * hh;  // key index 8*(v/4) + v%4 + 32*kt must be <= last
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    s[kt][v] = kt * 32 + 8 * (v >> 2) + (v & 3) <= last ? s[kt][v] : -INFINITY;
-        }
+        if (need_mask)
+            apply_mask(s, t, pos);
         float mx = s[0][0];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -626,8 +655,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 template <bool BF, int D, int GK>
 hipError_t launch_typed(const PrefillParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_kernel<BF, D, GK>), dim3(round_up8(p.n_items)), dim3(kThreads), 0,
-                       stream, p);
+    if (p.tree_mask)
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, true>), dim3(round_up8(p.n_items)),
+                           dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false>), dim3(round_up8(p.n_items)),
+                           dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -662,6 +695,7 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
     p.block_tables = d.block_tables;
     p.seq_lens = d.seq_lens;
     p.cu_q_lens = d.cu_q_lens;
+    p.tree_mask = d.tree_mask;
     p.out = (uint16_t *)d.out;
     p.max_blocks = d.max_blocks;
     p.num_seqs = d.num_seqs;

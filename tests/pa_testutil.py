@@ -78,3 +78,27 @@ def assert_attention_close(got_words, ref, dtype, what="", strict=True):
     if strict:
         assert max_abs <= ATOL, f"{what}: max abs error {max_abs:.3e} > {ATOL}"
         assert max_rel <= ROW_RTOL, f"{what}: row-normwise relative error {max_rel:.3e} > {ROW_RTOL}"
+
+
+# ------------------------------------------------------------------ drafted-token trees
+def random_parents(n, rng):
+    """A drafted-token tree in topological order: node i's parent is -1 (a child of the last
+    context token) or an earlier node."""
+    return [int(rng.integers(-1, i)) if i else -1 for i in range(n)]
+
+
+def tree_path(parents, i):
+    """Chunk indices on node i's path from the root, ascending (i included)."""
+    out = []
+    while i >= 0:
+        out.append(i)
+        i = parents[i]
+    return out[::-1]
+
+
+def tree_masks(parents):
+    """The 64-bit mask of every node: itself and its ancestors."""
+    m = []
+    for i, par in enumerate(parents):
+        m.append((1 << i) | (m[par] if par >= 0 else 0))
+    return np.array(m, dtype=np.uint64)

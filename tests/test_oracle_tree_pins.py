@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import pa_workloads as W
+from pa_testutil import random_parents, tree_masks as masks, tree_path as path
 
 
 def sdpa64(q, K, V, scale):
@@ -28,28 +29,6 @@ def rows_of(w, cache, s, kvh, positions):
     pool = np.asarray(cache).reshape(w.num_blocks, w.H_kv, W.BLOCK, w.D)
     blk = w.block_tables[s][pos // W.BLOCK]
     return oracle.to_double(pool[blk, kvh, pos % W.BLOCK, :], w.dtype)
-
-
-def random_parents(n, rng):
-    """A drafted-token tree in topological order: node i's parent is -1 (a child of the last
-    context token) or an earlier node."""
-    return [int(rng.integers(-1, i)) if i else -1 for i in range(n)]
-
-
-def path(parents, i):
-    """Chunk indices on node i's path from the root, ascending (i included)."""
-    out = []
-    while i >= 0:
-        out.append(i)
-        i = parents[i]
-    return out[::-1]
-
-
-def masks(parents):
-    m = []
-    for i, par in enumerate(parents):
-        m.append((1 << i) | (m[par] if par >= 0 else 0))
-    return np.array(m, dtype=np.uint64)
 
 
 def run_tree(w, tree_masks):
