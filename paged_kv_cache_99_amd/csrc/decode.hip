@@ -1,4 +1,6 @@
-// decode.hip -- paged decode attention for gfx950 (HBM-bound; vector ALU, no MFMA).
+// decode.hip -- paged decode attention for gfx950 (HBM-bound): a vector-ALU kernel for groups of 1
+// or 2 query heads per kv head, an MFMA kernel for larger GQA groups and for shared prefixes, and
+// the split-K merge.
 //
 // What it computes: for each sequence s and query head h, softmax(scale * q K^T) V over positions
 // 0..L-1 of kv head h / group (lecture 32 "LLM 在线推理两阶段" §3.1 formula and decode step, §3.4
@@ -8,11 +10,11 @@
 // are combined by rescaling to the common maximum (devpress.csdn.net/amd vLLM overview, §9 (4)
 // online softmax; §3 (3) per-block accumulation over the block table).
 //
-// Work unit: one workgroup of kUnitWaves wavefronts per (sequence, kv head, query-head subgroup,
-// partition); wave w takes blocks w, w + kUnitWaves, ... of the unit's range, and the waves'
-// results are merged through LDS at the end (a unit then takes a quarter of the time, which
-// shortens the tail of batches with few, uneven units). A (block,
-// kv head) tile is 16 rows x D contiguous 16-bit words (4 KiB at D = 128). Lane l of the wave
+// Vector-ALU kernel. Work unit: one workgroup of kUnitWaves wavefronts per (sequence, kv head,
+// query-head subgroup, partition); wave w takes blocks w, w + kUnitWaves, ... of the unit's range,
+// and the waves' results are merged through LDS at the end (a unit then takes a quarter of the
+// time, which shortens the tail of batches with few, uneven units). A (block, kv head) tile is
+// 16 rows x D contiguous 16-bit words (4 KiB at D = 128). Lane l of the wave
 // loads 16 bytes at offset 16*l of each 1 KiB piece of the tile, so every load instruction reads
 // one contiguous KiB, and lane l then holds 8 dims (l % RL)*8.. of token rows (l / RL) + ROWS*i.
 // Scores: each lane dots its 8 dims with the G queries (v_dot2_f32_{f16,bf16}); the RL lanes of a
@@ -27,8 +29,12 @@
 // conversions; k_scale is folded into the score scale and v_scale into the output.
 //
 // Split-K: with partition_size P > 0 the unit covers tokens [part*P, (part+1)*P) and writes its
-// unnormalised accumulator, max and sum (log2 domain) to the workspace; a merge kernel rescales the
-// parts of each (sequence, head) to their common maximum and normalises.
+// unnormalised accumulator, max and sum (log2 domain) to a workspace slot (the MFMA kernel first
+// merges four consecutive parts in LDS and writes one slot for them); a merge kernel rescales the
+// slots of each (sequence, head) to their common maximum and normalises.
+//
+// MFMA kernel (GQA groups of 3 or more, and shared prefixes): the query rows that read one
+// (kv head, token range) are the 16 columns of v_mfma_f32_16x16x32; see mfma_unit below.
 #include <math.h>
 
 #include "pa_device.h"
@@ -69,7 +75,7 @@ struct DecodeParams {
     int32_t slot_tokens;  // tokens of a row's own workspace slot: part_tokens * wg_parts
     int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: part_tokens * kMfmaWaves
     int32_t slot_base;    // first slot these units write
-    int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix parts (merge)
+    int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix results (merge)
     int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
 };
 
