@@ -53,6 +53,10 @@ def lib():
         L.oracle_prefill.argtypes = [_u16p, _u16p, _u16p, _i32p, _c_int, _i32p, _i32p, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_double,
                                      ctypes.c_void_p, _c_int, _c_int, _f64p]
+        L.oracle_prefill_fp8.argtypes = [_u16p, _u8p, _u8p, _i32p, _c_int, _i32p, _i32p, _c_int,
+                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_double,
+                                         _c_double, _c_double, ctypes.c_void_p, _c_int, _c_int,
+                                         _f64p]
         L.oracle_prefill_tree.argtypes = [_u16p, _u16p, _u16p, _i32p, _c_int, _i32p, _i32p,
                                           _u64p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_double, _c_int, _f64p]
@@ -309,6 +313,26 @@ def decode_fp8(query, k_cache, v_cache, block_tables, seq_lens, H_q, H_kv, D, nu
                                  _i32(seq_lens), B, H_q, H_kv, D, num_blocks, _DTYPES[dtype],
                                  scale, k_scale, v_scale, pp, n, nthreads, out)
     _check(rc, "decode_fp8")
+    return out
+
+
+def prefill_fp8(query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens, H_q, H_kv, D,
+                num_blocks, dtype, scale, k_scale, v_scale, rows=None, nthreads=0):
+    """F7: paged causal prefill over E4M3 caches. query [total_q][H_q][D] words of dtype. Returns
+    float64 [total_q][H_q][D], or [n][D] for an explicit list of (row, head) pairs."""
+    bt = _i32(block_tables)
+    cu = _i32(cu_q_lens)
+    if rows is None:
+        out = np.zeros((int(cu[-1]), H_q, D), dtype=np.float64)
+        rp, n = None, 0
+    else:
+        rows = _i32(np.asarray(rows).reshape(-1, 2))
+        out = np.zeros((rows.shape[0], D), dtype=np.float64)
+        rp, n = rows.ctypes.data_as(ctypes.c_void_p), rows.shape[0]
+    rc = lib().oracle_prefill_fp8(_u16(query), _u8(k_cache), _u8(v_cache), bt, bt.shape[1],
+                                  _i32(seq_lens), cu, bt.shape[0], H_q, H_kv, D, num_blocks,
+                                  _DTYPES[dtype], scale, k_scale, v_scale, rp, n, nthreads, out)
+    _check(rc, "prefill_fp8")
     return out
 
 

@@ -451,11 +451,11 @@ int oracle_decode_fp8(const uint16_t *query, const uint8_t *k_cache, const uint8
  * itself). Row i of the chunk sits at absolute position p = seq_lens[s] - q_len + i and attends
  * keys 0..p ([PD] §1.1). `rows` lists (row, head) pairs ([n_rows][2]); NULL means every
  * (row, head) in order. out is [n_rows][D] (or [total_q][H_q][D]). */
-int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
-                   const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
-                   const int32_t *cu_q_lens, int S, int H_q, int H_kv, int D, int num_blocks,
-                   int dtype, double scale, const int32_t *rows, int n_rows, int nthreads,
-                   double *out)
+static int prefill_rows(const uint16_t *query, const void *k_cache, const void *v_cache, int fp8,
+                        double k_scale, double v_scale, const int32_t *block_tables,
+                        int max_blocks, const int32_t *seq_lens, const int32_t *cu_q_lens, int S,
+                        int H_q, int H_kv, int D, int num_blocks, int dtype, double scale,
+                        const int32_t *rows, int n_rows, int nthreads, double *out)
 {
     if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
         return OR_BAD_ARG;
@@ -492,9 +492,11 @@ int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_
                     rc = OR_NO_MEM;
                 } else {
                     const int32_t *row = block_tables + (size_t)s * max_blocks;
-                    rc = oracle_gather(k_cache, row, L, h / group, num_blocks, H_kv, D, dtype, K);
+                    rc = gather_kv(k_cache, fp8, k_scale, row, L, h / group, num_blocks, H_kv, D,
+                                   dtype, K);
                     if (rc == OR_OK)
-                        rc = oracle_gather(v_cache, row, L, h / group, num_blocks, H_kv, D, dtype, V);
+                        rc = gather_kv(v_cache, fp8, v_scale, row, L, h / group, num_blocks, H_kv,
+                                       D, dtype, V);
                     for (int d = 0; d < D; ++d)
                         q[d] = oracle_to_double(query[((size_t)r * H_q + h) * D + d], dtype);
                     if (rc == OR_OK)
@@ -513,6 +515,32 @@ int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_
         }
     }
     return status;
+}
+
+int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
+                   const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                   const int32_t *cu_q_lens, int S, int H_q, int H_kv, int D, int num_blocks,
+                   int dtype, double scale, const int32_t *rows, int n_rows, int nthreads,
+                   double *out)
+{
+    return prefill_rows(query, k_cache, v_cache, 0, 1.0, 1.0, block_tables, max_blocks, seq_lens,
+                        cu_q_lens, S, H_q, H_kv, D, num_blocks, dtype, scale, rows, n_rows,
+                        nthreads, out);
+}
+
+/* F7: O7 over E4M3 caches ([V1] §4.4): the gathered rows are code value x k_scale / v_scale (F5),
+ * the queries 16-bit words of dtype. */
+int oracle_prefill_fp8(const uint16_t *query, const uint8_t *k_cache, const uint8_t *v_cache,
+                       const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                       const int32_t *cu_q_lens, int S, int H_q, int H_kv, int D, int num_blocks,
+                       int dtype, double scale, double k_scale, double v_scale,
+                       const int32_t *rows, int n_rows, int nthreads, double *out)
+{
+    if (!(k_scale > 0) || !(v_scale > 0))
+        return OR_BAD_ARG;
+    return prefill_rows(query, k_cache, v_cache, 1, k_scale, v_scale, block_tables, max_blocks,
+                        seq_lens, cu_q_lens, S, H_q, H_kv, D, num_blocks, dtype, scale, rows,
+                        n_rows, nthreads, out);
 }
 
 

@@ -186,3 +186,44 @@ def test_fp8_decode_matches_sdpa_on_dequantized_rows():
             q = torch.from_numpy(oracle.to_double(w.query_decode[s, h], "f16"))[None, None, None]
             want = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=w.scale)
             assert np.allclose(out[s, h], want[0, 0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fp8_prefill_equals_16bit_prefill_on_exactly_representable_pool(dtype):
+    """F7 on a pool that E4M3 codes hold without loss equals the 16-bit prefill (O7) bit for bit."""
+    w = W.build([30, 90, 17], 4, 2, 64, dtype, seed=54, n_decode=0, q_lens=[30, 25, 4])
+    rng = np.random.default_rng(54)
+    ks, vs = 2.0 ** -6, 2.0 ** -4
+    k16, kcodes = exact_fp8_pool(w, rng, ks)
+    v16, vcodes = exact_fp8_pool(w, rng, vs)
+    a = oracle.prefill(w.query_prefill, k16, v16, w.block_tables, w.seq_lens, w.cu_q_lens, 4, 2,
+                       64, w.num_blocks, dtype, w.scale)
+    b = oracle.prefill_fp8(w.query_prefill, kcodes, vcodes, w.block_tables, w.seq_lens,
+                           w.cu_q_lens, 4, 2, 64, w.num_blocks, dtype, w.scale, ks, vs)
+    assert np.array_equal(a, b)
+
+
+def test_fp8_prefill_rows_match_causal_sdpa_on_dequantized_rows():
+    """Chunk rows of F7 are causal softmax attention over code value * scale rows (torch sdpa,
+    float64, explicit mask), the rows gathered with numpy from the 4-d pool view."""
+    w = W.build([70, 33], 4, 2, 64, "bf16", seed=55, n_decode=0, q_lens=[20, 33])
+    ks, vs = 0.05, 0.015
+    kc = oracle.quantize_e4m3(w.k_cache, "bf16", ks)
+    vc = oracle.quantize_e4m3(w.v_cache, "bf16", vs)
+    out = oracle.prefill_fp8(w.query_prefill, kc, vc, w.block_tables, w.seq_lens, w.cu_q_lens,
+                             4, 2, 64, w.num_blocks, "bf16", w.scale, ks, vs)
+    k4 = torch_e4m3_to_f64(kc).reshape(w.num_blocks, 2, 16, 64) * ks
+    v4 = torch_e4m3_to_f64(vc).reshape(w.num_blocks, 2, 16, 64) * vs
+    for s in range(2):
+        L = int(w.seq_lens[s])
+        a, b = int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1])
+        pos = np.arange(L)
+        blk = w.block_tables[s][pos // 16]
+        mask = torch.from_numpy(np.arange(L)[None, :] <= np.arange(L - (b - a), L)[:, None])
+        for h in range(4):
+            K = torch.from_numpy(k4[blk, h // 2, pos % 16])[None, None]
+            V = torch.from_numpy(v4[blk, h // 2, pos % 16])[None, None]
+            q = torch.from_numpy(oracle.to_double(w.query_prefill[a:b, h], "bf16"))[None, None]
+            want = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=mask[None, None],
+                                                                    scale=w.scale)
+            assert np.allclose(out[a:b, h], want[0, 0].numpy(), rtol=1e-12, atol=1e-13)
