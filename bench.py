@@ -72,12 +72,12 @@ def copy_bytes(w, esize=2):
     return 4 * len(w.copy_pairs) * 16 * w.H_kv * w.D * esize
 
 
-def prefill_bytes_flops(w):
+def prefill_bytes_flops(w, esize=2):
     nd = w.n_decode
     lens = w.seq_lens[nd:].astype(np.int64)
     cu = np.asarray(w.cu_q_lens, np.int64)
     qlen = np.diff(cu)
-    kv = int(np.sum(lens)) * 2 * w.H_kv * w.D * 2
+    kv = int(np.sum(lens)) * 2 * w.H_kv * w.D * esize
     rows = int(cu[-1]) if len(cu) else 0
     flops = 0
     for L, ql in zip(lens, qlen):
@@ -177,8 +177,7 @@ def main():
                     help="decode shared-prefix groups per sequence instead of reading each "
                          "group's common blocks once")
     ap.add_argument("--kv-cache", choices=["auto", "fp8"], default="auto",
-                    help="fp8: E4M3 caches (quantizing scatter, E4M3 decode); decode-only "
-                         "workloads")
+                    help="fp8: E4M3 caches (quantizing scatter, E4M3 decode and prefill)")
     ap.add_argument("--k-scale", type=float, default=0.03, help="E4M3 key scale")
     ap.add_argument("--v-scale", type=float, default=0.02, help="E4M3 value scale")
     ap.add_argument("--print-decode-src-hash", action="store_true",
@@ -209,10 +208,6 @@ def main():
     print(f"[bench] workload {w.name}: {len(w.seq_lens)} sequences, pool {w.num_blocks} blocks, "
           f"built in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     fp8 = args.kv_cache == "fp8"
-    if fp8 and len(w.cu_q_lens) > 1 and int(w.cu_q_lens[-1]) > 0:
-        print("bench.py --kv-cache fp8 runs decode-only workloads (no prefill kernel reads E4M3 "
-              "caches)", file=sys.stderr)
-        sys.exit(2)
     esize = 1 if fp8 else 2
     g = GpuStep(w, partition_size=args.partition,
                 shared_prefix=not args.no_shared_prefix,
@@ -252,7 +247,7 @@ def main():
 
     d_bytes = decode_bytes(w, esize)
     u_bytes = decode_unique_bytes(w, esize) if g.shared_prefix else d_bytes
-    p_bytes, p_flops = prefill_bytes_flops(w)
+    p_bytes, p_flops = prefill_bytes_flops(w, esize)
     step_bytes = u_bytes + scatter_bytes(w, esize) + copy_bytes(w, esize) + p_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_gbs = u_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0

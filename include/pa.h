@@ -193,6 +193,20 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
                              int32_t num_q_heads, float scale, void *stream);
 
 /*
+ * pa_prefill_chunk_fp8 -- pa_prefill_chunk over E4M3 caches ([V1] §4.4 with [PD] §5.4): keys and
+ * values are read as code value times k_scale / v_scale; query and out are of `dtype` (F16 or
+ * BF16); layouts, the other arguments and errors as in pa_prefill_chunk.
+ */
+pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                 int32_t head_dim, void *out, const void *query,
+                                 const void *k_cache, const void *v_cache,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                 int32_t num_q_heads, float scale, float k_scale, float v_scale,
+                                 void *stream);
+
+/*
  * pa_prefill_chunk_tree -- pa_prefill_chunk for chunks that hold a tree of drafted tokens.
  * [V1] §5.3: a draft tree (EAGLE) is checked by the target model in one pass, every drafted token
  * seeing the context and the drafted tokens on its own path from the root; [PD] §5.4: the k drafts

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_fp8.restype = _i
         L.pa_decode_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _f,
                                     _f, _i, _p, _sz, _p]
+        L.pa_prefill_chunk_fp8.restype = _i
+        L.pa_prefill_chunk_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i,
+                                           _i, _i, _f, _f, _f, _p]
         L.pa_prefill_chunk_tree.restype = _i
         L.pa_prefill_chunk_tree.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p,
                                             _i, _i, _i, _i, _f, _p]
@@ -298,6 +301,31 @@ def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_len
                                   int(block_tables.shape[1]), seq_lens.data_ptr(),
                                   cu_q_lens.data_ptr(), S, tq, int(max_q_len), hq, float(scale),
                                   _stream(stream)))
+
+
+def prefill_chunk_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,
+                      max_q_len: int, scale: float, k_scale: float, v_scale: float,
+                      stream=None) -> None:
+    """pa_prefill_chunk_fp8: pa_prefill_chunk over E4M3 caches (uint8 or float8_e4m3fn;
+    elements = code value * k_scale / v_scale); query/out float16 or bfloat16."""
+    _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=True)
+    dt = _act_dtype(query, "query")
+    tq, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, query.dtype)
+        if tuple(t.shape) != (tq, hq, d):
+            raise ValueError(f"{n} must be [{tq}, {hq}, {d}]")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (cu_q_lens, "cu_q_lens")):
+        _gpu(t, n, torch.int32)
+    S = int(seq_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q_lens.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and cu_q_lens [S + 1]")
+    _check(lib().pa_prefill_chunk_fp8(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
+                                      k_cache.data_ptr(), v_cache.data_ptr(),
+                                      block_tables.data_ptr(), int(block_tables.shape[1]),
+                                      seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, tq,
+                                      int(max_q_len), hq, float(scale), float(k_scale),
+                                      float(v_scale), _stream(stream)))
 
 
 # ------------------------------------------------------------------------- E4M3 caches

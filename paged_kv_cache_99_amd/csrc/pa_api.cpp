@@ -460,7 +460,8 @@ pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_he
                          int32_t max_blocks_per_seq, const int32_t *seq_lens,
                          const int32_t *cu_q_lens, const uint64_t *tree_mask, bool tree,
                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                         int32_t num_q_heads, float scale, void *stream)
+                         int32_t num_q_heads, float scale, void *stream, bool fp8 = false,
+                         float k_scale = 1.0f, float v_scale = 1.0f)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -471,6 +472,10 @@ pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_he
     REQUIRE(max_q_len >= 0, "max_q_len %d < 0", max_q_len);
     if (tree)
         REQUIRE(max_q_len <= 64, "max_q_len %d > 64: a tree mask covers at most 64 rows", max_q_len);
+    if (fp8)
+        REQUIRE(good_scale(k_scale) && good_scale(v_scale),
+                "k_scale %g / v_scale %g is not a finite positive number", (double)k_scale,
+                (double)v_scale);
     REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
             "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
             num_kv_heads);
@@ -508,8 +513,11 @@ pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_he
     p.num_q_heads = num_q_heads;
     p.scale = scale;
     p.tree_mask = tree ? tree_mask : nullptr;
+    p.c.fp8 = fp8;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
     return launched(pa::launch_prefill(p, (hipStream_t)stream),
-                    tree ? "prefill_chunk_tree" : "prefill_chunk");
+                    tree ? "prefill_chunk_tree" : fp8 ? "prefill_chunk_fp8" : "prefill_chunk");
 }
 
 }  // namespace
@@ -527,6 +535,21 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
     return prefill_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
                         block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, nullptr, false,
                         num_seqs, total_q, max_q_len, num_q_heads, scale, stream);
+}
+
+pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                 int32_t head_dim, void *out, const void *query,
+                                 const void *k_cache, const void *v_cache,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                 int32_t num_q_heads, float scale, float k_scale, float v_scale,
+                                 void *stream)
+{
+    return prefill_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                        block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, nullptr, false,
+                        num_seqs, total_q, max_q_len, num_q_heads, scale, stream, true, k_scale,
+                        v_scale);
 }
 
 pa_status_t pa_prefill_chunk_tree(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,

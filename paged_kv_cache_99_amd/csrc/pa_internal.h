@@ -86,6 +86,9 @@ struct PrefillLaunch {
     int32_t max_q_len;
     int32_t num_q_heads;
     float scale;
+    // E4M3 caches (c.fp8): element = code value * k_scale / v_scale; query/out of dtype c.bf16
+    float k_scale = 1.0f;
+    float v_scale = 1.0f;
 };
 bool prefill_supported(int32_t head_dim, int32_t group);
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);

@@ -81,6 +81,7 @@ struct PrefillParams {
     int32_t n_items;
     int32_t total_q;
     float scale_log2;
+    float v_scale;  // E4M3 caches: value scale, applied to the output (k_scale is in scale_log2)
 };
 
 constexpr int kWaves = 8;                // waves per workgroup
@@ -108,7 +109,7 @@ __device__ __forceinline__ int swz(int r)
         return (r >> 1) & 7;
 }
 
-template <bool BF, int D, int GK, bool TREE>
+template <bool BF, int D, int GK, bool TREE, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 {
     constexpr int R = kPairs / GK;                  // query rows per workgroup
@@ -288,7 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const int v_dim = (g16 & 1) * 16 + 4 * v_q;      // dim within a 32-dim tile
 
     // a bfloat16 P needs its hi + lo split only while some row sees few keys (see kOnePartKeys)
-    const bool one_part = !BF || unmasked_below + 1 >= kOnePartKeys;
+    // (E4M3 caches take the plain loop, which stages their tiles through registers)
+    const bool one_part = !F8 && (!BF || unmasked_below + 1 >= kOnePartKeys);
     if (one_part && n_tiles > 0) {
         // ---------------------------------------------------------------- pipelined loop
         // Step t computes PV(t-1), QK(t+1) and the softmax of tile t. Tiles are loaded in pairs:
@@ -532,13 +534,70 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         (void)issue_span(One{}, p.k_cache, lds + b * TILEB, t);
         (void)issue_span(One{}, p.v_cache, lds + (4 + b) * TILEB, t);
     };
-    if (!one_part && n_tiles > 0)
-        issue(0, 0);
+    // E4M3 caches ([V1] §4.4: one byte per element): thread i stages the 16 codes of piece i % PPR
+    // of row i / PPR of a tile, for K and for V, through registers -- loaded while the previous
+    // tile is computed, then converted exactly to the 16-bit type (v_cvt_scalef32_pk_*_fp8) and
+    // written as the two 16-byte pieces of the same swizzled LDS rows the 16-bit path fills. A
+    // wave's rows lie in one paged block (8 or 16 rows, block aligned), so its block id is one
+    // scalar load. Rows past the context are not written (they keep finite values, as above).
+    constexpr int PPR = D / 16;                // 16-code pieces per row
+    constexpr int STAGERS = kKeys * PPR;       // threads that stage a tile
+    const int r8 = tid / PPR, c8 = tid % PPR;
+    const int row0_8 = __builtin_amdgcn_readfirstlane((wave * kWave) / PPR);  // the wave's first row
+    uint4 k8 = make_uint4(0, 0, 0, 0), v8 = k8;
+    bool have8 = false;
+    auto load8 = [&](int t) PA_INLINE {
+        have8 = false;
+        if (tid >= STAGERS || t * kKeys + row0_8 >= L)
+            return;
+        const int blk = table[(t * kKeys + row0_8) / kBlock];
+        const int key = t * kKeys + r8;
+        if ((unsigned)blk >= (unsigned)p.num_blocks || key >= L)
+            return;
+        const size_t off = (((size_t)blk * p.num_kv_heads + kvh) * kBlock + key % kBlock) * D +
+                           c8 * 16;
+        k8 = *(const uint4 *)((const uint8_t *)p.k_cache + off);
+        v8 = *(const uint4 *)((const uint8_t *)p.v_cache + off);
+        have8 = true;
+    };
+    auto store8 = [&](int b) PA_INLINE {
+        if (!have8)
+            return;
+        const int swr = swz<D>(r8);
+        auto put = [&](uint8_t *tile, const uint4 &w) PA_INLINE {
+            const uint4 lo = make_uint4(e4m3x2_to_pk16<BF, false>(w.x), e4m3x2_to_pk16<BF, true>(w.x),
+                                        e4m3x2_to_pk16<BF, false>(w.y), e4m3x2_to_pk16<BF, true>(w.y));
+            const uint4 hi = make_uint4(e4m3x2_to_pk16<BF, false>(w.z), e4m3x2_to_pk16<BF, true>(w.z),
+                                        e4m3x2_to_pk16<BF, false>(w.w), e4m3x2_to_pk16<BF, true>(w.w));
+            *(uint4 *)(tile + r8 * ROWB + (((2 * c8) ^ swr) << 4)) = lo;
+            *(uint4 *)(tile + r8 * ROWB + (((2 * c8 + 1) ^ swr) << 4)) = hi;
+        };
+        put(lds + b * TILEB, k8);
+        put(lds + (4 + b) * TILEB, v8);
+    };
+    // bfloat16 P in hi + lo parts while some row of the group sees fewer than kOnePartKeys keys
+    // (the 16-bit path reaches this loop only then; E4M3 caches also for longer rows)
+    const bool lo_part = BF && unmasked_below + 1 < kOnePartKeys;
+    if constexpr (F8) {
+        if (n_tiles > 0) {
+            load8(0);
+            store8(0);
+        }
+    } else {
+        if (!one_part && n_tiles > 0)
+            issue(0, 0);
+    }
     for (int t = 0; !one_part && t < n_tiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed in LDS
+        if constexpr (!F8)
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed in LDS
         __syncthreads();                // everyone's have; everyone is done with tile t-1
-        if (t + 1 < n_tiles)
-            issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
+        if constexpr (F8) {
+            if (t + 1 < n_tiles)
+                load8(t + 1);  // registers: converted into the other buffer after tile t
+        } else {
+            if (t + 1 < n_tiles)
+                issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
+        }
         const uint8_t *kb = lds + (t & 1) * TILEB;
         const uint8_t *vb = lds + (4 + (t & 1)) * TILEB;
         // the two 32-key halves are independent accumulator chains: interleave them so that no
@@ -604,7 +663,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                 const float p0 = s[kt][b + 2 * e], p1 = s[kt][b + 2 * e + 1];
                 hw[e] = pack2<BF>(p0, p1);
                 if constexpr (BF)
-                    lw[e] = pack2<BF>(p0 - lo_f32<BF>(hw[e]), p1 - hi_f32<BF>(hw[e]));
+                    if (lo_part)
+                        lw[e] = pack2<BF>(p0 - lo_f32<BF>(hw[e]), p1 - hi_f32<BF>(hw[e]));
             }
         }
 #pragma unroll
@@ -629,17 +689,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             for (int dt = 0; dt < DT; ++dt)
                 o[dt] = mfma32<BF>(a[dt], pb[c4], o[dt]);
             if constexpr (BF) {
+                if (lo_part) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    o[dt] = mfma32<BF>(a[dt], pl[c4], o[dt]);
+                    for (int dt = 0; dt < DT; ++dt)
+                        o[dt] = mfma32<BF>(a[dt], pl[c4], o[dt]);
+                }
             }
+        }
+        if constexpr (F8) {
+            // the other buffer was last read in step t-1, which every wave finished before the
+            // barrier of this step
+            if (t + 1 < n_tiles)
+                store8((t + 1) & 1);
         }
     }
 
     l_run = pair_sum(l_run);
     if (!row_ok)
         return;
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    const float inv = l_run > 0.0f ? (F8 ? p.v_scale : 1.0f) / l_run : 0.0f;
     uint16_t *dst = p.out + ((size_t)(q0 + row) * p.num_q_heads + head) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -653,25 +721,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
 }
 
 template <bool BF, int D, int GK>
-hipError_t launch_typed(const PrefillParams &p, hipStream_t stream)
+hipError_t launch_typed(const PrefillParams &p, bool fp8, hipStream_t stream)
 {
-    if (p.tree_mask)
-        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, true>), dim3(round_up8(p.n_items)),
+    if (fp8)
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, true>), dim3(round_up8(p.n_items)),
+                           dim3(kThreads), 0, stream, p);
+    else if (p.tree_mask)
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, true, false>), dim3(round_up8(p.n_items)),
                            dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false>), dim3(round_up8(p.n_items)),
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, false>), dim3(round_up8(p.n_items)),
                            dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <bool BF, int D>
-hipError_t launch_gk(int gk, const PrefillParams &p, hipStream_t stream)
+hipError_t launch_gk(int gk, const PrefillParams &p, bool fp8, hipStream_t stream)
 {
     switch (gk) {
-    case 8: return launch_typed<BF, D, 8>(p, stream);
-    case 4: return launch_typed<BF, D, 4>(p, stream);
-    case 2: return launch_typed<BF, D, 2>(p, stream);
-    default: return launch_typed<BF, D, 1>(p, stream);
+    case 8: return launch_typed<BF, D, 8>(p, fp8, stream);
+    case 4: return launch_typed<BF, D, 4>(p, fp8, stream);
+    case 2: return launch_typed<BF, D, 2>(p, fp8, stream);
+    default: return launch_typed<BF, D, 1>(p, fp8, stream);
     }
 }
 
@@ -710,12 +781,16 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
     if (items > 0x7ffffff0)
         return hipErrorInvalidValue;
     p.n_items = (int32_t)items;
-    p.scale_log2 = (float)((double)d.scale * 1.4426950408889634);
+    const bool fp8 = d.c.fp8;
+    if (fp8 && d.tree_mask)
+        return hipErrorInvalidValue;  // no tree mask over E4M3 caches
+    p.scale_log2 = (float)((double)d.scale * (fp8 ? (double)d.k_scale : 1.0) * 1.4426950408889634);
+    p.v_scale = fp8 ? d.v_scale : 1.0f;
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, stream)
-                                  : launch_gk<true, 128>(gk, p, stream);
-    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, stream)
-                              : launch_gk<false, 128>(gk, p, stream);
+        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, fp8, stream)
+                                  : launch_gk<true, 128>(gk, p, fp8, stream);
+    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, fp8, stream)
+                              : launch_gk<false, 128>(gk, p, fp8, stream);
 }
 
 }  // namespace pa

@@ -44,7 +44,7 @@ class GpuStep:
     kv_cache="fp8" keeps the caches as E4M3 codes (lecture 34 §4.4) with scales k_scale, v_scale:
     fp8_pool gives their initial bytes (numpy uint8, the pool layout); without it the 16-bit pool is
     quantized on the device by the library's own FP8 scatter, each slot being one token. Such a
-    step runs copy, scatter and decode (plain or shared-prefix); it has no prefill stage.
+    step runs every stage over the E4M3 caches (the *_fp8 entry points).
     """
 
     def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
@@ -161,8 +161,10 @@ class GpuStep:
 
     def prefill(self, stream=None):
         if self.pre_query.shape[0] and self.fp8:
-            raise ValueError("no prefill kernel reads E4M3 caches")
-        if self.pre_query.shape[0]:
+            binding.prefill_chunk_fp8(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
+                                      self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
+                                      self.w.scale, self.k_scale, self.v_scale, stream)
+        elif self.pre_query.shape[0]:
             binding.prefill_chunk(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
                                   self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
                                   self.w.scale, stream)

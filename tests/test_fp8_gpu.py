@@ -215,3 +215,72 @@ def test_shared_prefix_decode_is_deterministic_and_matches_plain():
     assert_attention_close(words_from_device(plain), ref, w.dtype, "fp8 plain decode",
                            strict=False)
     assert_attention_close(first, ref, w.dtype, "fp8 shared-prefix decode", strict=False)
+
+
+# --------------------------------------------------------------- chunked prefill, E4M3
+def run_fp8_prefill(w, ks, vs):
+    kc, vc = oracle_fp8_pool(w, ks, vs)
+    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(kc, vc))
+    print(f"[fp8] prefill {w.name}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} "
+          f"rows={w.query_prefill.shape[0]}", flush=True)
+    g.copy()
+    g.scatter()
+    g.decode()
+    g.prefill()
+    torch.cuda.synchronize()
+    kc, vc = oracle_fp8_after_step(w, kc, vc, ks, vs)
+    nd = w.n_decode
+    ref = oracle.prefill_fp8(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
+                             w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                             ks, vs)
+    return g, ref
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (16, 4), (32, 2), (6, 2), (12, 12)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_chunks(H_q, H_kv, D, dtype):
+    """Chunks of whole prompts (first rows see one key), chunks over cached context, a ragged
+    last row tile and a context ending mid-block, plus decodes in the same step."""
+    lens = [40, 700, 1300, 97, 16, 2049]
+    q_lens = [40, 129, 300, 1, 16, 64]
+    w = W.build([300, 1000] + lens, H_q, H_kv, D, dtype, seed=660 + H_q + D, n_decode=2,
+                q_lens=q_lens)
+    g, ref = run_fp8_prefill(w, 0.04, 0.025)
+    assert_attention_close(words_from_device(g.pre_out), ref, dtype,
+                           f"fp8 prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}", strict=False)
+
+
+def test_prefill_mixed_step_sampled():
+    """The 2048-token mixed step over E4M3 caches: every decode row, and sampled chunk rows
+    (first, last and random) against the oracle."""
+    w = W.named("chunked_prefill_mixed")
+    ks, vs = 0.03, 0.02
+    kc, vc = oracle_fp8_pool(w, ks, vs, poison=False)
+    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(kc, vc))
+    print("[fp8] mixed step", flush=True)
+    g.run()
+    torch.cuda.synchronize()
+    kc, vc = oracle_fp8_after_step(w, kc, vc, ks, vs)
+    nd = w.n_decode
+    ref_d = oracle.decode_fp8(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd],
+                              w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+    assert_attention_close(words_from_device(g.dec_out), ref_d, w.dtype, "fp8 mixed decode")
+    rng = np.random.default_rng(670)
+    tq = w.query_prefill.shape[0]
+    rows = sorted(set([0, tq - 1] + rng.integers(0, tq, 40).tolist()))
+    pairs = np.array([(r, h) for r in rows for h in range(w.H_q)], np.int32)
+    ref_p = oracle.prefill_fp8(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
+                               w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                               ks, vs, rows=pairs)
+    got = words_from_device(g.pre_out)[pairs[:, 0], pairs[:, 1]]
+    assert_attention_close(got, ref_p, w.dtype, "fp8 mixed prefill rows")
+
+
+def test_prefill_is_deterministic():
+    w = W.build([900, 2100], 32, 8, 128, "bf16", seed=680, n_decode=0, q_lens=[300, 200])
+    g, _ = run_fp8_prefill(w, 0.03, 0.02)
+    first = words_from_device(g.pre_out)
+    g.prefill()
+    torch.cuda.synchronize()
+    assert np.array_equal(first, words_from_device(g.pre_out))
