@@ -1,4 +1,5 @@
-"""A short serving loop on the GPU, driven by the library's native block manager.
+"""A short serving loop on the GPU, driven by the library's native block manager, over 16-bit and
+over E4M3 caches (lecture 34 "vLLM 生产级系统架构全景剖析" §4.4).
 
 Requests share a system prompt (prefix cache), one request forks into parallel samples (copy on
 write of its partly filled last block), requests finish and new ones reuse cached free blocks.
@@ -28,7 +29,9 @@ pytestmark = pytest.mark.gpu
 
 H_Q, H_KV, D, BLOCK = 8, 2, 128, 16
 NAN_WORD = {"f16": 0x7E00, "bf16": 0x7FC0}
+NAN_E4M3 = 0x7F
 TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
+KS, VS = 0.03, 0.02  # E4M3 cache scales
 _MOD = (1 << 61) - 1
 
 
@@ -56,10 +59,15 @@ class TokenRows:
         return np.stack(ks), np.stack(vs)
 
 
-def reference_attention(q_words, ids, upto, rows: TokenRows, dtype, scale):
-    """float64 [H_q][D]: the query of position upto-1 over contiguous rows 0..upto-1."""
+def reference_attention(q_words, ids, upto, rows: TokenRows, dtype, scale, fp8=False):
+    """float64 [H_q][D]: the query of position upto-1 over contiguous rows 0..upto-1 (with fp8,
+    the rows as E4M3 caches hold them: the codes of x / scale, times the scale)."""
     K, V = rows.rows(ids, 0, upto)
-    Kd, Vd = oracle.to_double(K, dtype), oracle.to_double(V, dtype)
+    if fp8:
+        Kd = oracle.e4m3_to_double(oracle.quantize_e4m3(K, dtype, KS)) * KS
+        Vd = oracle.e4m3_to_double(oracle.quantize_e4m3(V, dtype, VS)) * VS
+    else:
+        Kd, Vd = oracle.to_double(K, dtype), oracle.to_double(V, dtype)
     qd = oracle.to_double(q_words, dtype)
     g = H_Q // H_KV
     return np.stack([oracle.attention(qd[h], np.ascontiguousarray(Kd[:, h // g]),
@@ -68,17 +76,20 @@ def reference_attention(q_words, ids, upto, rows: TokenRows, dtype, scale):
 
 
 class Loop:
-    def __init__(self, dtype, num_blocks, seed):
-        self.dtype, self.nb = dtype, num_blocks
+    def __init__(self, dtype, num_blocks, seed, fp8=False):
+        self.dtype, self.nb, self.fp8 = dtype, num_blocks, fp8
         self.rng = np.random.default_rng(seed)
         order = self.rng.permutation(num_blocks)
         self.native = BlockManager(num_blocks, order, prefix_caching=True)
         self.ref = OracleBlockManager(num_blocks, order, prefix_caching=True)
         n = num_blocks * H_KV * BLOCK * D
-        self.kc_ref = np.full(n, NAN_WORD[dtype], np.uint16)   # slots never written stay NaN
+        if fp8:
+            self.kc_ref = np.full(n, NAN_E4M3, np.uint8)        # slots never written stay NaN
+            self.kc = torch.from_numpy(self.kc_ref.copy()).cuda()
+        else:
+            self.kc_ref = np.full(n, NAN_WORD[dtype], np.uint16)
+            self.kc = torch.from_numpy(self.kc_ref.view(np.int16).copy()).view(TORCH[dtype]).cuda()
         self.vc_ref = self.kc_ref.copy()
-        tdt = TORCH[dtype]
-        self.kc = torch.from_numpy(self.kc_ref.view(np.int16).copy()).view(tdt).cuda()
         self.kc = self.kc.view(num_blocks, H_KV, BLOCK, D)
         self.vc = self.kc.clone()
         self.rows = TokenRows(dtype)
@@ -97,8 +108,8 @@ class Loop:
         if pairs:
             m = np.array(pairs, np.int32)
             binding.copy_blocks(self.kc, self.vc, self.i32(m))
-            self.kc_ref, self.vc_ref = oracle.copy_blocks(self.kc_ref, self.vc_ref, m, self.nb,
-                                                          H_KV, D)
+            copy = oracle.copy_blocks_fp8 if self.fp8 else oracle.copy_blocks
+            self.kc_ref, self.vc_ref = copy(self.kc_ref, self.vc_ref, m, self.nb, H_KV, D)
         ks, vs, slots = [], [], []
         for sid, p0, sl in toks:
             k, v = self.rows.rows(self.ids[sid], p0, p0 + len(sl))
@@ -108,9 +119,16 @@ class Loop:
         if not slots:
             return
         K, V, S = np.concatenate(ks), np.concatenate(vs), np.array(slots, np.int32)
-        binding.reshape_and_cache(self.dev_words(K), self.dev_words(V), self.kc, self.vc, self.i32(S))
-        self.kc_ref, self.vc_ref = oracle.reshape_and_cache(K, V, self.kc_ref, self.vc_ref, S,
-                                                            self.nb, H_KV, D)
+        if self.fp8:
+            binding.reshape_and_cache_fp8(self.dev_words(K), self.dev_words(V), self.kc, self.vc,
+                                          self.i32(S), KS, VS)
+            self.kc_ref, self.vc_ref = oracle.reshape_and_cache_fp8(
+                K, V, self.kc_ref, self.vc_ref, S, self.nb, H_KV, D, self.dtype, KS, VS)
+        else:
+            binding.reshape_and_cache(self.dev_words(K), self.dev_words(V), self.kc, self.vc,
+                                      self.i32(S))
+            self.kc_ref, self.vc_ref = oracle.reshape_and_cache(K, V, self.kc_ref, self.vc_ref, S,
+                                                                self.nb, H_KV, D)
 
     def both(self, fn, *args):
         a = getattr(self.native, fn)(*args)
@@ -145,12 +163,15 @@ class Loop:
         q = f32_to_words(self.rng.standard_normal((int(cu[-1]), H_Q, D), dtype=np.float32),
                          self.dtype)
         out = torch.empty((int(cu[-1]), H_Q, D), dtype=TORCH[self.dtype], device="cuda")
-        binding.prefill_chunk(out, self.dev_words(q), self.kc, self.vc, self.i32(self.tables(sids)),
-                              self.i32([n for _, _, n in rows]), self.i32(cu), max(q_lens),
-                              self.scale)
+        args = (out, self.dev_words(q), self.kc, self.vc, self.i32(self.tables(sids)),
+                self.i32([n for _, _, n in rows]), self.i32(cu), max(q_lens), self.scale)
+        if self.fp8:
+            binding.prefill_chunk_fp8(*args, KS, VS)
+        else:
+            binding.prefill_chunk(*args)
         got = out.cpu().view(torch.int16).numpy().view(np.uint16)
         ref = np.stack([reference_attention(q[cu[i] + j], self.ids[sid], h + j + 1, self.rows,
-                                            self.dtype, self.scale)
+                                            self.dtype, self.scale, self.fp8)
                         for i, (sid, h, n) in enumerate(rows) for j in range(n - h)])
         self.check_pools()
         assert_attention_close(got, ref, self.dtype, f"prefill {sids}", strict=False)
@@ -171,11 +192,16 @@ class Loop:
         q = f32_to_words(self.rng.standard_normal((len(sids), H_Q, D), dtype=np.float32),
                          self.dtype)
         out = torch.empty((len(sids), H_Q, D), dtype=TORCH[self.dtype], device="cuda")
-        binding.decode(out, self.dev_words(q), self.kc, self.vc, self.i32(self.tables(sids)),
-                       self.i32(lens), max(lens), self.scale, partition_size=partition_size)
+        if self.fp8:
+            binding.decode_fp8(out, self.dev_words(q), self.kc, self.vc, self.i32(self.tables(sids)),
+                               self.i32(lens), max(lens), self.scale, KS, VS,
+                               partition_size=partition_size)
+        else:
+            binding.decode(out, self.dev_words(q), self.kc, self.vc, self.i32(self.tables(sids)),
+                           self.i32(lens), max(lens), self.scale, partition_size=partition_size)
         got = out.cpu().view(torch.int16).numpy().view(np.uint16)
         ref = np.stack([reference_attention(q[i], self.ids[s], lens[i], self.rows, self.dtype,
-                                            self.scale) for i, s in enumerate(sids)])
+                                            self.scale, self.fp8) for i, s in enumerate(sids)])
         self.check_pools()
         assert_attention_close(got, ref, self.dtype, f"decode {sids}", strict=False)
         return len(pairs)
@@ -183,7 +209,10 @@ class Loop:
     def check_pools(self):
         torch.cuda.synchronize()
         for dev, ref in ((self.kc, self.kc_ref), (self.vc, self.vc_ref)):
-            words = dev.cpu().view(torch.int16).numpy().view(np.uint16).ravel()
+            if self.fp8:
+                words = dev.cpu().numpy().ravel()
+            else:
+                words = dev.cpu().view(torch.int16).numpy().view(np.uint16).ravel()
             assert np.array_equal(words, ref), "pool differs from the oracle's"
 
     def fork(self, parent, child):
@@ -195,10 +224,11 @@ class Loop:
         del self.ids[sid]
 
 
-@pytest.mark.parametrize("dtype,partition_size", [("f16", 0), ("bf16", 32)])
-def test_serving_loop_with_native_block_manager(dtype, partition_size):
-    print(f"[serving loop] dtype={dtype} partition={partition_size}", flush=True)
-    L = Loop(dtype, num_blocks=64, seed=5)
+@pytest.mark.parametrize("dtype,partition_size,kv", [("f16", 0, "auto"), ("bf16", 32, "auto"),
+                                                     ("f16", 32, "fp8"), ("bf16", 0, "fp8")])
+def test_serving_loop_with_native_block_manager(dtype, partition_size, kv):
+    print(f"[serving loop] dtype={dtype} partition={partition_size} kv={kv}", flush=True)
+    L = Loop(dtype, num_blocks=64, seed=5, fp8=kv == "fp8")
     system = [int(x) for x in L.rng.integers(0, 50, 40)]      # 2.5 blocks of shared prompt
     qs = [[int(x) for x in L.rng.integers(0, 50, n)] for n in (9, 23, 4, 17)]
     hits = L.admit([(0, system + qs[0]), (1, system + qs[1])])
