@@ -8,13 +8,14 @@
 // consumed tile by tile with a running max and sum (devpress.csdn.net/amd vLLM overview §9 (3)(4):
 // query and key/value tiling with online softmax).
 //
-// Tiling. A workgroup of 4 waves owns 128 (query row, query head) pairs of one kv-head group: the
-// GK heads that share the kv head, for 128/GK consecutive rows, so each K/V tile staged in LDS serves
+// Tiling. A workgroup of 8 waves owns 256 (query row, query head) pairs of one kv-head group: the
+// GK heads that share the kv head, for 256/GK consecutive rows, so each K/V tile staged in LDS serves
 // every head of the group. Per 64-key tile (4 paged blocks):
-//   - K and V rows go to LDS untouched, straight from HBM (global_load_lds_dwordx4: no staging
-//     registers), into one of two buffers while the other is computed. Rows are stored without
-//     padding; the 16-byte pieces of row r are XOR-swizzled (piece c at c ^ swz(r)) so that the
-//     column reads below hit distinct banks.
+//   - 16-bit K and V rows go to LDS untouched, straight from HBM (global_load_lds_dwordx4: no
+//     staging registers), into buffers that are filled while others are computed. Rows are stored
+//     without padding; the 16-byte pieces of row r are XOR-swizzled (piece c at c ^ swz(r)) so that
+//     the column reads below hit distinct banks. E4M3 rows pass through registers instead, where
+//     they are converted exactly to the query's 16-bit type, and land in the same LDS layout.
 //   - Each wave computes S^T = K Q^T for its 32 pairs with v_mfma_f32_32x32x16 (A = 32 keys x 16
 //     dims, one ds_read_b128 per lane; B = Q^T held in registers for the whole kernel).
 //   - Online softmax in the accumulator layout: lane l holds column l%32 (one pair) and 16 keys per
@@ -29,13 +30,13 @@
 // beyond the context are never loaded; LDS starts zeroed, so such slots hold finite stale values that
 // meet zero probabilities (no NaN reaches an MFMA).
 //
-// Two tile loops. Where every row of the workgroup attends at least kOnePartKeys keys, the loop is
-// software-pipelined so that the matrix cores and the vector ALUs work at once: while the softmax
-// of tile t runs on the VALU, the MFMAs of S^T for tile t+1 and of O^T += V^T P^T for tile t-1 are
-// in flight (K and V have separate double buffers: K runs two tiles ahead of V). P is rounded to
-// the 16-bit type in one part there. Rows with fewer keys -- the first rows of a prompt, where a
-// handful of keys can dominate and cancel -- take the plain loop, which splits a bfloat16 P into
-// hi + lo parts.
+// Two tile loops. The main loop is software-pipelined so that the matrix cores and the vector ALUs
+// work at once: while the softmax of tile t runs on the VALU, the MFMAs of S^T for tile t+1 and of
+// O^T += V^T P^T for tile t-1 are in flight (K and V have four LDS slots each: K runs two tiles
+// ahead of V). P is rounded to the 16-bit type in one part there. fp16 queries always take it;
+// bfloat16 ones where every row of the workgroup attends at least kOnePartKeys keys. Rows with fewer
+// keys -- the first rows of a prompt, where a handful of keys can dominate and cancel -- take the
+// plain loop, which splits a bfloat16 P into hi + lo parts.
 #include <math.h>
 
 #include <type_traits>
@@ -288,9 +289,41 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const int v_half = g16 >> 1;                     // lane half h of the destination lanes
     const int v_dim = (g16 & 1) * 16 + 4 * v_q;      // dim within a 32-dim tile
 
+    // E4M3 caches ([V1] §4.4: one byte per element) are staged through registers: thread i loads
+    // the 16 codes of piece i % PPR of row i / PPR of a 64-key tile, converts them exactly to the
+    // 16-bit type (v_cvt_scalef32_pk_*_fp8) and writes them as the two 16-byte pieces of the same
+    // swizzled LDS row the 16-bit path fills. A wave's rows lie in one paged block (8 or 16 rows,
+    // block aligned), so its block id is one scalar load. Rows past the context are not written
+    // (they keep finite values, as above).
+    constexpr int PPR = D / 16;                // 16-code pieces per row
+    constexpr int STAGERS = kKeys * PPR;       // threads that stage a tile
+    const int r8 = tid / PPR, c8 = tid % PPR;
+    const int row0_8 = __builtin_amdgcn_readfirstlane((wave * kWave) / PPR);  // the wave's first row
+    // this thread's codes of tile t of one cache; false where its row holds no token
+    auto load_codes = [&](const uint16_t *cache, int t, uint4 &dst) PA_INLINE -> bool {
+        if (tid >= STAGERS || t * kKeys + row0_8 >= L)
+            return false;
+        const int blk = table[(t * kKeys + row0_8) / kBlock];
+        const int key = t * kKeys + r8;
+        if ((unsigned)blk >= (unsigned)p.num_blocks || key >= L)
+            return false;
+        const size_t off = (((size_t)blk * p.num_kv_heads + kvh) * kBlock + key % kBlock) * D +
+                           c8 * 16;
+        dst = *(const uint4 *)((const uint8_t *)cache + off);
+        return true;
+    };
+    auto put_codes = [&](uint8_t *tile, const uint4 &w) PA_INLINE {
+        const int swr = swz<D>(r8);
+        const uint4 lo = make_uint4(e4m3x2_to_pk16<BF, false>(w.x), e4m3x2_to_pk16<BF, true>(w.x),
+                                    e4m3x2_to_pk16<BF, false>(w.y), e4m3x2_to_pk16<BF, true>(w.y));
+        const uint4 hi = make_uint4(e4m3x2_to_pk16<BF, false>(w.z), e4m3x2_to_pk16<BF, true>(w.z),
+                                    e4m3x2_to_pk16<BF, false>(w.w), e4m3x2_to_pk16<BF, true>(w.w));
+        *(uint4 *)(tile + r8 * ROWB + (((2 * c8) ^ swr) << 4)) = lo;
+        *(uint4 *)(tile + r8 * ROWB + (((2 * c8 + 1) ^ swr) << 4)) = hi;
+    };
+
     // a bfloat16 P needs its hi + lo split only while some row sees few keys (see kOnePartKeys)
-    // (E4M3 caches take the plain loop, which stages their tiles through registers)
-    const bool one_part = !F8 && (!BF || unmasked_below + 1 >= kOnePartKeys);
+    const bool one_part = !BF || unmasked_below + 1 >= kOnePartKeys;
     if (one_part && n_tiles > 0) {
         // ---------------------------------------------------------------- pipelined loop
         // Step t computes PV(t-1), QK(t+1) and the softmax of tile t. Tiles are loaded in pairs:
@@ -445,12 +478,46 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         float alpha_prev = 1.0f;
         bool rescale = false;
 
+        // E4M3: the codes staged at an odd step (K tiles 2v+2, 2v+3, V tiles 2v, 2v+1 for v =
+        // (t+1)/2) are converted into their slots at the next odd step, before its barrier: by
+        // then no wave reads those slots (their previous tiles were last read two steps before)
+        uint4 sk[2], sv[2];
+        bool okk[2] = {false, false}, okv[2] = {false, false};
+        int staged_v = 0;
+        auto stage = [&](int v) PA_INLINE {
+            staged_v = v;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                okk[i] = 2 * v + 2 + i < n_tiles && load_codes(p.k_cache, 2 * v + 2 + i, sk[i]);
+                okv[i] = 2 * v + i < n_tiles && load_codes(p.v_cache, 2 * v + i, sv[i]);
+            }
+        };
+        auto write_staged = [&]() PA_INLINE {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (okk[i])
+                    put_codes(kslot(2 * staged_v + 2 + i), sk[i]);
+                if (okv[i])
+                    put_codes(vslot(2 * staged_v + i), sv[i]);
+            }
+        };
+
         // K tiles 0..3 and V tiles 0, 1 before step 0; QK(0) needs K tiles 0, 1 only
-        (void)issue_span(Two{}, p.k_cache, kslot(0), 0);
-        const int c1 = n_tiles > 2 ? issue_span(Two{}, p.k_cache, kslot(2), 1) : 0;
-        const int c2 = issue_span(Two{}, p.v_cache, vslot(0), 0);
-        wait_loads(c1 + c2);
-        __syncthreads();
+        if constexpr (F8) {
+            uint4 c;
+            if (load_codes(p.k_cache, 0, c))
+                put_codes(kslot(0), c);
+            if (n_tiles > 1 && load_codes(p.k_cache, 1, c))
+                put_codes(kslot(1), c);
+            stage(0);
+            __syncthreads();
+        } else {
+            (void)issue_span(Two{}, p.k_cache, kslot(0), 0);
+            const int c1 = n_tiles > 2 ? issue_span(Two{}, p.k_cache, kslot(2), 1) : 0;
+            const int c2 = issue_span(Two{}, p.v_cache, vslot(0), 0);
+            wait_loads(c1 + c2);
+            __syncthreads();
+        }
         qk(std::integral_constant<int, 0>{}, std::integral_constant<int, DC>{}, sa,
            lds0 + k_lane);
 
@@ -461,12 +528,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                         const uint4 (&p_in)[4], uint4 (&p_out)[4]) PA_INLINE {
             if constexpr (decltype(par)::value == 1) {
                 const int u = t >> 1;  // t = 2u + 1
-                wait_loads(0);         // K tiles 2u+2, 2u+3 and V tiles 2u, 2u+1 landed
-                __syncthreads();       // for every wave; every wave is done with step t-1
-                if (2 * u + 4 < n_tiles)
-                    (void)issue_span(Two{}, p.k_cache, kslot(2 * u + 4), u + 2);
-                if (2 * u + 2 < n_tiles)
-                    (void)issue_span(Two{}, p.v_cache, vslot(2 * u + 2), u + 1);
+                if constexpr (F8) {
+                    write_staged();    // K tiles 2u+2, 2u+3 and V tiles 2u, 2u+1
+                    __syncthreads();
+                    stage(u + 1);      // K tiles 2u+4, 2u+5 and V tiles 2u+2, 2u+3
+                } else {
+                    wait_loads(0);     // K tiles 2u+2, 2u+3 and V tiles 2u, 2u+1 landed
+                    __syncthreads();   // for every wave; every wave is done with step t-1
+                    if (2 * u + 4 < n_tiles)
+                        (void)issue_span(Two{}, p.k_cache, kslot(2 * u + 4), u + 2);
+                    if (2 * u + 2 < n_tiles)
+                        (void)issue_span(Two{}, p.v_cache, vslot(2 * u + 2), u + 1);
+                }
             }
             if (rescale) {
 #pragma unroll
@@ -513,7 +586,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         };
         run(std::false_type{}, t_mask);
         run(std::true_type{}, n_tiles);
-        wait_loads(0);
+        if constexpr (F8)
+            write_staged();  // V tile n_tiles-1 may be among them
+        else
+            wait_loads(0);
         __syncthreads();
         if (rescale) {
 #pragma unroll
@@ -534,58 +610,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         (void)issue_span(One{}, p.k_cache, lds + b * TILEB, t);
         (void)issue_span(One{}, p.v_cache, lds + (4 + b) * TILEB, t);
     };
-    // E4M3 caches ([V1] §4.4: one byte per element): thread i stages the 16 codes of piece i % PPR
-    // of row i / PPR of a tile, for K and for V, through registers -- loaded while the previous
-    // tile is computed, then converted exactly to the 16-bit type (v_cvt_scalef32_pk_*_fp8) and
-    // written as the two 16-byte pieces of the same swizzled LDS rows the 16-bit path fills. A
-    // wave's rows lie in one paged block (8 or 16 rows, block aligned), so its block id is one
-    // scalar load. Rows past the context are not written (they keep finite values, as above).
-    constexpr int PPR = D / 16;                // 16-code pieces per row
-    constexpr int STAGERS = kKeys * PPR;       // threads that stage a tile
-    const int r8 = tid / PPR, c8 = tid % PPR;
-    const int row0_8 = __builtin_amdgcn_readfirstlane((wave * kWave) / PPR);  // the wave's first row
+    // E4M3 staging of the plain loop: this thread's K and V codes of the next tile
     uint4 k8 = make_uint4(0, 0, 0, 0), v8 = k8;
     bool have8 = false;
     auto load8 = [&](int t) PA_INLINE {
-        have8 = false;
-        if (tid >= STAGERS || t * kKeys + row0_8 >= L)
-            return;
-        const int blk = table[(t * kKeys + row0_8) / kBlock];
-        const int key = t * kKeys + r8;
-        if ((unsigned)blk >= (unsigned)p.num_blocks || key >= L)
-            return;
-        const size_t off = (((size_t)blk * p.num_kv_heads + kvh) * kBlock + key % kBlock) * D +
-                           c8 * 16;
-        k8 = *(const uint4 *)((const uint8_t *)p.k_cache + off);
-        v8 = *(const uint4 *)((const uint8_t *)p.v_cache + off);
-        have8 = true;
+        have8 = load_codes(p.k_cache, t, k8);
+        if (have8)
+            (void)load_codes(p.v_cache, t, v8);
     };
     auto store8 = [&](int b) PA_INLINE {
-        if (!have8)
-            return;
-        const int swr = swz<D>(r8);
-        auto put = [&](uint8_t *tile, const uint4 &w) PA_INLINE {
-            const uint4 lo = make_uint4(e4m3x2_to_pk16<BF, false>(w.x), e4m3x2_to_pk16<BF, true>(w.x),
-                                        e4m3x2_to_pk16<BF, false>(w.y), e4m3x2_to_pk16<BF, true>(w.y));
-            const uint4 hi = make_uint4(e4m3x2_to_pk16<BF, false>(w.z), e4m3x2_to_pk16<BF, true>(w.z),
-                                        e4m3x2_to_pk16<BF, false>(w.w), e4m3x2_to_pk16<BF, true>(w.w));
-            *(uint4 *)(tile + r8 * ROWB + (((2 * c8) ^ swr) << 4)) = lo;
-            *(uint4 *)(tile + r8 * ROWB + (((2 * c8 + 1) ^ swr) << 4)) = hi;
-        };
-        put(lds + b * TILEB, k8);
-        put(lds + (4 + b) * TILEB, v8);
+        if (have8) {
+            put_codes(lds + b * TILEB, k8);
+            put_codes(lds + (4 + b) * TILEB, v8);
+        }
     };
-    // bfloat16 P in hi + lo parts while some row of the group sees fewer than kOnePartKeys keys
-    // (the 16-bit path reaches this loop only then; E4M3 caches also for longer rows)
-    const bool lo_part = BF && unmasked_below + 1 < kOnePartKeys;
-    if constexpr (F8) {
-        if (n_tiles > 0) {
+    // bfloat16 P in hi + lo parts: this loop runs only while some row of the group sees fewer
+    // than kOnePartKeys keys
+    constexpr bool lo_part = BF;
+    if (!one_part && n_tiles > 0) {
+        if constexpr (F8) {
             load8(0);
             store8(0);
-        }
-    } else {
-        if (!one_part && n_tiles > 0)
+        } else {
             issue(0, 0);
+        }
     }
     for (int t = 0; !one_part && t < n_tiles; ++t) {
         if constexpr (!F8)
