@@ -14,6 +14,10 @@ Prints ONE JSON line:
                against the 8 TB/s HBM peak; traffic from the committed rocprofv3 counter summary
                when it was taken on the current decode source, else null;
   cpu_baseline the CPU oracle (float64) timed on this host over the full decode of the workload.
+  decode_ms, prefill_ms: mean of the per-call event times (their 10th/50th/90th percentiles
+               beside them). Decode contexts are far larger than the 256 MB Infinity Cache, so each
+               step reads them from HBM; --evict-mb 512 also displaces every cache level before
+               each timed decode, to show that.
 
 Algorithmic bytes (what the method must move, per stage; E = 2 bytes per cache element, 1 with
 --kv-cache fp8, whose caches hold E4M3 codes):
@@ -185,13 +189,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
                     help="after timing, copy PAIRS whole blocks with pa_copy_blocks (a plain copy of "
                          "known size, for scaling HBM byte counters)")
+    ap.add_argument("--evict-mb", type=int, default=0, metavar="MB",
+                    help="read an MB-megabyte buffer before each timed decode (outside the decode "
+                         "events, inside the step time) so that no cache level holds K/V rows from "
+                         "the previous step; 512 exceeds the 256 MB Infinity Cache twice over")
     args = ap.parse_args()
     if args.print_decode_src_hash:
         print(src_hash(DECODE_SRCS))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the hot path is not sharded across GPUs in this build "
+        print("bench.py measures one GPU: the library does not shard the hot path across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -224,11 +232,17 @@ def main():
     evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     has_prefill = g.pre_query.shape[0] > 0
+    # eviction by reading: a write would leave dirty lines whose write-back competes with the
+    # decode's reads
+    evict = (torch.zeros(args.evict_mb << 18, dtype=torch.int32, device="cuda")
+             if args.evict_mb > 0 else None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         g.copy()
         g.scatter()
+        if evict is not None:
+            torch.amax(evict)
         ev[i][0].record(stream)
         g.decode()
         ev[i][1].record(stream)
@@ -239,8 +253,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if g.n_decode else 0.0
-    pre_ms = float(np.mean([a.elapsed_time(b) for a, b in evp])) if has_prefill else 0.0
+    dec_t = [a.elapsed_time(b) for a, b in ev] if g.n_decode else [0.0]
+    pre_t = [a.elapsed_time(b) for a, b in evp] if has_prefill else [0.0]
+    dec_ms = float(np.mean(dec_t))
+    pre_ms = float(np.mean(pre_t))
 
     if args.copy_calibration:
         calibration_copy(g, args.copy_calibration)
@@ -279,9 +295,11 @@ def main():
             "prefill_rows": int(g.pre_query.shape[0]),
             "shared_prefix_read_once": bool(g.shared_prefix),
             "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
+            "evict_mb": args.evict_mb,
         },
         "decode_tokens_per_s": round(w.n_decode / (ms_per_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 5),
+        "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_t, [10, 50, 90])],
         "decode_GBps": round(dec_gbs, 2),
         "pct_of_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -303,6 +321,8 @@ def main():
         out["decode_GBps_logical"] = round(d_bytes / (dec_ms * 1e-3) / 1e9, 2)
     if has_prefill:
         out["prefill_ms"] = round(pre_ms, 5)
+        out["prefill_ms_p10_p50_p90"] = [round(float(x), 5)
+                                         for x in np.percentile(pre_t, [10, 50, 90])]
         out["prefill_TFLOPs"] = round(p_flops / (pre_ms * 1e-3) / 1e12, 2)
         out["prefill_mfma_frac"] = round(p_flops / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     if not args.no_cpu_baseline:
