@@ -10,7 +10,8 @@ single-layer decode: 64 sequences of U{512..4096} tokens, 32 query = 32 kv heads
 Prints ONE JSON line:
   value        algorithmic bytes of the whole step / time per step (GB/s), inputs resident in HBM;
   roofline     for the dominant kernel (decode): algorithmic bytes per launch / its average
-               duration from HIP events recorded on the launch stream during the timed steps,
+               duration from HIP events recorded on the launch stream during the timed steps
+               (timing-only events without the system-scope fence, see TimingEvents),
                against the 8 TB/s HBM peak; traffic from the committed rocprofv3 counter summary
                when it was taken on the current decode source, else null;
   cpu_baseline the CPU oracle (float64) timed on this host over the full decode of the workload.
@@ -151,6 +152,55 @@ def cpu_baseline(w, max_seconds, fp8=None):
             "seconds": round(elapsed, 3)}
 
 
+class TimingEvents:
+    """Pairs of HIP timing events created with hipEventDisableSystemFence (hip_runtime_api.h).
+
+    Recording a default event adds a system-scope release and acquire: a cache writeback and
+    invalidation between the measured kernels and the work around them, which costs several
+    microseconds per event and slows what follows. These events only write timestamps. They come
+    from the HIP runtime torch has loaded (soname libamdhip64.so.7), the one the library runs on.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, pairs):
+        import ctypes
+        self._ct = ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = hip
+        self._ev = []
+        for _ in range(2 * pairs):
+            e = ctypes.c_void_p()
+            self._check(hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE),
+                        "hipEventCreateWithFlags")
+            self._ev.append(e)
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError_t {rc}")
+
+    def record(self, i, end, stream):
+        """Record the start (end=False) or end event of pair i on a torch stream."""
+        self._check(self._hip.hipEventRecord(self._ev[2 * i + int(end)], stream.cuda_stream),
+                    "hipEventRecord")
+
+    def elapsed_ms(self, i):
+        """Milliseconds between the two events of pair i (both must have completed)."""
+        ms = self._ct.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._ct.byref(ms), self._ev[2 * i],
+                                                  self._ev[2 * i + 1]), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def close(self):
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
+
+
 def calibration_copy(g, pairs):
     """Copy `pairs` blocks src = 0..pairs-1 -> dst = pairs..2*pairs-1 in both caches (the timed steps
     are over; the pool contents no longer matter) and report the bytes a perfect copy moves."""
@@ -227,10 +277,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    ev = TimingEvents(K)   # decode call of each step
+    evp = TimingEvents(K)  # prefill call of each step
     has_prefill = g.pre_query.shape[0] > 0
     # eviction by reading: a write would leave dirty lines whose write-back competes with the
     # decode's reads
@@ -243,18 +291,20 @@ def main():
         g.scatter()
         if evict is not None:
             torch.amax(evict)
-        ev[i][0].record(stream)
+        ev.record(i, False, stream)
         g.decode()
-        ev[i][1].record(stream)
+        ev.record(i, True, stream)
         if has_prefill:
-            evp[i][0].record(stream)
+            evp.record(i, False, stream)
             g.prefill()
-            evp[i][1].record(stream)
+            evp.record(i, True, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
-    dec_t = [a.elapsed_time(b) for a, b in ev] if g.n_decode else [0.0]
-    pre_t = [a.elapsed_time(b) for a, b in evp] if has_prefill else [0.0]
+    dec_t = [ev.elapsed_ms(i) for i in range(K)] if g.n_decode else [0.0]
+    pre_t = [evp.elapsed_ms(i) for i in range(K)] if has_prefill else [0.0]
+    ev.close()
+    evp.close()
     dec_ms = float(np.mean(dec_t))
     pre_ms = float(np.mean(pre_t))
 
