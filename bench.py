@@ -111,8 +111,21 @@ def committed_traffic(per_launch_algorithmic):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, max_seconds, fp8=None):
-    """Time the float64 oracle over the workload's decode (a bounded sample when it is long).
+    """Time the float64 oracle over the workload's decode (a bounded sample when it is long), on
+    every host thread, then on one thread over a sample of a quarter of that time.
     fp8 = (k_scale, v_scale): the oracle's E4M3 decode over its own quantization of the pool."""
     import oracle
     nd = w.n_decode
@@ -122,34 +135,42 @@ def cpu_baseline(w, max_seconds, fp8=None):
         esize = 1
         k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, fp8[0])
         v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, fp8[1])
-    order = np.arange(nd)
-    # grow the sample by whole sequences until the next one would pass max_seconds of wall time
-    done_tokens, elapsed, n_seq = 0, 0.0, 0
-    t0 = time.perf_counter()
-    while n_seq < nd:
-        take = order[n_seq:n_seq + max(1, nd // 8)]
-        pairs = np.array([(s, h) for s in take for h in range(w.H_q)], np.int32)
-        if fp8 is None:
-            oracle.decode(w.query_decode, w.k_cache, w.v_cache, w.block_tables[:nd],
-                          w.seq_lens[:nd], w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
-                          pairs=pairs, nthreads=threads)
-        else:
-            oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd],
-                              w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, fp8[0], fp8[1],
-                              pairs=pairs, nthreads=threads)
-        n_seq += len(take)
-        done_tokens += int(np.sum(w.seq_lens[take]))
-        elapsed = time.perf_counter() - t0
-        if elapsed > max_seconds:
-            break
-    nbytes = done_tokens * 2 * w.H_kv * w.D * esize + 2 * n_seq * w.H_q * w.D * 2
+
+    def timed(nthreads, seconds, step):
+        # grow the sample by whole sequences until the next batch would pass `seconds`
+        done_tokens, elapsed, n_seq = 0, 0.0, 0
+        t0 = time.perf_counter()
+        while n_seq < nd:
+            take = np.arange(n_seq, min(nd, n_seq + step))
+            pairs = np.array([(s, h) for s in take for h in range(w.H_q)], np.int32)
+            if fp8 is None:
+                oracle.decode(w.query_decode, w.k_cache, w.v_cache, w.block_tables[:nd],
+                              w.seq_lens[:nd], w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype,
+                              w.scale, pairs=pairs, nthreads=nthreads)
+            else:
+                oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd],
+                                  w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, fp8[0],
+                                  fp8[1], pairs=pairs, nthreads=nthreads)
+            n_seq += len(take)
+            done_tokens += int(np.sum(w.seq_lens[take]))
+            elapsed = time.perf_counter() - t0
+            if elapsed > seconds:
+                break
+        nbytes = done_tokens * 2 * w.H_kv * w.D * esize + 2 * n_seq * w.H_q * w.D * 2
+        return n_seq, done_tokens, nbytes, elapsed
+
+    n_seq, done_tokens, nbytes, elapsed = timed(threads, max_seconds, max(1, nd // 8))
+    n1, _, b1, e1 = timed(1, max_seconds / 4, 1)
     what = "E4M3 decode" if fp8 is not None else "decode"
     return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"float64 oracle {what} of {n_seq} of {nd} sequences x {w.H_q} query heads "
                       f"({done_tokens} context tokens, {nbytes / 1e9:.3f} GB of K/V) in "
                       f"{elapsed:.2f} s, pool before the step's scatter",
-            "seconds": round(elapsed, 3)}
+            "seconds": round(elapsed, 3),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(b1 / e1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{n1} of {nd} sequences in {e1:.2f} s"}}
 
 
 class TimingEvents:
