@@ -85,6 +85,11 @@ __device__ __forceinline__ int unit_start(const DecodeParams &p, int seq, int L)
     return p.seq_starts ? min(max(p.seq_starts[seq], 0), L) : 0;
 }
 
+// Lazy reference point of the running softmax: a row's running maximum moves (and its sums are
+// rescaled) only when a score passes it by more than 2^kLazy, so probabilities and partial sums
+// stay below 2^8 times their true scale and most blocks skip the rescale.
+constexpr float kLazy = 8.0f;  // log2 units
+
 // F8: the caches hold E4M3 codes (one byte per element) instead of 16-bit elements.
 // Waves per unit of the vector-ALU kernel. Measured on the 7B-shaped layer and on 256 sequences
 // of U{1..512} tokens: 1 wave per unit (two units per workgroup) 76.7 % / 70.5 % of 8 TB/s, 2 waves
@@ -197,20 +202,25 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
 #pragma unroll
                 for (int i = 1; i < NCH; ++i)
                     mx = fmaxf(mx, s[h][i]);
-                const float mn = fmaxf(m[h], mx);
-                const float ms = mn == -INFINITY ? 0.0f : mn;
-                const float alpha = fast_exp2(m[h] - ms);
+                // the reference m moves only when some lane's scores pass it by more than
+                // 2^kLazy (the first valid block always does: m starts at -inf)
+                if (!__all(!(mx - m[h] > kLazy))) {
+                    const float mn = fmaxf(m[h], mx);
+                    const float alpha = fast_exp2(m[h] - (mn == -INFINITY ? 0.0f : mn));
+                    l[h] *= alpha;
+#pragma unroll
+                    for (int j = 0; j < EPL; ++j)
+                        acc[h][j] *= alpha;
+                    m[h] = mn;
+                }
+                const float ms = m[h] == -INFINITY ? 0.0f : m[h];
                 float psum = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    pr[h][i] = fast_exp2(s[h][i] - ms);
+                    pr[h][i] = fast_exp2(s[h][i] - ms);  // masked: exp2(-inf) = 0
                     psum += pr[h][i];
                 }
-                l[h] = l[h] * alpha + psum;
-                m[h] = mn;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j)
-                    acc[h][j] *= alpha;
+                l[h] += psum;
             }
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
@@ -346,11 +356,6 @@ __global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(Decod
         }
     }
 }
-
-// Lazy reference point of the MFMA units below: a column's running maximum moves (and its sums
-// are rescaled) only when a score passes it by more than 2^kLazy, so partial sums stay below 2^8
-// times their true scale and most steps skip the rescale.
-constexpr float kLazy = 8.0f;  // log2 units
 
 // ------------------------------------------------------------------ head groups on MFMA
 // Up to 16 query rows that read one (kv head, token range) -- the query heads of a GQA group, or the
