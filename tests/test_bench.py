@@ -1,0 +1,61 @@
+"""bench.py's command-line contract: one JSON line with the fields a reader of the results relies on.
+
+The GPU test runs a short benchmark of the tiny workload and of the mixed step (bench.main() in the
+test's own process) and checks the line's fields and their consistency: roofline fraction =
+achieved / peak, percentiles in order, the CPU baseline's sample stated. The CPU test checks that
+more than one GPU is refused before anything touches a device.
+"""
+import json
+import sys
+
+import pytest
+
+import bench
+
+REQUIRED = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+            "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "roofline")
+
+
+def run_bench(monkeypatch, *args):
+    """bench.main() in this process (no child process: the GPU may already be initialised)."""
+    monkeypatch.setattr(sys, "argv", ["bench.py", *args])
+    bench.main()
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    with pytest.raises(SystemExit) as e:
+        run_bench(monkeypatch, "--gpus", "2")
+    assert e.value.code == 2
+    out = capsys.readouterr()
+    assert "one GPU" in out.err and out.out.strip() == ""
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("workload,cpu", [("tiny_decode", True), ("chunked_prefill_mixed", False)])
+def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys):
+    args = ["--workload", workload, "--steps", "3", "--warmup", "1", "--cpu-seconds", "2"]
+    if not cpu:
+        args.append("--no-cpu-baseline")
+    print(f"[bench contract] {workload}", file=sys.stderr, flush=True)
+    run_bench(monkeypatch, *args)
+    stdout = capsys.readouterr().out
+    lines = [l for l in stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, stdout
+    d = json.loads(lines[0])
+    for k in REQUIRED:
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["config"]["workload"] == workload
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    p10, p50, p90 = d["decode_ms_p10_p50_p90"]
+    assert 0 < p10 <= p50 <= p90
+    if cpu:
+        c = d["cpu_baseline"]
+        assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
+        assert c["single_thread"]["value"] > 0
+    else:
+        assert "cpu_baseline" not in d
+        assert d["prefill_ms"] > 0 and 0 < d["prefill_mfma_frac"] < 1
