@@ -433,25 +433,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             pt[c4].w = pack2<BF>(s[kt][b + 6], s[kt][b + 7]);
         };
         // The work of one iteration in four chunks; the compiler interleaves within a chunk and
-        // never moves work across chunk boundaries, which bounds the operands in flight.
+        // never moves work across chunk boundaries, which bounds the operands in flight. The wave's
+        // issue priority steps down from 3 to 0 over the four chunks (s_setprio: a per-wave issue
+        // preference inside the SIMD): of the two waves on a SIMD, the one earlier in its step
+        // issues first, which keeps the two out of phase so that one's MFMAs overlap the other's
+        // softmax (mixed-step chunk 227.9 -> 221.3 us, results bit-identical; a strict split of
+        // each chunk into an MFMA block at priority 1 and a vector block at 0 was slower). E4M3
+        // instances keep one priority: their register staging at odd steps already staggers the
+        // waves, and the steps measured 245 -> 247 us there.
         auto region = [&](auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
                           const uint4 (&p_in)[4], uint4 (&p_out)[4], uint32_t kb,
                           uint32_t vb) PA_INLINE -> float {
             using C = std::integral_constant<int, 0>;
+            if constexpr (!F8)
+                __builtin_amdgcn_s_setprio(3);
             pv(std::integral_constant<int, 0>{}, p_in, vb);
             qk(C{}, std::integral_constant<int, DC / 4>{}, s_out, kb);
             const float alpha = sm_max(masked, s_in, t);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!F8)
+                __builtin_amdgcn_s_setprio(2);
             pv(std::integral_constant<int, 1>{}, p_in, vb);
             qk(std::integral_constant<int, DC / 4>{}, std::integral_constant<int, DC / 2>{}, s_out, kb);
             sm_exp(C{}, std::integral_constant<int, 11>{}, s_in);
             sm_pack(std::integral_constant<int, 0>{}, s_in, p_out);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!F8)
+                __builtin_amdgcn_s_setprio(1);
             pv(std::integral_constant<int, 2>{}, p_in, vb);
             qk(std::integral_constant<int, DC / 2>{}, std::integral_constant<int, 3 * DC / 4>{}, s_out, kb);
             sm_exp(std::integral_constant<int, 11>{}, std::integral_constant<int, 22>{}, s_in);
             sm_pack(std::integral_constant<int, 1>{}, s_in, p_out);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!F8)
+                __builtin_amdgcn_s_setprio(0);
             pv(std::integral_constant<int, 3>{}, p_in, vb);
             qk(std::integral_constant<int, 3 * DC / 4>{}, std::integral_constant<int, DC>{}, s_out, kb);
             sm_exp(std::integral_constant<int, 22>{}, std::integral_constant<int, 32>{}, s_in);
