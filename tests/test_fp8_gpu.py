@@ -101,7 +101,9 @@ def test_pool_quantized_on_device_equals_oracle():
     assert np.array_equal(bytes_of(g.v_cache), vc)
 
 
-def run_fp8_decode(w, ks, vs, partition_size=None):
+def run_fp8_decode(w, ks, vs, partition_size=None, pairs=None):
+    """The E4M3 decode on the GPU and the oracle's F6 reference: [B, H_q, D], or [n, D] for an
+    explicit list of (sequence, head) pairs."""
     kc, vc = oracle_fp8_pool(w, ks, vs)
     g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(kc, vc),
                 partition_size=partition_size)
@@ -114,15 +116,25 @@ def run_fp8_decode(w, ks, vs, partition_size=None):
     kc, vc = oracle_fp8_after_step(w, kc, vc, ks, vs)
     nd = w.n_decode
     ref = oracle.decode_fp8(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
-                            w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+                            w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs, pairs=pairs)
     return g, ref
 
 
 @pytest.mark.parametrize("name", ["tiny_decode", "llama2_7b_decode", "llama70b_gqa_decode"])
 def test_decode_named_workload(name):
     w = W.named(name)
-    g, ref = run_fp8_decode(w, 0.03, 0.02)
-    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, f"fp8 decode {name}")
+    pairs = None
+    if name == "llama70b_gqa_decode":
+        # full size, sampled outputs: every sequence with a quarter of its query heads, rotating
+        # with the sequence so that every head and kv head is checked (the oracle's E4M3 decode
+        # of all 2048 rows takes minutes on a loaded host)
+        pairs = np.array([(s, h) for s in range(w.n_decode) for h in range(w.H_q) if h % 4 == s % 4],
+                         dtype=np.int32)
+    g, ref = run_fp8_decode(w, 0.03, 0.02, pairs=pairs)
+    got = words_from_device(g.dec_out)
+    if pairs is not None:
+        got = got[pairs[:, 0], pairs[:, 1]]
+    assert_attention_close(got, ref, w.dtype, f"fp8 decode {name}")
 
 
 @pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (32, 8), (64, 8), (6, 2), (12, 4)])
