@@ -179,14 +179,28 @@ class TimingEvents:
     Recording a default event adds a system-scope release and acquire: a cache writeback and
     invalidation between the measured kernels and the work around them, which costs several
     microseconds per event and slows what follows. These events only write timestamps. They come
-    from the HIP runtime torch has loaded (soname libamdhip64.so.7), the one the library runs on.
+    from the HIP runtime this process has already mapped (torch's, which the library shares).
     """
     DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @staticmethod
+    def _loaded_hip_runtime():
+        """Path of the libamdhip64 already mapped into this process (dlopen of the same file returns
+        the loaded library), else its usual soname."""
+        try:
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    path = line.split()[-1] if len(line.split()) >= 6 else ""
+                    if os.path.basename(path).startswith("libamdhip64.so"):
+                        return path
+        except OSError:
+            pass
+        return "libamdhip64.so.7"
 
     def __init__(self, pairs):
         import ctypes
         self._ct = ctypes
-        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip = ctypes.CDLL(self._loaded_hip_runtime())
         hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
