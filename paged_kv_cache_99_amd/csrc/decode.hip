@@ -95,10 +95,11 @@ constexpr float kLazy = 8.0f;  // log2 units
 // heads). In a plain decode the parts of a sequence are taken in descending order: the units
 // issued last are then every sequence's first part -- many units of the full part length -- and
 // not the last parts that only the longest sequences have, which would leave most CUs idle while
-// a few finish (70B GQA layer 431.8 → 422.9 µs, 7B layer 409.5 → 405.4-407.2 µs). Units that
-// start at a per-sequence offset (the own tokens after a shared prefix, mostly under one part)
-// keep the ascending order: descending would issue their many empty high parts first (383 →
-// 388 µs on the 2040-token shared-prefix workload).
+// a few finish (32 sequences of 8K-32K tokens, 64 query / 8 kv heads: 431.8 → 422.9 µs; 64
+// sequences of 512-4K tokens, 32 heads: 409.5 → 405.4-407.2 µs). Units that start at a
+// per-sequence offset (the own tokens after a shared prefix, mostly under one part) keep the
+// ascending order: descending would issue their many empty high parts first (256 sequences in
+// groups of 8 sharing a 2040-token prompt: 383 → 388 µs).
 __device__ __forceinline__ int unit_part(const DecodeParams &p, int r, int n)
 {
     return p.seq_starts ? r : n - 1 - r;
