@@ -1,0 +1,88 @@
+"""Random shapes against the oracle: decode and chunked prefill, 16-bit and E4M3 caches.
+
+Each case draws from its own seeded generator: a head group (MHA, GQA of 2 to 8, and groups that
+are not powers of two), head_dim 64 or 128, fp16 or bf16, 1-11 decode sequences of 1-3000 tokens,
+often 1-3 prefill chunks of 1-299 rows over 0-1499 cached tokens, a partition size (library
+default, unsplit, 16, 256, 512 or 1024), and E4M3 scales. The whole step runs on the GPU (copy,
+scatter, decode, prefill) and every output row is compared with the float64 oracle on the pool after
+the step's scatter, within the element-wise attention gate (short contexts give outputs near 1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pa_workloads as W
+from paged_kv_cache_99_amd.step import GpuStep, words_from_device
+from pa_testutil import assert_attention_close, oracle_pool_after_step
+
+pytestmark = pytest.mark.gpu
+
+GROUPS = [(4, 4), (8, 8), (16, 8), (32, 8), (12, 4), (6, 2), (24, 8), (10, 2), (64, 8), (20, 4),
+          (2, 2), (8, 2)]
+PARTS = [None, 0, 16, 256, 512, 1024]
+
+
+def draw_case(case):
+    rng = np.random.default_rng(9100 + case)
+    H_q, H_kv = GROUPS[rng.integers(len(GROUPS))]
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    n_dec = int(rng.integers(1, 12))
+    lens = rng.integers(1, int(rng.choice([64, 700, 3000])), size=n_dec).tolist()
+    q_lens = []
+    if rng.random() < 0.6:
+        n_pre = int(rng.integers(1, 4))
+        q_lens = rng.integers(1, 300, size=n_pre).tolist()
+        lens += (rng.integers(0, 1500, size=n_pre) + np.array(q_lens)).tolist()
+    part = PARTS[rng.integers(len(PARTS))]
+    w = W.build(lens, H_q, H_kv, D, dtype, seed=int(rng.integers(1 << 30)), n_decode=n_dec,
+                q_lens=q_lens, partition_size=part)
+    scales = float(rng.choice([0.01, 0.03, 0.1])), float(rng.choice([0.01, 0.02, 0.1]))
+    return w, scales
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_step_matches_oracle(case):
+    w, (ks, vs) = draw_case(case)
+    nd = w.n_decode
+    tag = (f"case {case}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} decodes={nd} "
+           f"chunks={np.diff(w.cu_q_lens).tolist() if len(w.cu_q_lens) else []} "
+           f"partition={w.partition_size}")
+    print(f"[random] {tag}", flush=True)
+
+    g = GpuStep(w)
+    g.run()
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool_after_step(w)
+    ref = oracle.decode(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
+                        w.H_kv, w.D, w.num_blocks, w.dtype, w.scale)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "decode " + tag,
+                           strict=False)
+    has_chunks = g.pre_query.shape[0] > 0
+    if has_chunks:
+        ref = oracle.prefill(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
+                             w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale)
+        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "prefill " + tag,
+                               strict=False)
+    del g
+
+    k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, ks)
+    v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, vs)
+    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(k8, v8))
+    g.run()
+    torch.cuda.synchronize()
+    if len(w.copy_pairs):
+        k8, v8 = oracle.copy_blocks_fp8(k8, v8, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+    k8, v8 = oracle.reshape_and_cache_fp8(w.new_key, w.new_value, k8, v8, w.slot_mapping,
+                                          w.num_blocks, w.H_kv, w.D, w.dtype, ks, vs)
+    ref = oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
+                            w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "E4M3 decode " + tag,
+                           strict=False)
+    if has_chunks:
+        ref = oracle.prefill_fp8(w.query_prefill, k8, v8, w.block_tables[nd:], w.seq_lens[nd:],
+                                 w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                                 ks, vs)
+        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "E4M3 prefill " + tag,
+                               strict=False)
