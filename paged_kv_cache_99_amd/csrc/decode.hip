@@ -984,7 +984,7 @@ template <bool BF, bool F8, int D>
 hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hipStream_t stream)
 {
     hipError_t e;
-    if (pre) {
+    if (pre && pre->n_units > 0) {  // no prefix units when no sequence shares a token
         hipLaunchKernelGGL((decode_prefix_mfma_kernel<BF, F8, D>), dim3(round_up8(pre->n_units)),
                            dim3(kWave * kMfmaWaves), 0, stream, *pre);
         if ((e = hipGetLastError()) != hipSuccess)

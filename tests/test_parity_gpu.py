@@ -287,6 +287,39 @@ def test_shared_prefix_decode_named(name):
                            f"shared-prefix decode {name}")
 
 
+@pytest.mark.parametrize("kv", ["auto", "fp8"])
+def test_shared_prefix_decode_with_nothing_shared(kv):
+    """Groups whose prompts share no token (every prefix 0): the prefix pass has no work and must
+    not be launched; the call decodes the members like pa_decode (found by a random-shape sweep:
+    the empty prefix grid was rejected by the launch)."""
+    w = W.build_shared_groups([(0, [5, 9, 700]), (0, [33])], 8, 2, 128, "bf16", seed=140)
+    print(f"[parity] shared-prefix decode, nothing shared, kv={kv}", flush=True)
+    if kv == "auto":
+        g = run_on_gpu(w, stages=("copy", "scatter", "decode"), shared_prefix=True)
+        kc, vc = oracle_pool_after_step(w)
+        ref = oracle_decode(w, kc, vc)
+    else:
+        ks, vs = 0.03, 0.02
+        k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, ks)
+        v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, vs)
+        g = GpuStep(w, shared_prefix=True, kv_cache="fp8", k_scale=ks, v_scale=vs,
+                    fp8_pool=(k8, v8))
+        g.copy()
+        g.scatter()
+        g.decode()
+        torch.cuda.synchronize()
+        if len(w.copy_pairs):
+            k8, v8 = oracle.copy_blocks_fp8(k8, v8, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+        k8, v8 = oracle.reshape_and_cache_fp8(w.new_key, w.new_value, k8, v8, w.slot_mapping,
+                                              w.num_blocks, w.H_kv, w.D, w.dtype, ks, vs)
+        nd = w.n_decode
+        ref = oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd],
+                                w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+    assert g.shared_prefix
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype,
+                           f"shared-prefix decode, nothing shared ({kv})", strict=False)
+
+
 SHARED_GROUPS = [
     (40, [41, 60, 100]),                                        # prompt ends mid-block: CoW
     (512, [513, 700]),
