@@ -3,9 +3,9 @@
 The workload's physical blocks are relabelled to the top of a pool of more than 4 GiB per cache
 (block b becomes b + offset; tables, slots and copy pairs move with it; the blocks below are
 never touched). The library then runs the step -- copy_blocks, reshape_and_cache, decode (the
-vector-ALU kernel for MHA, the MFMA kernel for GQA), prefill -- and its results must equal the
-oracle's on the original, small pool: pools word for word at the relabelled blocks, attention
-within the gate. Relabelling blocks changes no result (the oracle pins block-relabelling
+vector-ALU kernel for MHA, the MFMA kernel for GQA), prefill (16-bit and E4M3 caches) -- and its
+results must equal the oracle's on the original, small pool: pools word for word at the
+relabelled blocks, attention within the gate. Relabelling blocks changes no result (the oracle pins block-relabelling
 invariance on the CPU).
 """
 import numpy as np
@@ -101,8 +101,8 @@ def test_step_on_blocks_past_4gib(H_q, H_kv, dtype):
 @pytest.mark.parametrize("H_q,H_kv,dtype", [(8, 8, "f16"), (32, 8, "bf16")])
 def test_e4m3_step_on_blocks_past_4gib(H_q, H_kv, dtype):
     D, ks, vs = 128, 0.03, 0.02
-    w = W.build(np.random.default_rng(810 + H_q).integers(200, 3000, size=12).tolist(), H_q, H_kv,
-                D, dtype, seed=811 + H_q, n_decode=12)
+    w = W.build(np.random.default_rng(810 + H_q).integers(200, 3000, size=12).tolist() + [1500, 700],
+                H_q, H_kv, D, dtype, seed=811 + H_q, n_decode=12, q_lens=[300, 64])
     block_bytes = H_kv * W.BLOCK * D
     off = (4 * GIB + 64 * 1024 * 1024) // block_bytes + 1
     nb = w.num_blocks + off
@@ -121,19 +121,30 @@ def test_e4m3_step_on_blocks_past_4gib(H_q, H_kv, dtype):
                                   words_to_device(w.new_value, dtype, dev), kc, vc,
                                   ints_to_device(slots, dev), ks, vs)
     tables = shifted(w.block_tables, off)
-    lens = np.asarray(w.seq_lens, np.int32)
+    nd = w.n_decode
+    lens = np.asarray(w.seq_lens[:nd], np.int32)
     max_len = int(lens.max())
     part = binding.default_partition_size(max_len)
-    ws = binding.alloc_decode_workspace(len(lens), H_q, D, max_len, part, dev)
+    ws = binding.alloc_decode_workspace(nd, H_q, D, max_len, part, dev)
     dq = words_to_device(w.query_decode, dtype, dev)
     dout = torch.empty_like(dq)
-    binding.decode_fp8(dout, dq, kc, vc, ints_to_device(tables, dev), ints_to_device(lens, dev),
-                       max_len, w.scale, ks, vs, part, ws)
+    binding.decode_fp8(dout, dq, kc, vc, ints_to_device(tables[:nd], dev),
+                       ints_to_device(lens, dev), max_len, w.scale, ks, vs, part, ws)
+    pq = words_to_device(w.query_prefill, dtype, dev)
+    pout = torch.empty_like(pq)
+    cu = np.asarray(w.cu_q_lens, np.int32)
+    binding.prefill_chunk_fp8(pout, pq, kc, vc, ints_to_device(tables[nd:], dev),
+                              ints_to_device(w.seq_lens[nd:], dev), ints_to_device(cu, dev),
+                              int(np.diff(cu).max()), w.scale, ks, vs)
     torch.cuda.synchronize()
     kr, vr = oracle.reshape_and_cache_fp8(w.new_key, w.new_value, k8, v8, w.slot_mapping,
                                           w.num_blocks, H_kv, D, dtype, ks, vs)
     for got, ref in ((kc, kr), (vc, vr)):
         assert np.array_equal(got[off:].cpu().numpy().ravel(), np.asarray(ref).ravel())
-    ref_d = oracle.decode_fp8(w.query_decode, kr, vr, w.block_tables, w.seq_lens, H_q, H_kv, D,
-                              w.num_blocks, dtype, w.scale, ks, vs)
+    ref_d = oracle.decode_fp8(w.query_decode, kr, vr, w.block_tables[:nd], w.seq_lens[:nd], H_q,
+                              H_kv, D, w.num_blocks, dtype, w.scale, ks, vs)
     assert_attention_close(words_from_device(dout), ref_d, dtype, "E4M3 decode past 4 GiB")
+    ref_p = oracle.prefill_fp8(w.query_prefill, kr, vr, w.block_tables[nd:], w.seq_lens[nd:],
+                               w.cu_q_lens, H_q, H_kv, D, w.num_blocks, dtype, w.scale, ks, vs)
+    assert_attention_close(words_from_device(pout), ref_p, dtype, "E4M3 prefill past 4 GiB",
+                           strict=False)
