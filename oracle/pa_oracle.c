@@ -363,6 +363,152 @@ static int gather_kv(const void *cache, int fp8, double cache_scale, const int32
     return oracle_gather((const uint16_t *)cache, row, L, kvh, num_blocks, H_kv, D, dtype, out);
 }
 
+/* The attention outputs one call evaluates: output row `out` is O5 of query row `qrow`, head `h`,
+ * over rows 0..L-1 of the gathered K and V of (sequence s, kv head g). */
+typedef struct {
+    int s, g, L, qrow, h;
+    long out;
+} or_item;
+
+static int item_order(const void *a, const void *b)
+{
+    const or_item *x = (const or_item *)a, *y = (const or_item *)b;
+    if (x->s != y->s)
+        return x->s < y->s ? -1 : 1;
+    if (x->g != y->g)
+        return x->g < y->g ? -1 : 1;
+    return (x->out > y->out) - (x->out < y->out);
+}
+
+/* Evaluate the items. Items of one (s, g) read the same gathered rows (O4 is exact, so gathering
+ * them once and letting each item read its leading L rows gives the very doubles a per-item gather
+ * would), so they are sorted by (s, g) and the gathers of a batch of keys, at most about 256 MB of
+ * doubles unless one key alone is larger, are made once before its items are evaluated. */
+static int run_items(or_item *it, long n, const uint16_t *query, int H_q, const void *k_cache,
+                     const void *v_cache, int fp8, double k_scale, double v_scale,
+                     const int32_t *block_tables, int max_blocks, int num_blocks, int H_kv, int D,
+                     int dtype, double scale, int nthreads, double *out)
+{
+    const size_t budget = (size_t)32 << 20; /* doubles of K plus V per batch */
+    int status = OR_OK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+    qsort(it, (size_t)n, sizeof(or_item), item_order);
+    long i0 = 0;
+    while (i0 < n) {
+        /* keys of this batch: [k0, k1) in the list of distinct (s, g) starting at item i0 */
+        long *first = NULL;
+        int nk = 0, cap = 0;
+        size_t used = 0;
+        long i = i0;
+        while (i < n) {
+            long j = i;
+            int L = 0;
+            while (j < n && it[j].s == it[i].s && it[j].g == it[i].g) {
+                if (it[j].L > L)
+                    L = it[j].L;
+                ++j;
+            }
+            size_t need = (size_t)2 * (size_t)L * D;
+            if (nk > 0 && used + need > budget)
+                break;
+            if (nk == cap) {
+                cap = cap ? 2 * cap : 64;
+                long *nf = (long *)realloc(first, sizeof(long) * (size_t)(cap + 1));
+                if (!nf) {
+                    free(first);
+                    return OR_NO_MEM;
+                }
+                first = nf;
+            }
+            first[nk++] = i;
+            used += need;
+            i = j;
+        }
+        first[nk] = i; /* end of the batch's items */
+        double **K = (double **)calloc((size_t)nk, sizeof(double *));
+        double **V = (double **)calloc((size_t)nk, sizeof(double *));
+        int *krc = (int *)calloc((size_t)nk, sizeof(int));
+        if (!K || !V || !krc) {
+            free(K);
+            free(V);
+            free(krc);
+            free(first);
+            return OR_NO_MEM;
+        }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+        for (int k = 0; k < nk; ++k) {
+            const or_item *head = &it[first[k]];
+            int L = 0;
+            for (long j = first[k]; j < first[k + 1]; ++j)
+                if (it[j].L > L)
+                    L = it[j].L;
+            K[k] = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
+            V[k] = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
+            if (!K[k] || !V[k]) {
+                krc[k] = OR_NO_MEM;
+                continue;
+            }
+            const int32_t *row = block_tables + (size_t)head->s * max_blocks;
+            krc[k] = gather_kv(k_cache, fp8, k_scale, row, L, head->g, num_blocks, H_kv, D, dtype,
+                               K[k]);
+            if (krc[k] == OR_OK)
+                krc[k] = gather_kv(v_cache, fp8, v_scale, row, L, head->g, num_blocks, H_kv, D,
+                                   dtype, V[k]);
+        }
+        const long nb = first[nk] - i0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+        for (long jj = 0; jj < nb; ++jj) {
+            const long j = i0 + jj;
+            int lo = 0, hi = nk - 1; /* the key whose items [first[k], first[k+1]) hold j */
+            while (lo < hi) {
+                int mid = (lo + hi + 1) / 2;
+                if (first[mid] <= j)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int k = lo;
+            int rc = krc[k];
+            if (rc == OR_OK) {
+                double *q = (double *)malloc(sizeof(double) * (size_t)D);
+                if (!q) {
+                    rc = OR_NO_MEM;
+                } else {
+                    for (int d = 0; d < D; ++d)
+                        q[d] = oracle_to_double(query[((size_t)it[j].qrow * H_q + it[j].h) * D + d],
+                                                dtype);
+                    rc = oracle_attention(q, K[k], V[k], it[j].L, D, scale,
+                                          out + (size_t)it[j].out * D);
+                    free(q);
+                }
+            }
+            if (rc != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+                status = rc;
+            }
+        }
+        for (int k = 0; k < nk; ++k) {
+            free(K[k]);
+            free(V[k]);
+        }
+        free(K);
+        free(V);
+        free(krc);
+        i0 = first[nk];
+        free(first);
+    }
+    return status;
+}
+
 static int decode_pairs(const uint16_t *query, const void *k_cache, const void *v_cache, int fp8,
                         double k_scale, double v_scale, const int32_t *block_tables,
                         int max_blocks, const int32_t *seq_lens, int B, int H_q, int H_kv, int D,
@@ -371,55 +517,34 @@ static int decode_pairs(const uint16_t *query, const void *k_cache, const void *
 {
     if (B < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
         return OR_BAD_ARG;
-    int n = pairs ? n_pairs : B * H_q;
+    long n = pairs ? n_pairs : (long)B * H_q;
     int group = H_q / H_kv;
-    int status = OR_OK;
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
-#endif
-    for (int i = 0; i < n; ++i) {
-        int s = pairs ? pairs[2 * i] : i / H_q;
-        int h = pairs ? pairs[2 * i + 1] : i % H_q;
-        int rc = OR_OK;
+    or_item *it = (or_item *)malloc(sizeof(or_item) * (size_t)(n + 1));
+    if (!it)
+        return OR_NO_MEM;
+    for (long i = 0; i < n; ++i) {
+        int s = pairs ? pairs[2 * i] : (int)(i / H_q);
+        int h = pairs ? pairs[2 * i + 1] : (int)(i % H_q);
         if (s < 0 || s >= B || h < 0 || h >= H_q) {
-            rc = OR_BAD_ARG;
-        } else {
-            int L = seq_lens[s];
-            if (L < 0 || L > max_blocks * OR_BLOCK) {
-                rc = OR_BAD_INDEX;
-            } else {
-                double *K = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
-                double *V = (double *)malloc(sizeof(double) * ((size_t)L * D + 1));
-                double *q = (double *)malloc(sizeof(double) * (size_t)D);
-                if (!K || !V || !q) {
-                    rc = OR_NO_MEM;
-                } else {
-                    const int32_t *row = block_tables + (size_t)s * max_blocks;
-                    rc = gather_kv(k_cache, fp8, k_scale, row, L, h / group, num_blocks, H_kv, D,
-                                   dtype, K);
-                    if (rc == OR_OK)
-                        rc = gather_kv(v_cache, fp8, v_scale, row, L, h / group, num_blocks, H_kv,
-                                       D, dtype, V);
-                    for (int d = 0; d < D; ++d)
-                        q[d] = oracle_to_double(query[((size_t)s * H_q + h) * D + d], dtype);
-                    if (rc == OR_OK)
-                        rc = oracle_attention(q, K, V, L, D, scale, out + (size_t)i * D);
-                }
-                free(K);
-                free(V);
-                free(q);
-            }
+            free(it);
+            return OR_BAD_ARG;
         }
-        if (rc != OR_OK) {
-#ifdef _OPENMP
-#pragma omp critical
-#endif
-            status = rc;
+        int L = seq_lens[s];
+        if (L < 0 || L > max_blocks * OR_BLOCK) {
+            free(it);
+            return OR_BAD_INDEX;
         }
+        it[i].s = s;
+        it[i].g = h / group;
+        it[i].L = L;
+        it[i].qrow = s;
+        it[i].h = h;
+        it[i].out = i;
     }
-    return status;
+    int rc = run_items(it, n, query, H_q, k_cache, v_cache, fp8, k_scale, v_scale, block_tables,
+                       max_blocks, num_blocks, H_kv, D, dtype, scale, nthreads, out);
+    free(it);
+    return rc;
 }
 
 int oracle_decode(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
@@ -460,61 +585,39 @@ static int prefill_rows(const uint16_t *query, const void *k_cache, const void *
     if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || D <= 0)
         return OR_BAD_ARG;
     int total_q = cu_q_lens[S];
-    int n = rows ? n_rows : total_q * H_q;
+    long n = rows ? n_rows : (long)total_q * H_q;
     int group = H_q / H_kv;
-    int status = OR_OK;
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
-#endif
-    for (int i = 0; i < n; ++i) {
-        int r = rows ? rows[2 * i] : i / H_q;
-        int h = rows ? rows[2 * i + 1] : i % H_q;
-        int rc = OR_OK;
+    or_item *it = (or_item *)malloc(sizeof(or_item) * (size_t)(n + 1));
+    if (!it)
+        return OR_NO_MEM;
+    for (long i = 0; i < n; ++i) {
+        int r = rows ? rows[2 * i] : (int)(i / H_q);
+        int h = rows ? rows[2 * i + 1] : (int)(i % H_q);
         int s = -1;
         for (int j = 0; j < S; ++j)
             if (cu_q_lens[j] <= r && r < cu_q_lens[j + 1])
                 s = j;
         if (s < 0 || h < 0 || h >= H_q) {
-            rc = OR_BAD_ARG;
-        } else {
-            int q_len = cu_q_lens[s + 1] - cu_q_lens[s];
-            int p = seq_lens[s] - q_len + (r - cu_q_lens[s]);
-            if (p < 0 || seq_lens[s] > max_blocks * OR_BLOCK) {
-                rc = OR_BAD_INDEX;
-            } else {
-                int L = p + 1;
-                double *K = (double *)malloc(sizeof(double) * (size_t)L * D);
-                double *V = (double *)malloc(sizeof(double) * (size_t)L * D);
-                double *q = (double *)malloc(sizeof(double) * (size_t)D);
-                if (!K || !V || !q) {
-                    rc = OR_NO_MEM;
-                } else {
-                    const int32_t *row = block_tables + (size_t)s * max_blocks;
-                    rc = gather_kv(k_cache, fp8, k_scale, row, L, h / group, num_blocks, H_kv, D,
-                                   dtype, K);
-                    if (rc == OR_OK)
-                        rc = gather_kv(v_cache, fp8, v_scale, row, L, h / group, num_blocks, H_kv,
-                                       D, dtype, V);
-                    for (int d = 0; d < D; ++d)
-                        q[d] = oracle_to_double(query[((size_t)r * H_q + h) * D + d], dtype);
-                    if (rc == OR_OK)
-                        rc = oracle_attention(q, K, V, L, D, scale, out + (size_t)i * D);
-                }
-                free(K);
-                free(V);
-                free(q);
-            }
+            free(it);
+            return OR_BAD_ARG;
         }
-        if (rc != OR_OK) {
-#ifdef _OPENMP
-#pragma omp critical
-#endif
-            status = rc;
+        int q_len = cu_q_lens[s + 1] - cu_q_lens[s];
+        int p = seq_lens[s] - q_len + (r - cu_q_lens[s]);
+        if (p < 0 || seq_lens[s] > max_blocks * OR_BLOCK) {
+            free(it);
+            return OR_BAD_INDEX;
         }
+        it[i].s = s;
+        it[i].g = h / group;
+        it[i].L = p + 1; /* the row attends positions 0..p */
+        it[i].qrow = r;
+        it[i].h = h;
+        it[i].out = i;
     }
-    return status;
+    int rc = run_items(it, n, query, H_q, k_cache, v_cache, fp8, k_scale, v_scale, block_tables,
+                       max_blocks, num_blocks, H_kv, D, dtype, scale, nthreads, out);
+    free(it);
+    return rc;
 }
 
 int oracle_prefill(const uint16_t *query, const uint16_t *k_cache, const uint16_t *v_cache,
