@@ -10,6 +10,7 @@ import oracle
 
 ATOL = 2e-3      # max |gpu - oracle| over every element
 ROW_RTOL = 1e-2  # max over (token, head) rows of ||gpu - oracle||_inf / ||oracle||_inf
+BF16_HALF_ULP = 2.0 ** -8  # largest relative rounding error of a bfloat16 output
 
 
 def words_to_f64(words, dtype):
@@ -59,25 +60,41 @@ def attention_errors(got_words, ref, dtype):
     return (float(err.max()) if err.size else 0.0), (float(rel.max()) if rel.size else 0.0), got
 
 
-def assert_attention_close(got_words, ref, dtype, what="", strict=True):
-    """Gate of an attention output against the float64 oracle.
+def elementwise_bound(ref, dtype):
+    """Per-element bound on |gpu - oracle| for an attention output of `dtype`.
 
-    Always: every element within |gpu - ref| <= 2e-3 + 1e-2 * |ref| (absolute 2e-3 and relative
-    1e-2 read together, as torch.testing.assert_close does). strict=True adds the stronger gate used
-    on the named workloads: max |gpu - ref| <= 2e-3 over every element and a row-normwise relative
-    error <= 1e-2. Short contexts give outputs near 1, where rounding to bfloat16 alone moves a value
-    by up to 2^-9 * |ref| (3.9e-3 at |ref| in [1, 2)): edge-case tests of such contexts run with
-    strict=False.
+    f16 outputs: 2e-3. A binary16 output keeps 11 significant bits, so rounding it moves a value by
+    at most 2^-11 |ref| (below 1e-3 for |ref| < 2), well inside the bound.
+    bf16 outputs: 2e-3 + 2^-8 |ref|. A bfloat16 output keeps 8 significant bits; rounding to nearest
+    moves x in [2^e, 2^(e+1)) by up to half a unit in the last place, 2^(e-8), which is 2^-8 |x| at
+    the bottom of the binade. No correct kernel can do better than its own output rounding, so the
+    gate adds exactly that to the 2e-3 allowed for the arithmetic.
+    """
+    if dtype == "bf16":
+        return ATOL + BF16_HALF_ULP * np.abs(ref)
+    assert dtype == "f16", dtype
+    return np.full(np.shape(ref), ATOL)
+
+
+def assert_attention_close(got_words, ref, dtype, what="", absolute=False):
+    """Gate of an attention output against the float64 oracle (the 2e-3 / 1e-2 bound read per
+    output type):
+      (i)  every element: |gpu - ref| <= elementwise_bound(ref, dtype) -- 2e-3 for f16 outputs,
+           2e-3 + 2^-8 |ref| for bf16 outputs;
+      (ii) every (token, head) row: ||gpu - ref||_inf / ||ref||_inf <= 1e-2.
+    absolute=True adds max |gpu - ref| <= 2e-3 for bf16 outputs too; the long-context workloads,
+    whose outputs are small, meet it.
     """
     max_abs, max_rel, got = attention_errors(got_words, ref, dtype)
-    excess = float((np.abs(got - ref) - (ATOL + ROW_RTOL * np.abs(ref))).max()) if ref.size else 0.0
-    print(f"[parity] {what}: max_abs={max_abs:.3e} max_row_rel={max_rel:.3e} "
-          f"max(|d| - (atol + rtol|ref|))={excess:.3e} n={ref.size}", flush=True)
+    bound = elementwise_bound(ref, dtype)
+    excess = float((np.abs(got - ref) - bound).max()) if ref.size else 0.0
+    print(f"[parity] {what}: {dtype} max_abs={max_abs:.3e} max_row_rel={max_rel:.3e} "
+          f"max(|d| - bound)={excess:.3e} n={ref.size}", flush=True)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    assert excess <= 0, f"{what}: |d| exceeds 2e-3 + 1e-2 |ref| by {excess:.3e}"
-    if strict:
+    assert excess <= 0, f"{what}: |d| exceeds the {dtype} element bound by {excess:.3e}"
+    assert max_rel <= ROW_RTOL, f"{what}: row-normwise relative error {max_rel:.3e} > {ROW_RTOL}"
+    if absolute:
         assert max_abs <= ATOL, f"{what}: max abs error {max_abs:.3e} > {ATOL}"
-        assert max_rel <= ROW_RTOL, f"{what}: row-normwise relative error {max_rel:.3e} > {ROW_RTOL}"
 
 
 # ------------------------------------------------------------------ drafted-token trees

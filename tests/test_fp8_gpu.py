@@ -7,6 +7,8 @@ subnormal and saturating inputs included); the E4M3 decode is within the attenti
 absolute, 1e-2 row-normwise) of the oracle's decode of the same codes, bitwise reproducible, and
 never reads a slot outside a sequence's context (such slots hold the NaN code).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -122,19 +124,12 @@ def run_fp8_decode(w, ks, vs, partition_size=None, pairs=None):
 
 @pytest.mark.parametrize("name", ["tiny_decode", "llama2_7b_decode", "llama70b_gqa_decode"])
 def test_decode_named_workload(name):
+    """Every output row of the named workloads at full size (the 70B-shaped one: 32 sequences of
+    8K-32K tokens, all 64 query heads)."""
     w = W.named(name)
-    pairs = None
-    if name == "llama70b_gqa_decode":
-        # full size, sampled outputs: every sequence with a quarter of its query heads, rotating
-        # with the sequence so that every head and kv head is checked (the oracle's E4M3 decode
-        # of all 2048 rows takes minutes on a loaded host)
-        pairs = np.array([(s, h) for s in range(w.n_decode) for h in range(w.H_q) if h % 4 == s % 4],
-                         dtype=np.int32)
-    g, ref = run_fp8_decode(w, 0.03, 0.02, pairs=pairs)
-    got = words_from_device(g.dec_out)
-    if pairs is not None:
-        got = got[pairs[:, 0], pairs[:, 1]]
-    assert_attention_close(got, ref, w.dtype, f"fp8 decode {name}")
+    g, ref = run_fp8_decode(w, 0.03, 0.02)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, f"fp8 decode {name}",
+                           absolute=True)
 
 
 @pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (32, 8), (64, 8), (6, 2), (12, 4)])
@@ -146,7 +141,7 @@ def test_decode_head_groups(H_q, H_kv, D, dtype):
     for part, (ks, vs) in ((0, (1.0, 1.0)), (256, (0.05, 0.015)), (512, (2.0 ** -5, 0.3))):
         g, ref = run_fp8_decode(w, ks, vs, partition_size=part)
         assert_attention_close(words_from_device(g.dec_out), ref, dtype,
-                               f"fp8 decode H_q={H_q} H_kv={H_kv} D={D} P={part}", strict=False)
+                               f"fp8 decode H_q={H_q} H_kv={H_kv} D={D} P={part}")
 
 
 def test_decode_is_deterministic():
@@ -206,7 +201,7 @@ def test_shared_prefix_decode_groups(H_q, H_kv, D, dtype, part, ks, vs):
     g, ref = run_fp8_shared_prefix(w, ks, vs, partition_size=part)
     assert_attention_close(words_from_device(g.dec_out), ref, dtype,
                            f"fp8 shared-prefix decode H_q={H_q} H_kv={H_kv} D={D} {dtype} "
-                           f"part={part}", strict=False)
+                           f"part={part}")
 
 
 def test_shared_prefix_decode_is_deterministic_and_matches_plain():
@@ -222,11 +217,10 @@ def test_shared_prefix_decode_is_deterministic_and_matches_plain():
     binding.decode_fp8(plain, g.dec_query, g.k_cache, g.v_cache, g.dec_tables, g.dec_lens,
                        g.max_seq_len, w.scale, 0.03, 0.02, 256)
     torch.cuda.synchronize()
-    # contexts of 5 to 17 tokens give outputs near 1: the elementwise gate (bf16 rounding there
-    # alone is up to 3.9e-3)
-    assert_attention_close(words_from_device(plain), ref, w.dtype, "fp8 plain decode",
-                           strict=False)
-    assert_attention_close(first, ref, w.dtype, "fp8 shared-prefix decode", strict=False)
+    # contexts of 5 to 17 tokens give outputs near 1, where the bf16 output's own rounding alone
+    # reaches 2^-8 |ref| (3.9e-3 at |ref| = 1): the bf16 gate, not the absolute one
+    assert_attention_close(words_from_device(plain), ref, w.dtype, "fp8 plain decode")
+    assert_attention_close(first, ref, w.dtype, "fp8 shared-prefix decode")
 
 
 # --------------------------------------------------------------- chunked prefill, E4M3
@@ -260,12 +254,12 @@ def test_prefill_chunks(H_q, H_kv, D, dtype):
                 q_lens=q_lens)
     g, ref = run_fp8_prefill(w, 0.04, 0.025)
     assert_attention_close(words_from_device(g.pre_out), ref, dtype,
-                           f"fp8 prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}", strict=False)
+                           f"fp8 prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}")
 
 
-def test_prefill_mixed_step_sampled():
-    """The 2048-token mixed step over E4M3 caches: every decode row, and sampled chunk rows
-    (first, last and random) against the oracle."""
+def test_prefill_mixed_step_full():
+    """The 2048-token mixed step over E4M3 caches: every decode row and every row of the 1856-row
+    chunk (all 32 heads) against the oracle."""
     w = W.named("chunked_prefill_mixed")
     ks, vs = 0.03, 0.02
     kc, vc = oracle_fp8_pool(w, ks, vs, poison=False)
@@ -277,16 +271,15 @@ def test_prefill_mixed_step_sampled():
     nd = w.n_decode
     ref_d = oracle.decode_fp8(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd],
                               w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
-    assert_attention_close(words_from_device(g.dec_out), ref_d, w.dtype, "fp8 mixed decode")
-    rng = np.random.default_rng(670)
-    tq = w.query_prefill.shape[0]
-    rows = sorted(set([0, tq - 1] + rng.integers(0, tq, 40).tolist()))
-    pairs = np.array([(r, h) for r in rows for h in range(w.H_q)], np.int32)
+    assert_attention_close(words_from_device(g.dec_out), ref_d, w.dtype, "fp8 mixed decode",
+                           absolute=True)
+    t = time.time()
     ref_p = oracle.prefill_fp8(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
                                w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
-                               ks, vs, rows=pairs)
-    got = words_from_device(g.pre_out)[pairs[:, 0], pairs[:, 1]]
-    assert_attention_close(got, ref_p, w.dtype, "fp8 mixed prefill rows")
+                               ks, vs)
+    print(f"[fp8] oracle prefill of the whole chunk: {time.time() - t:.1f}s", flush=True)
+    assert_attention_close(words_from_device(g.pre_out), ref_p, w.dtype, "fp8 mixed prefill",
+                           absolute=True)
 
 
 def test_prefill_is_deterministic():

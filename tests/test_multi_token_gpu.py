@@ -59,8 +59,7 @@ def test_multi_token_rows_equal_per_row_decode(H_q, H_kv, D, dtype):
     tables, cut = per_row_decode_view(w)
     ref = oracle.decode(w.query_prefill, kc, vc, tables, cut, H_q, H_kv, D, w.num_blocks, dtype,
                         w.scale)
-    assert_attention_close(got, ref, dtype, f"multi-token rows H_q={H_q} H_kv={H_kv} D={D}",
-                           strict=False)
+    assert_attention_close(got, ref, dtype, f"multi-token rows H_q={H_q} H_kv={H_kv} D={D}")
 
     # the same rows as one-token decodes on the GPU (pool after this step's scatter)
     dec = GpuStep(w)
@@ -74,4 +73,4 @@ def test_multi_token_rows_equal_per_row_decode(H_q, H_kv, D, dtype):
     binding.decode(out, dec.pre_query, dec.k_cache, dec.v_cache, tables_d, lens_d, max_len,
                    w.scale, part, ws)
     torch.cuda.synchronize()
-    assert_attention_close(words_from_device(out), ref, dtype, "per-row GPU decode", strict=False)
+    assert_attention_close(words_from_device(out), ref, dtype, "per-row GPU decode")

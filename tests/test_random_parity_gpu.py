@@ -57,14 +57,12 @@ def test_random_step_matches_oracle(case):
     kc, vc = oracle_pool_after_step(w)
     ref = oracle.decode(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
                         w.H_kv, w.D, w.num_blocks, w.dtype, w.scale)
-    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "decode " + tag,
-                           strict=False)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "decode " + tag)
     has_chunks = g.pre_query.shape[0] > 0
     if has_chunks:
         ref = oracle.prefill(w.query_prefill, kc, vc, w.block_tables[nd:], w.seq_lens[nd:],
                              w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale)
-        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "prefill " + tag,
-                               strict=False)
+        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "prefill " + tag)
     del g
 
     k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, ks)
@@ -78,11 +76,9 @@ def test_random_step_matches_oracle(case):
                                           w.num_blocks, w.H_kv, w.D, w.dtype, ks, vs)
     ref = oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,
                             w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
-    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "E4M3 decode " + tag,
-                           strict=False)
+    assert_attention_close(words_from_device(g.dec_out), ref, w.dtype, "E4M3 decode " + tag)
     if has_chunks:
         ref = oracle.prefill_fp8(w.query_prefill, k8, v8, w.block_tables[nd:], w.seq_lens[nd:],
                                  w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
                                  ks, vs)
-        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "E4M3 prefill " + tag,
-                               strict=False)
+        assert_attention_close(words_from_device(g.pre_out), ref, w.dtype, "E4M3 prefill " + tag)

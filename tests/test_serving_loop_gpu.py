@@ -174,7 +174,7 @@ class Loop:
                                             self.dtype, self.scale, self.fp8)
                         for i, (sid, h, n) in enumerate(rows) for j in range(n - h)])
         self.check_pools()
-        assert_attention_close(got, ref, self.dtype, f"prefill {sids}", strict=False)
+        assert_attention_close(got, ref, self.dtype, f"prefill {sids}")
         return [h for _, h, _ in rows]
 
     def decode_step(self, sids, partition_size):
@@ -203,7 +203,7 @@ class Loop:
         ref = np.stack([reference_attention(q[i], self.ids[s], lens[i], self.rows, self.dtype,
                                             self.scale, self.fp8) for i, s in enumerate(sids)])
         self.check_pools()
-        assert_attention_close(got, ref, self.dtype, f"decode {sids}", strict=False)
+        assert_attention_close(got, ref, self.dtype, f"decode {sids}")
         return len(pairs)
 
     def check_pools(self):

@@ -57,7 +57,7 @@ def test_tree_rows_match_oracle(H_q, H_kv, D, dtype):
     ref = oracle.prefill_tree(w.query_prefill, kc, vc, w.block_tables, w.seq_lens, w.cu_q_lens,
                               masks, H_q, H_kv, D, w.num_blocks, dtype, w.scale)
     assert_attention_close(words_from_device(g.pre_out), ref, dtype,
-                           f"tree rows H_q={H_q} H_kv={H_kv} D={D} {dtype}", strict=False)
+                           f"tree rows H_q={H_q} H_kv={H_kv} D={D} {dtype}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
