@@ -902,9 +902,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     const int seq = idx / p.num_q_heads;
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int start = unit_start(p, seq, L);
-    // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots
-    const int n_pre = p.pre_slots > 0 ? (start + p.pre_slot_tokens - 1) / p.pre_slot_tokens : 0;
-    const int n_own = (L - start + p.slot_tokens - 1) / p.slot_tokens;
+    // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots.
+    // Both counts are clamped to the slots the workspace has, so that prefix lengths breaking the
+    // caller's contract (unequal within a group, above max_prefix_len) give unspecified output but
+    // never a read outside the workspace.
+    const int n_pre = p.pre_slots > 0
+                          ? min((start + p.pre_slot_tokens - 1) / p.pre_slot_tokens, p.pre_slots)
+                          : 0;
+    const int n_own = min((L - start + p.slot_tokens - 1) / p.slot_tokens, p.ws_slots - p.pre_slots);
     const int np = n_pre + n_own;
     auto slot_of = [&](int jj) { return jj < n_pre ? jj : p.pre_slots + (jj - n_pre); };
     const float *ml = p.ws_ml + (size_t)idx * p.ws_slots * 2;

@@ -38,6 +38,37 @@ def ints_to_device(a, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
 
 
+def check_shared_prefix(group_starts, prefix_lens, seq_lens, block_tables) -> None:
+    """Host-side check of the groups given to pa_decode_shared_prefix{,_fp8}, on the numpy arrays
+    the caller already holds: the library takes them as device memory and trusts them (a group
+    that breaks them gives unspecified output). Raises ValueError naming the first violation.
+
+    group_starts [G+1] starts at 0 and does not decrease; prefix_lens [B] is a multiple of 16, equal
+    across the members of a group, at most every member's length, 0 outside the groups; the table
+    entries of a group's shared blocks are the same for every member (openeuler.csdn.net
+    "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are one physical copy)."""
+    gs = np.asarray(group_starts, np.int64)
+    pl = np.asarray(prefix_lens, np.int64)
+    lens = np.asarray(seq_lens, np.int64)
+    bt = np.asarray(block_tables)
+    B = len(pl)
+    if len(gs) == 0 or gs[0] != 0 or np.any(np.diff(gs) < 0) or gs[-1] > B:
+        raise ValueError("group_starts must rise from 0 to at most num_seqs")
+    if np.any(pl < 0) or np.any(pl % binding.BLOCK_SIZE) or np.any(pl > lens[:B]):
+        raise ValueError("prefix_lens must be multiples of 16 within [0, seq_lens]")
+    if np.any(pl[gs[-1]:] != 0):
+        raise ValueError("a sequence in no group must have prefix_lens 0")
+    for g in range(len(gs) - 1):
+        a, b = int(gs[g]), int(gs[g + 1])
+        if b == a:
+            continue
+        if np.any(pl[a:b] != pl[a]):
+            raise ValueError(f"group {g}: members have different prefix_lens")
+        nb = int(pl[a]) // binding.BLOCK_SIZE
+        if nb and np.any(bt[a:b, :nb] != bt[a, :nb]):
+            raise ValueError(f"group {g}: members do not share the prefix blocks")
+
+
 class GpuStep:
     """Device buffers of one step and its stages.
 
@@ -93,6 +124,7 @@ class GpuStep:
         if self.shared_prefix:
             gs = np.asarray(meta["group_starts"], np.int32)
             pl = np.asarray(meta["shared_prefix"], np.int32)[:nd]
+            check_shared_prefix(gs, pl, w.seq_lens[:nd], w.block_tables[:nd])
             self.group_starts = ints_to_device(gs, dev)
             self.prefix_lens = ints_to_device(pl, dev)
             self.max_group_size = int(np.max(np.diff(gs))) if len(gs) > 1 else 1

@@ -124,3 +124,41 @@ def test_generator_is_deterministic():
     assert np.array_equal(a.k_cache, b.k_cache) and np.array_equal(a.block_tables, b.block_tables)
     c = W.build([30, 50], 4, 2, 64, "bf16", seed=10)
     assert not np.array_equal(a.k_cache, c.k_cache)
+
+
+# ---------------------------------------------------------- host check of shared-prefix groups
+def test_shared_prefix_groups_pass_the_host_check():
+    from paged_kv_cache_99_amd.step import check_shared_prefix
+    for w in (W.build_shared_groups([(40, [41, 60, 90]), (64, [65, 70])], 8, 2, 64, "f16", seed=1,
+                                    independent=[5, 33]),
+              W.named("prefix_sharing_2040")):
+        m = w.meta
+        check_shared_prefix(m["group_starts"], m["shared_prefix"], w.seq_lens, w.block_tables)
+
+
+@pytest.mark.parametrize("breach", ["unequal", "not_shared", "past_length", "unaligned",
+                                    "outside_group", "bad_starts"])
+def test_shared_prefix_contract_violations_are_rejected_on_the_host(breach):
+    """Groups that break pa_decode_shared_prefix's contract never reach the library: the step
+    driver's host check names the violation."""
+    from paged_kv_cache_99_amd.step import check_shared_prefix
+    w = W.build_shared_groups([(40, [41, 60, 90]), (64, [65, 70])], 8, 2, 64, "f16", seed=1,
+                              independent=[5, 33])
+    gs = w.meta["group_starts"].copy()
+    pl = w.meta["shared_prefix"].copy()
+    bt = w.block_tables.copy()
+    lens = w.seq_lens.copy()
+    if breach == "unequal":
+        pl[1] = 16
+    elif breach == "not_shared":
+        bt[2, 0] = bt[3, 0]
+    elif breach == "past_length":
+        lens[3] = 48               # member 3 shares 64 prefix tokens but would hold only 48
+    elif breach == "unaligned":
+        pl[0:3] = 40
+    elif breach == "outside_group":
+        pl[5] = 16
+    else:
+        gs = np.array([1, 3, 5], np.int32)
+    with pytest.raises(ValueError):
+        check_shared_prefix(gs, pl, lens, bt)
