@@ -21,7 +21,8 @@
  *  - Every tensor argument is a DEVICE pointer owned by the caller, row-major and contiguous, and
  *    aligned to 16 bytes. These entry points allocate no memory, keep no state between calls (apart
  *    from a thread-local error message) and may be called from several threads. (The host-side
- *    block manager of pa_block_manager.h, also in this library, is the one stateful part.)
+ *    block manager of pa_block_manager.h, also in this library, is the one stateful part;
+ *    pa_decode_noalloc keeps its partial results in a static device array instead of a workspace.)
  *  - 16-bit element type: PA_DTYPE_F16 (IEEE binary16) or PA_DTYPE_BF16 (bfloat16). Queries, keys,
  *    values, caches and outputs all share it. Arithmetic is float32; outputs are rounded to nearest
  *    even.
@@ -137,6 +138,32 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
                       int32_t max_seq_len, int32_t num_q_heads, float scale,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no workspace and
+ * allocates nothing: the split-K partial results go to a static scratch array inside this library
+ * (PA_DECODE_SCRATCH_BYTES, 64 MiB), one copy on every GPU the library runs on, held from its
+ * first use there until the process ends. Its address on a GPU is looked up once (the first call
+ * on that GPU, for the device that owns `stream`; the current device for the null stream).
+ * Arguments, results and errors are those of pa_decode (16-bit caches), with two more rules:
+ *   - the partial results of these sizes, num_seqs * num_q_heads * slots * (head_dim + 2) fp32
+ *     values (slots = ceil(ceil(max_seq_len / partition_size) / w), w = 4 for head groups of 3 or
+ *     more, else 1; none when unsplit), must fit PA_DECODE_SCRATCH_BYTES, else PA_ERR_WORKSPACE
+ *     before anything is enqueued;
+ *   - every call on one GPU shares its scratch: calls that overlap in time on one GPU (different
+ *     streams, or threads without ordering) race and give unspecified output. Calls ordered on one
+ *     stream are safe. Nothing in the scratch needs to start at zero: each call writes every
+ *     partial it reads.
+ */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+pa_status_t pa_decode_noalloc(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                              int32_t head_dim, void *out, const void *query, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                              int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                              float scale, int32_t partition_size, void *stream);
 
 /*
  * pa_decode_shared_prefix -- pa_decode for batches whose sequences share prompt blocks, reading

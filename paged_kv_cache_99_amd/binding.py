@@ -20,6 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 BLOCK_SIZE = 16
+DECODE_SCRATCH_BYTES = 64 << 20  # PA_DECODE_SCRATCH_BYTES: pa_decode_noalloc's static scratch
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 _DTYPE = {torch.float16: 0, torch.bfloat16: 1}
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode.restype = _i
         L.pa_decode.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _i,
                                 _p, _sz, _p]
+        L.pa_decode_noalloc.restype = _i
+        L.pa_decode_noalloc.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                        _f, _i, _p]
         L.pa_decode_shared_prefix_workspace_size.restype = _sz
         L.pa_decode_shared_prefix_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
         L.pa_decode_shared_prefix.restype = _i
@@ -199,6 +203,29 @@ def decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: in
                            int(block_tables.shape[1]), seq_lens.data_ptr(), B, int(max_seq_len),
                            hq, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                            _stream(stream)))
+
+
+def decode_noalloc(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+                   scale: float, partition_size: Optional[int] = None, stream=None) -> None:
+    """pa_decode_noalloc: pa_decode with its partial results in the library's static scratch (no
+    workspace, nothing allocated); arguments as decode."""
+    dt, nb, hkv, d = _cache_dims(k_cache, v_cache)
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, k_cache.dtype)
+        if tuple(t.shape) != (B, hq, d):
+            raise ValueError(f"{n} must be [{B}, {hq}, {d}]")
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(seq_lens, "seq_lens", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
+    if partition_size is None:
+        partition_size = default_partition_size(max_seq_len)
+    _check(lib().pa_decode_noalloc(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
+                                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                   int(block_tables.shape[1]), seq_lens.data_ptr(), B,
+                                   int(max_seq_len), hq, float(scale), int(partition_size),
+                                   _stream(stream)))
 
 
 def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,

@@ -37,6 +37,8 @@
 // (kv head, token range) are the 16 columns of v_mfma_f32_16x16x32; see mfma_unit below.
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -723,7 +725,7 @@ __device__ __forceinline__ void mfma_write_output(const DecodeParams &p, int qro
                                               pack2<BF>(o[t][2] * inv, o[t][3] * inv));
 }
 
-constexpr int kMfmaWaves = 4;  // MFMA units (waves) per workgroup
+constexpr int kMfmaWaves = kDecodeMfmaWaves;  // MFMA units (waves) per workgroup
 
 // LDS of a workgroup of kMfmaWaves MFMA units: each wave's V staging area, reused by the merge.
 template <int D>
@@ -1007,9 +1009,47 @@ hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hi
 
 }  // namespace
 
-bool decode_supported(int32_t head_dim, int32_t group)
+// Decode scratch for callers that cannot allocate (pa_decode_noalloc): a file-scope device array,
+// one copy per GPU at its own address, held from the library's first use on that GPU until the
+// process ends. Host code never passes the array's name to a kernel: in host code that name is a
+// host-side stand-in. It uses the address hipGetSymbolAddress returns on each device instead.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device ordinal; null until looked up
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void **ptr)
 {
-    return (head_dim == 64 || head_dim == 128) && group >= 1;
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // the lookup needs the stream's device current; the caller's current device is restored
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return e;
+        if (back != hipSuccess)
+            return back;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
@@ -1028,8 +1068,6 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.block_tables = d.block_tables;
     p.seq_lens = d.seq_lens;
     p.out = (uint16_t *)d.out;
-    p.ws_acc = d.ws_acc;
-    p.ws_ml = d.ws_ml;
     p.max_blocks = d.max_blocks;
     p.num_seqs = d.num_seqs;
     p.num_kv_heads = d.c.num_kv_heads;
@@ -1050,18 +1088,24 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     const int own_slots = (p.max_parts + p.wg_parts - 1) / p.wg_parts;
     p.ws_slots = own_slots;
     p.ws_rows = d.num_seqs * d.num_q_heads;
-
-    DecodeParams pre;
+    int pre_slots = 0;
     if (cascade) {
         // slots [0, pre_slots) of every row hold shared-prefix results (kMfmaWaves parts each),
         // the rest its own parts
         const int pre_parts = (d.max_prefix_len + d.partition_size - 1) / d.partition_size;
-        const int pre_slots = (pre_parts + kMfmaWaves - 1) / kMfmaWaves;
+        pre_slots = (pre_parts + kMfmaWaves - 1) / kMfmaWaves;
+        p.ws_slots = pre_slots + own_slots;
+    }
+    // workspace: acc [slots][rows][D], then (m, l) [rows][slots][2]
+    p.ws_acc = (float *)d.workspace;
+    p.ws_ml = p.split ? p.ws_acc + (size_t)p.ws_rows * p.ws_slots * d.c.head_dim : nullptr;
+
+    DecodeParams pre;
+    if (cascade) {
         p.seq_starts = d.seq_starts;
         p.pre_slots = pre_slots;
         p.pre_slot_tokens = d.partition_size * kMfmaWaves;
         p.slot_base = pre_slots;
-        p.ws_slots = pre_slots + own_slots;
         pre = p;
         pre.group_starts = d.group_starts;
         pre.num_groups = d.num_groups;

@@ -198,7 +198,8 @@ pa_status_t decode_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_hea
                         int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
                         int32_t max_seq_len, int32_t num_q_heads, float scale,
                         int32_t partition_size, void *workspace, size_t workspace_bytes,
-                        void *stream, bool fp8, float k_scale, float v_scale)
+                        void *stream, bool fp8, float k_scale, float v_scale,
+                        bool use_scratch = false)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -230,13 +231,30 @@ pa_status_t decode_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_hea
     REQUIRE_PTR(v_cache, "v_cache");
     REQUIRE(block_tables != nullptr, "block_tables is NULL");
     REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
-    const size_t need =
-        pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
-    if (need > 0) {
-        if (workspace == nullptr || workspace_bytes < need)
-            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
-                        need);
-        REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    if (use_scratch) {
+        // the library's static scratch instead of a caller's workspace: no allocation anywhere
+        const size_t used = pa::decode_workspace_used(num_seqs, num_q_heads, num_kv_heads,
+                                                      head_dim, max_seq_len, partition_size);
+        if (used > pa::kDecodeScratchBytes)
+            return fail(PA_ERR_WORKSPACE,
+                        "partial results need %zu bytes, above the %zu-byte static scratch "
+                        "(use pa_decode with a workspace, or a larger partition_size)",
+                        used, pa::kDecodeScratchBytes);
+        workspace = nullptr;
+        if (used > 0) {
+            const hipError_t e = pa::decode_scratch((hipStream_t)stream, &workspace);
+            if (e != hipSuccess)
+                return fail(PA_ERR_HIP, "decode scratch lookup: %s", hipGetErrorString(e));
+        }
+    } else {
+        const size_t need =
+            pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
+        if (need > 0) {
+            if (workspace == nullptr || workspace_bytes < need)
+                return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed",
+                            workspace_bytes, need);
+            REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+        }
     }
     pa::DecodeLaunch d;
     d.c = c;
@@ -258,9 +276,7 @@ pa_status_t decode_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_hea
     d.num_groups = 0;
     d.max_group_size = 0;
     d.max_prefix_len = 0;
-    d.ws_acc = (float *)workspace;
-    d.ws_ml = need ? (float *)workspace + (size_t)num_seqs * num_q_heads * d.max_parts * head_dim
-                   : nullptr;
+    d.workspace = workspace;
     d.fp8 = fp8;
     d.c.fp8 = fp8;
     d.k_scale = k_scale;
@@ -284,6 +300,19 @@ pa_status_t pa_decode(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads
                        block_tables, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
                        num_q_heads, scale, partition_size, workspace, workspace_bytes, stream,
                        false, 1.0f, 1.0f);
+}
+
+pa_status_t pa_decode_noalloc(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                              int32_t head_dim, void *out, const void *query, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                              int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                              float scale, int32_t partition_size, void *stream)
+{
+    return decode_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                       num_q_heads, scale, partition_size, nullptr, 0, stream, false, 1.0f, 1.0f,
+                       true);
 }
 
 pa_status_t pa_decode_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
@@ -397,10 +426,7 @@ pa_status_t shared_prefix_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num
         d.seq_starts = nullptr;
         d.max_prefix_len = 0;
     }
-    // workspace: acc [rows][slots][D], then (m, l) [rows][slots][2]; slots = prefix parts + own
-    const int32_t slots = (d.max_prefix_len + partition_size - 1) / partition_size + own;
-    d.ws_acc = (float *)workspace;
-    d.ws_ml = (float *)workspace + (size_t)num_seqs * num_q_heads * slots * head_dim;
+    d.workspace = workspace;
     d.fp8 = fp8;
     d.c.fp8 = fp8;
     d.k_scale = k_scale;

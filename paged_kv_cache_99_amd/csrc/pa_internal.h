@@ -51,8 +51,9 @@ struct DecodeLaunch {
     int32_t num_q_heads;
     float scale;
     int32_t partition_size;  // 0 = unsplit
-    float *ws_acc;           // [num_seqs][num_q_heads][max_parts][head_dim]
-    float *ws_ml;            // [num_seqs][num_q_heads][slots][2]
+    // fp32 scratch of the partial results, laid out by launch_decode: acc [slots][rows][head_dim]
+    // then (m, l) [rows][slots][2], rows = num_seqs * num_q_heads; decode_workspace_used bytes
+    void *workspace;
     int32_t max_parts;       // own parts per sequence (0 = unsplit)
     // shared-prefix (cascade) decode; group_starts == nullptr for a plain decode
     const int32_t *seq_starts;    // [num_seqs] shared-prefix length of each sequence
@@ -65,9 +66,21 @@ struct DecodeLaunch {
     float k_scale = 1.0f;
     float v_scale = 1.0f;
 };
+// Host-side shape logic (pa_shapes.cpp) ------------------------------------------------------
+// The MFMA decode (head groups of 3 or more) runs workgroups of this many waves, and in a split
+// decode each workgroup merges that many consecutive parts into one workspace slot.
+constexpr int kDecodeMfmaWaves = 4;
 // Group sizes with a dedicated kernel; any other group size runs as several of these.
 bool decode_supported(int32_t head_dim, int32_t group);
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+// Bytes of workspace a plain (unshared) decode of these sizes writes and reads: one fp32 partial
+// (head_dim + 2 floats) per (sequence, query head, slot). At most pa_decode_workspace_size.
+size_t decode_workspace_used(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_seq_len, int32_t partition_size);
+// The library's static decode scratch (kDecodeScratchBytes) on the device that runs `stream`
+// (the current device for the null stream): its address there, looked up once per device.
+constexpr size_t kDecodeScratchBytes = PA_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(hipStream_t stream, void **ptr);
 
 // prefill.hip
 struct PrefillLaunch {
@@ -90,7 +103,7 @@ struct PrefillLaunch {
     float k_scale = 1.0f;
     float v_scale = 1.0f;
 };
-bool prefill_supported(int32_t head_dim, int32_t group);
+bool prefill_supported(int32_t head_dim, int32_t group);  // pa_shapes.cpp
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 
 }  // namespace pa

@@ -812,11 +812,6 @@ hipError_t launch_gk(int gk, const PrefillParams &p, bool fp8, hipStream_t strea
 
 }  // namespace
 
-bool prefill_supported(int32_t head_dim, int32_t group)
-{
-    return (head_dim == 64 || head_dim == 128) && group >= 1;
-}
-
 hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
 {
     if (d.num_seqs == 0 || d.total_q == 0 || d.max_q_len == 0)

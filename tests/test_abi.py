@@ -162,3 +162,28 @@ def test_fp8_entry_points_reject_bad_arguments():
     small = list(dec)
     small[12], small[17], small[9] = 4096, 512, 256
     assert lib.pa_decode_fp8(*small) == WORKSPACE
+
+
+def test_noalloc_decode_checks_its_scratch_limit_on_the_host():
+    """pa_decode_noalloc has pa_decode's checks, and refuses sizes whose partial results exceed its
+    static scratch before anything is enqueued (no device is touched here)."""
+    lib = binding.lib()
+    f = ctypes.c_float
+
+    def call(num_seqs, num_q_heads, num_kv_heads, max_seq_len, part, **kw):
+        a = dict(dtype=F16, out=FAKE, partition_size=part)
+        a.update(kw)
+        return lib.pa_decode_noalloc(a["dtype"], 100, num_kv_heads, 128, a["out"], FAKE, FAKE,
+                                     FAKE, FAKE, 2048, FAKE, num_seqs, max_seq_len, num_q_heads,
+                                     f(0.088), a["partition_size"], None)
+
+    assert binding.DECODE_SCRATCH_BYTES == 64 << 20
+    # 512 x 8 rows, head groups of 1 (one part per slot), 64 parts of 512 tokens: 136 MB
+    assert call(512, 8, 8, 32768, 512) == WORKSPACE
+    assert b"static scratch" in lib.pa_last_error()
+    # the same rows in head groups of 8 merge four parts per slot: 34 MB, within the limit, so
+    # only the argument checks decide (a bad partition size, a null output)
+    assert call(512, 64, 8, 32768, 24) == INVALID
+    assert call(512, 64, 8, 32768, 512, out=None) == INVALID
+    assert call(512, 8, 8, 32768, 512, dtype=FP8) == INVALID
+    assert call(0, 8, 8, 32768, 512) == OK          # no sequences: a no-op
