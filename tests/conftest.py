@@ -8,8 +8,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def use_sanitized_libraries():
+    """The host-sanitizer test (test_host_sanitizers.py) re-runs CPU tests in a child process
+    against libraries built with the address and undefined-behaviour sanitizers, named by these
+    variables. Test runs only."""
+    lib, olib = os.environ.get("PA_TEST_SANITIZED_LIBPA"), os.environ.get("PA_TEST_SANITIZED_ORACLE")
+    if lib:
+        from paged_kv_cache_99_amd import binding
+        binding.LIB_PATH, binding._lib = lib, None
+    if olib:
+        import oracle
+        oracle._LIB_PATH, oracle._lib = olib, None
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    use_sanitized_libraries()
 
 
 def pytest_collection_modifyitems(config, items):
