@@ -12,13 +12,22 @@ Prints ONE JSON line:
   roofline     for the dominant kernel (decode): algorithmic bytes per launch / its average
                duration from HIP events recorded on the launch stream during the timed steps
                (timing-only events without the system-scope fence, see TimingEvents),
-               against the 8 TB/s HBM peak; traffic from the committed rocprofv3 counter summary
-               when it was taken on the current decode source, else null;
-  cpu_baseline the CPU oracle (float64) timed on this host over the full decode of the workload.
+               against the 8 TB/s HBM peak; traffic = HBM bytes per launch from the workload's
+               committed counter record (profiles/<workload>[_fp8]_traffic.json) when it was taken
+               on the current decode sources, else null;
+  roofline_prefill  (steps with a prefill chunk) the chunk's causal FLOPs / its event time against
+               the 2.5 PFLOP/s dense bf16 MFMA peak, with the MFMA-busy share of SIMD cycles from
+               the committed counter record of the current prefill sources, else null;
+  step_tokens_per_s  query tokens the step attends for (decode sequences + prefill rows) / step
+               time: the mixed step's 2048-token budget per step;
+  cpu_baseline the CPU oracle (float64) timed on this host over the workload's decode (a bounded
+               sample when it is long); cpu_baseline_prefill the oracle's prefill over a sample of
+               chunk rows, in GFLOP/s.
   decode_ms, prefill_ms: mean of the per-call event times (their 10th/50th/90th percentiles
-               beside them). Decode contexts are far larger than the 256 MB Infinity Cache, so each
-               step reads them from HBM; --evict-mb 512 also displaces every cache level before
-               each timed decode, to show that.
+               beside them; decode_us_per_call the same mean in microseconds). Decode contexts are
+               far larger than the 256 MB Infinity Cache, so each step reads them from HBM;
+               --evict-mb 512 also displaces every cache level before each timed decode, to show
+               that.
 
 Algorithmic bytes (what the method must move, per stage; E = 2 bytes per cache element, 1 with
 --kv-cache fp8, whose caches hold E4M3 codes):
@@ -43,9 +52,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_99_amd", "csrc", f)
-               for f in ("decode.hip", "pa_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_traffic.json")
+CSRC = os.path.join(ROOT, "paged_kv_cache_99_amd", "csrc")
+# sources of the decode kernels and of the prefill kernel: a committed counter record quotes the
+# hash of the sources it was taken on, and is used only while that hash matches
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "pa_device.h", "pa_internal.h")]
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill.hip", "pa_device.h", "pa_internal.h")]
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def decode_bytes(w, esize=2):
@@ -99,16 +111,21 @@ def src_hash(paths):
     return h.hexdigest()[:16]
 
 
-def committed_traffic(per_launch_algorithmic):
-    """HBM bytes per decode launch from the committed counter summary, if it matches the source."""
+def record_tag(workload, fp8, shared_prefix_read_once):
+    """Name of a workload's counter records under profiles/: <workload>[_fp8][_per_sequence]."""
+    meta_shared = workload.startswith("prefix_sharing")
+    return workload + ("_fp8" if fp8 else "") + \
+        ("_per_sequence" if meta_shared and not shared_prefix_read_once else "")
+
+
+def committed_record(tag, kind, srcs):
+    """profiles/<tag>_<kind>.json when its recorded source hash matches the current sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+        with open(os.path.join(PROFILES, f"{tag}_{kind}.json")) as f:
+            rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("decode_src_sha256_16") != src_hash(DECODE_SRCS):
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return rec if rec.get("src_sha256_16") == src_hash(srcs) else None
 
 
 def cpu_model():
@@ -171,6 +188,50 @@ def cpu_baseline(w, max_seconds, fp8=None):
             "cpu_model": cpu_model(),
             "single_thread": {"value": round(b1 / e1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"{n1} of {nd} sequences in {e1:.2f} s"}}
+
+
+def cpu_baseline_prefill(w, max_seconds, fp8=None):
+    """The float64 oracle's prefill of a sample of the workload's chunk rows (every query head of
+    each sampled row), on every host thread, grown until it passes max_seconds; rate in GFLOP/s of
+    the causal attention it computed (4 * D per visible key and (row, head))."""
+    import oracle
+    nd = w.n_decode
+    cu = np.asarray(w.cu_q_lens, np.int64)
+    total = int(cu[-1])
+    threads = oracle.max_threads()
+    lens = w.seq_lens[nd:].astype(np.int64)
+    if fp8 is not None:
+        k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, fp8[0])
+        v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, fp8[1])
+
+    def visible(r):  # keys row r attends
+        s = int(np.searchsorted(cu, r, side="right") - 1)
+        return int(lens[s] - (cu[s + 1] - cu[s]) + (r - cu[s]) + 1)
+
+    n_rows, elapsed, flops = 8, 0.0, 0
+    while True:
+        rows = np.unique(np.linspace(0, total - 1, min(n_rows, total)).astype(np.int64))
+        pairs = np.array([(r, h) for r in rows for h in range(w.H_q)], np.int32)
+        t0 = time.perf_counter()
+        if fp8 is None:
+            oracle.prefill(w.query_prefill, w.k_cache, w.v_cache, w.block_tables[nd:],
+                           w.seq_lens[nd:], w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks,
+                           w.dtype, w.scale, rows=pairs)
+        else:
+            oracle.prefill_fp8(w.query_prefill, k8, v8, w.block_tables[nd:], w.seq_lens[nd:],
+                               w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale,
+                               fp8[0], fp8[1], rows=pairs)
+        elapsed = time.perf_counter() - t0
+        flops = sum(4 * w.D * w.H_q * visible(int(r)) for r in rows)
+        if elapsed > max_seconds / 4 or len(rows) >= total:
+            break
+        n_rows *= 2
+    return {"value": round(flops / elapsed / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 oracle prefill of {len(rows)} of {total} chunk rows (evenly "
+                      f"spaced) x {w.H_q} query heads, {flops / 1e9:.2f} GFLOP of causal "
+                      f"attention, in {elapsed:.2f} s, pool before the step's scatter",
+            "seconds": round(elapsed, 3)}
 
 
 class TimingEvents:
@@ -270,7 +331,8 @@ def main():
     ap.add_argument("--k-scale", type=float, default=0.03, help="E4M3 key scale")
     ap.add_argument("--v-scale", type=float, default=0.02, help="E4M3 value scale")
     ap.add_argument("--print-decode-src-hash", action="store_true",
-                    help="print the hash of the decode sources (recorded with counter summaries)")
+                    help="print the hashes of the decode and of the prefill sources (recorded "
+                         "with counter summaries)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="PAIRS",
                     help="after timing, copy PAIRS whole blocks with pa_copy_blocks (a plain copy of "
                          "known size, for scaling HBM byte counters)")
@@ -280,7 +342,7 @@ def main():
                          "the previous step; 512 exceeds the 256 MB Infinity Cache twice over")
     args = ap.parse_args()
     if args.print_decode_src_hash:
-        print(src_hash(DECODE_SRCS))
+        print(src_hash(DECODE_SRCS), src_hash(PREFILL_SRCS))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -352,7 +414,10 @@ def main():
     step_bytes = u_bytes + scatter_bytes(w, esize) + copy_bytes(w, esize) + p_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_gbs = u_bytes / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0
-    traffic = committed_traffic(d_bytes) if w.name == "llama2_7b_decode" and not fp8 else None
+    tag = record_tag(w.name, fp8, g.shared_prefix)
+    trec = committed_record(tag, "traffic", DECODE_SRCS) if g.n_decode else None
+    traffic = trec.get("hbm_bytes_per_launch") if trec else None
+    step_tokens = int(w.n_decode) + int(g.pre_query.shape[0])
     out = {
         "metric": "pa_decode HBM GB/s (% of 8 TB/s peak) + decode tokens/s, 7B-shaped layer",
         "value": round(value, 2),
@@ -383,7 +448,10 @@ def main():
             "evict_mb": args.evict_mb,
         },
         "decode_tokens_per_s": round(w.n_decode / (ms_per_step * 1e-3), 1),
+        "step_tokens": step_tokens,
+        "step_tokens_per_s": round(step_tokens / (ms_per_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 5),
+        "decode_us_per_call": round(dec_ms * 1e3, 2),
         "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_t, [10, 50, 90])],
         "decode_GBps": round(dec_gbs, 2),
         "pct_of_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
@@ -410,9 +478,19 @@ def main():
                                          for x in np.percentile(pre_t, [10, 50, 90])]
         out["prefill_TFLOPs"] = round(p_flops / (pre_ms * 1e-3) / 1e12, 2)
         out["prefill_mfma_frac"] = round(p_flops / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        crec = committed_record(tag, "prefill_counters", PREFILL_SRCS)
+        out["roofline_prefill"] = {
+            "bound": "mfma", "kernel": "pa_prefill_chunk" + ("_fp8" if fp8 else ""),
+            "achieved": out["prefill_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": out["prefill_mfma_frac"], "flops_per_launch": int(p_flops),
+            # MFMA-busy share of SIMD cycles from the committed counter record of these sources
+            "mfma_busy_counter": crec.get("mfma_busy_frac") if crec else None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
                                            (args.k_scale, args.v_scale) if fp8 else None)
+        if has_prefill:
+            out["cpu_baseline_prefill"] = cpu_baseline_prefill(
+                w, args.cpu_seconds, (args.k_scale, args.v_scale) if fp8 else None)
     print(json.dumps(out), flush=True)
 
 

@@ -31,7 +31,8 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("workload,cpu", [("tiny_decode", True), ("chunked_prefill_mixed", False)])
+@pytest.mark.parametrize("workload,cpu", [("tiny_decode", True), ("chunked_prefill_mixed", True),
+                                          ("llama2_7b_decode", False)])
 def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys):
     args = ["--workload", workload, "--steps", "3", "--warmup", "1", "--cpu-seconds", "2"]
     if not cpu:
@@ -52,10 +53,23 @@ def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys)
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     p10, p50, p90 = d["decode_ms_p10_p50_p90"]
     assert 0 < p10 <= p50 <= p90
+    nd = d["config"]["num_seqs"]
+    assert d["step_tokens"] == nd + d["config"]["prefill_rows"]
+    assert abs(d["step_tokens_per_s"] - d["step_tokens"] / (d["ms_per_step"] * 1e-3)) < 1
+    assert abs(d["decode_us_per_call"] - 1e3 * d["decode_ms"]) < 0.01
     if cpu:
         c = d["cpu_baseline"]
         assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
         assert c["single_thread"]["value"] > 0
     else:
         assert "cpu_baseline" not in d
+    if d["config"]["prefill_rows"]:
+        assert d["step_tokens"] == 2048            # the mixed step's token budget
         assert d["prefill_ms"] > 0 and 0 < d["prefill_mfma_frac"] < 1
+        rp = d["roofline_prefill"]
+        assert rp["bound"] == "mfma" and rp["peak"] == 2500.0 and rp["frac"] == d["prefill_mfma_frac"]
+        if cpu:
+            cp = d["cpu_baseline_prefill"]
+            assert cp["kind"] == "oracle" and cp["unit"] == "GFLOP/s" and cp["value"] > 0
+    else:
+        assert "roofline_prefill" not in d and "cpu_baseline_prefill" not in d
