@@ -165,9 +165,13 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partitio
                                               partition_size))
 
 
-def default_partition_size(max_seq_len: int) -> int:
-    """Split long contexts into 512-token parts; short ones run unsplit."""
-    return 512 if max_seq_len > 512 else 0
+def default_partition_size(max_seq_len: int, group: int = 1) -> int:
+    """Tokens per split-K part for pa_decode: short contexts run unsplit; head groups of 1-2
+    (the vector-ALU kernel) take 1024-token parts over contexts of more than 2048 tokens, where
+    the library runs eight-wave units on them; everything else 512-token parts."""
+    if max_seq_len <= 512:
+        return 0
+    return 1024 if group <= 2 and max_seq_len > 2048 else 512
 
 
 def alloc_decode_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size,
@@ -193,7 +197,7 @@ def decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: in
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
     if partition_size is None:
-        partition_size = default_partition_size(max_seq_len)
+        partition_size = default_partition_size(max_seq_len, hq // hkv)
     need = decode_workspace_size(B, hq, d, max_seq_len, partition_size)
     if need and workspace is None:
         workspace = alloc_decode_workspace(B, hq, d, max_seq_len, partition_size, query.device)
@@ -220,7 +224,7 @@ def decode_noalloc(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
     if partition_size is None:
-        partition_size = default_partition_size(max_seq_len)
+        partition_size = default_partition_size(max_seq_len, hq // hkv)
     _check(lib().pa_decode_noalloc(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
                                    k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
                                    int(block_tables.shape[1]), seq_lens.data_ptr(), B,
@@ -397,7 +401,7 @@ def decode_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
     if partition_size is None:
-        partition_size = default_partition_size(max_seq_len)
+        partition_size = default_partition_size(max_seq_len, hq // hkv)
     need = decode_workspace_size(B, hq, d, max_seq_len, partition_size)
     if need and workspace is None:
         workspace = alloc_decode_workspace(B, hq, d, max_seq_len, partition_size, query.device)

@@ -10,8 +10,8 @@
 // are combined by rescaling to the common maximum (devpress.csdn.net/amd vLLM overview, §9 (4)
 // online softmax; §3 (3) per-block accumulation over the block table).
 //
-// Vector-ALU kernel. Work unit: one workgroup of kUnitWaves wavefronts per (sequence, kv head,
-// query-head subgroup, partition); wave w takes blocks w, w + kUnitWaves, ... of the unit's range,
+// Vector-ALU kernel. Work unit: one workgroup of UW (4 or 8) wavefronts per (sequence, kv head,
+// query-head subgroup, partition); wave w takes blocks w, w + UW, ... of the unit's range,
 // and the waves' results are merged through LDS at the end (a unit then takes a quarter of the
 // time, which shortens the tail of batches with few, uneven units). A (block, kv head) tile is
 // 16 rows x D contiguous 16-bit words (4 KiB at D = 128). Lane l of the wave
@@ -108,14 +108,19 @@ __device__ __forceinline__ int unit_part(const DecodeParams &p, int r, int n)
 }
 
 // F8: the caches hold E4M3 codes (one byte per element) instead of 16-bit elements.
-// Waves per unit of the vector-ALU kernel. Measured on the 7B-shaped layer and on 256 sequences
-// of U{1..512} tokens: 1 wave per unit (two units per workgroup) 76.7 % / 70.5 % of 8 TB/s, 2 waves
-// 77.3 % / 74.3 %, 4 waves 77.5 % / 76.7 %; 8 waves lost on E4M3 caches (66 %).
-constexpr int kUnitWaves = 4;
+// UW: waves per unit of the vector-ALU kernel. Four suit units of up to 512 tokens: measured on
+// the 7B-shaped layer (512-token parts) and on 256 sequences of U{1..512} tokens, 1 wave per unit
+// (two units per workgroup) 76.7 % / 70.5 % of 8 TB/s, 2 waves 77.3 % / 74.3 %, 4 waves 77.5 % /
+// 76.7 %. Eight suit 16-bit units of 1024 tokens or more -- each wave still streams eight blocks
+// while the units, partials and merge work halve: 7B-shaped layer, 512-token parts with four waves
+// 408.8-409.2 µs, 1024-token parts with eight 396.6-398.9 µs. E4M3 units keep four (eight lost,
+// 66 %), and so do shared-prefix own ranges (eight: 388 → 419 µs).
+constexpr int kUnitWavesMax = 8;
 
-template <bool BF, bool F8, int D, int GK>
-__global__ __launch_bounds__(64 * kUnitWaves) void decode_partition_kernel(DecodeParams p)
+template <bool BF, bool F8, int D, int GK, int UW>
+__global__ __launch_bounds__(64 * UW) void decode_partition_kernel(DecodeParams p)
 {
+    constexpr int kUnitWaves = UW;
     constexpr int EPL = F8 ? 16 : 8;     // cache elements per 16-byte piece = dims per lane
     constexpr int RL = D / EPL;          // lanes per token row
     constexpr int ROWS = kWave / RL;     // token rows per 1 KiB load
@@ -980,9 +985,12 @@ hipError_t launch_units(const DecodeParams &p, hipStream_t stream)
                                               ? p.n_units
                                               : (p.n_units + kMfmaWaves - 1) / kMfmaWaves)),
                            dim3(kWave * kMfmaWaves), 0, stream, p);
+    else if (!F8 && p.part_tokens >= 1024)
+        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK, kUnitWavesMax>),
+                           dim3(round_up8(p.n_units)), dim3(kWave * kUnitWavesMax), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK>), dim3(round_up8(p.n_units)),
-                           dim3(kWave * kUnitWaves), 0, stream, p);
+        hipLaunchKernelGGL((decode_partition_kernel<BF, F8, D, GK, 4>), dim3(round_up8(p.n_units)),
+                           dim3(kWave * 4), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -113,14 +113,16 @@ class GpuStep:
         self.max_seq_len = int(np.max(w.seq_lens[:nd])) if nd else 0
         if partition_size is None:
             partition_size = getattr(w, "partition_size", None)
+        meta = getattr(w, "meta", {}) or {}
+        self.shared_prefix = bool(shared_prefix and "group_starts" in meta and nd)
         if partition_size is None:
-            partition_size = binding.default_partition_size(self.max_seq_len)
+            # read-once shared prefixes keep 512-token parts: their own-token ranges are short
+            partition_size = 512 if self.shared_prefix else binding.default_partition_size(
+                self.max_seq_len, w.H_q // w.H_kv)
         self.partition_size = int(partition_size)
         self.workspace = binding.alloc_decode_workspace(nd, w.H_q, w.D, self.max_seq_len,
                                                         self.partition_size, dev) if nd else None
         # read-once shared prefixes: groups of sequences that hold common leading blocks
-        meta = getattr(w, "meta", {}) or {}
-        self.shared_prefix = bool(shared_prefix and "group_starts" in meta and nd)
         if self.shared_prefix:
             gs = np.asarray(meta["group_starts"], np.int32)
             pl = np.asarray(meta["shared_prefix"], np.int32)[:nd]
