@@ -5,7 +5,8 @@ are not powers of two), head_dim 64 or 128, fp16 or bf16, 1-11 decode sequences 
 often 1-3 prefill chunks of 1-299 rows over 0-1499 cached tokens, a partition size (library
 default, unsplit, 16, 256, 512 or 1024), and E4M3 scales. The whole step runs on the GPU (copy,
 scatter, decode, prefill) and every output row is compared with the float64 oracle on the pool after
-the step's scatter, within the element-wise attention gate (short contexts give outputs near 1).
+the step's scatter, within the attention gate of the output type (short contexts give outputs near
+1, where a bf16 output's own rounding is up to 2^-8 |ref|).
 """
 import numpy as np
 import pytest
@@ -23,13 +24,13 @@ GROUPS = [(4, 4), (8, 8), (16, 8), (32, 8), (12, 4), (6, 2), (24, 8), (10, 2), (
 PARTS = [None, 0, 16, 256, 512, 1024]
 
 
-def draw_case(case):
+def draw_case(case, max_len=3000):
     rng = np.random.default_rng(9100 + case)
     H_q, H_kv = GROUPS[rng.integers(len(GROUPS))]
     D = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
     n_dec = int(rng.integers(1, 12))
-    lens = rng.integers(1, int(rng.choice([64, 700, 3000])), size=n_dec).tolist()
+    lens = rng.integers(1, int(rng.choice([64, 700, max_len])), size=n_dec).tolist()
     q_lens = []
     if rng.random() < 0.6:
         n_pre = int(rng.integers(1, 4))
@@ -44,7 +45,12 @@ def draw_case(case):
 
 @pytest.mark.parametrize("case", range(24))
 def test_random_step_matches_oracle(case):
-    w, (ks, vs) = draw_case(case)
+    check_case(case)
+
+
+def check_case(case, max_len=3000):
+    """One seeded random step on the GPU, 16-bit and E4M3 caches, against the oracle."""
+    w, (ks, vs) = draw_case(case, max_len)
     nd = w.n_decode
     tag = (f"case {case}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} decodes={nd} "
            f"chunks={np.diff(w.cu_q_lens).tolist() if len(w.cu_q_lens) else []} "
