@@ -178,7 +178,12 @@ pa_status_t pa_decode_noalloc(pa_dtype_t dtype, int32_t num_blocks, int32_t num_
  * sequence's remaining positions by itself, and the parts are merged by rescaling with their
  * maxima and sums of exponentials ([OV] §9 (4)). out equals pa_decode's definition.
  *   Arguments as in pa_decode, plus group_starts [num_groups + 1], prefix_lens [num_seqs],
- *   max_group_size (>= every group's size, <= 64) and max_prefix_len (>= every prefix_lens).
+ *   max_group_size (>= every group's size, <= 64), max_prefix_len (>= every prefix_lens) and
+ *   max_own_len: an upper bound on every sequence's own range, seq_lens[s] - prefix_lens[s]
+ *   (<= 0: max_seq_len). It sizes the launch of the own-range units: a tight bound skips launching
+ *   units past every own range, and when every own range fits one part of head groups of 1 or 2,
+ *   each own unit also folds in its row's shared-prefix partials and writes the output (no merge
+ *   pass). Own ranges longer than it give unspecified output, never a fault.
  *   partition_size must be a multiple of 16 in [16, 1024]; workspace of at least
  *   pa_decode_shared_prefix_workspace_size(...) bytes.
  */
@@ -194,8 +199,9 @@ pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_
                                     int32_t max_seq_len, const int32_t *group_starts,
                                     const int32_t *prefix_lens, int32_t num_groups,
                                     int32_t max_group_size, int32_t max_prefix_len,
-                                    int32_t num_q_heads, float scale, int32_t partition_size,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+                                    int32_t max_own_len, int32_t num_q_heads, float scale,
+                                    int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /*
  * pa_prefill_chunk -- causal attention of prefill chunks over their paged context.
@@ -298,9 +304,10 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
                                         int32_t num_seqs, int32_t max_seq_len,
                                         const int32_t *group_starts, const int32_t *prefix_lens,
                                         int32_t num_groups, int32_t max_group_size,
-                                        int32_t max_prefix_len, int32_t num_q_heads, float scale,
-                                        float k_scale, float v_scale, int32_t partition_size,
-                                        void *workspace, size_t workspace_bytes, void *stream);
+                                        int32_t max_prefix_len, int32_t max_own_len,
+                                        int32_t num_q_heads, float scale, float k_scale,
+                                        float v_scale, int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *pa_status_string(pa_status_t status);

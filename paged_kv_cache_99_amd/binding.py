@@ -68,11 +68,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_shared_prefix_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
         L.pa_decode_shared_prefix.restype = _i
         L.pa_decode_shared_prefix.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i,
-                                              _p, _p, _i, _i, _i, _i, _f, _i, _p, _sz, _p]
+                                              _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]
         L.pa_decode_shared_prefix_fp8.restype = _i
         L.pa_decode_shared_prefix_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i,
-                                                  _i, _p, _p, _i, _i, _i, _i, _f, _f, _f, _i, _p,
-                                                  _sz, _p]
+                                                  _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                                  _p, _sz, _p]
         L.pa_reshape_and_cache_fp8.restype = _i
         L.pa_reshape_and_cache_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _f, _f, _p]
         L.pa_decode_fp8.restype = _i
@@ -241,7 +241,7 @@ def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim, max_seq
 
 def _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
                         group_starts, prefix_lens, max_group_size, max_prefix_len,
-                        partition_size, workspace, fp8):
+                        partition_size, workspace, fp8, max_own_len=0):
     """Checked arguments of pa_decode_shared_prefix{,_fp8} up to num_q_heads, and the workspace
     (pointer, bytes)."""
     _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=fp8)
@@ -269,19 +269,22 @@ def _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens, ma
     args = (dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(),
             v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
             seq_lens.data_ptr(), B, int(max_seq_len), group_starts.data_ptr(),
-            prefix_lens.data_ptr(), max(G, 0), int(max_group_size), int(max_prefix_len), hq)
+            prefix_lens.data_ptr(), max(G, 0), int(max_group_size), int(max_prefix_len),
+            int(max_own_len), hq)
     return args, ws
 
 
 def decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
                          group_starts, prefix_lens, max_group_size: int, max_prefix_len: int,
                          scale: float, partition_size: int = 512,
-                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                         workspace: Optional[torch.Tensor] = None, stream=None,
+                         max_own_len: int = 0) -> None:
     """pa_decode_shared_prefix: pa_decode whose groups of sequences (group_starts [G+1], int32)
-    read their common leading blocks (prefix_lens [B], int32) once."""
+    read their common leading blocks (prefix_lens [B], int32) once. max_own_len bounds every
+    seq_lens[s] - prefix_lens[s] (0: max_seq_len)."""
     args, ws = _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens,
                                    max_seq_len, group_starts, prefix_lens, max_group_size,
-                                   max_prefix_len, partition_size, workspace, False)
+                                   max_prefix_len, partition_size, workspace, False, max_own_len)
     _check(lib().pa_decode_shared_prefix(*args, float(scale), int(partition_size), *ws,
                                          _stream(stream)))
 
@@ -290,12 +293,12 @@ def decode_shared_prefix_fp8(out, query, k_cache, v_cache, block_tables, seq_len
                              max_seq_len: int, group_starts, prefix_lens, max_group_size: int,
                              max_prefix_len: int, scale: float, k_scale: float, v_scale: float,
                              partition_size: int = 512, workspace: Optional[torch.Tensor] = None,
-                             stream=None) -> None:
+                             stream=None, max_own_len: int = 0) -> None:
     """pa_decode_shared_prefix_fp8: decode_shared_prefix over E4M3 caches (uint8 or
     float8_e4m3fn; elements = code value * k_scale / v_scale)."""
     args, ws = _shared_prefix_args(out, query, k_cache, v_cache, block_tables, seq_lens,
                                    max_seq_len, group_starts, prefix_lens, max_group_size,
-                                   max_prefix_len, partition_size, workspace, True)
+                                   max_prefix_len, partition_size, workspace, True, max_own_len)
     _check(lib().pa_decode_shared_prefix_fp8(*args, float(scale), float(k_scale), float(v_scale),
                                              int(partition_size), *ws, _stream(stream)))
 

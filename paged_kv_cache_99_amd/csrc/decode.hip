@@ -75,10 +75,14 @@ struct DecodeParams {
     int32_t ws_rows;      // (sequence, head) rows: num_seqs * num_q_heads
     int32_t wg_parts;     // MFMA kernel: parts merged per workgroup (1 or kMfmaWaves)
     int32_t slot_tokens;  // tokens of a row's own workspace slot: part_tokens * wg_parts
-    int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: part_tokens * kMfmaWaves
+    int32_t pre_part_tokens;  // tokens per wave of a shared-prefix workgroup (partition_size)
+    int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: pre_part_tokens * kMfmaWaves
     int32_t slot_base;    // first slot these units write
     int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix results (merge)
     int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
+    // shared-prefix decode whose own ranges all fit one part (vector-ALU units): each own unit
+    // folds its row's shared-prefix partials in and writes the output, and no merge kernel runs
+    int32_t fused_finish;
 };
 
 // Position range of unit `part` of a sequence: [start + part*P, min(L, start + (part+1)*P)).
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(64 * UW) void decode_partition_kernel(DecodeParams 
 
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int t0 = unit_start(p, seq, L) + part * p.part_tokens;
-    if (p.split && t0 >= L)
+    if (p.split && t0 >= L && !p.fused_finish)
         return;  // a part with no tokens: the merge never reads it (uniform)
     const int t1 = min(L, t0 + p.part_tokens);
 
@@ -353,7 +357,46 @@ __global__ __launch_bounds__(64 * UW) void decode_partition_kernel(DecodeParams 
 #pragma unroll
         for (int h = 0; h < GK; ++h) {
             const size_t row = (size_t)seq * p.num_q_heads + h0 + h;
-            if (p.split) {
+            if (p.fused_finish) {
+                // the row's own tokens are this unit's range (its only part): fold in the row's
+                // shared-prefix partials, written by the prefix kernel that ran before this one
+                // on the stream, by rescaling to the common maximum, and write the output
+                const int n_pre = min((t0 + p.pre_slot_tokens - 1) / p.pre_slot_tokens, p.pre_slots);
+                const float *ml = p.ws_ml + row * p.ws_slots * 2;
+                float M = m[h];
+                for (int q = 0; q < n_pre; ++q)
+                    M = fmaxf(M, ml[2 * q]);
+                const float Ms = M == -INFINITY ? 0.0f : M;
+                const float f0 = fast_exp2(m[h] - Ms);
+                float W = l[h] * f0;
+                float o[EPL];
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    o[j] = acc[h][j] * f0;
+                for (int q = 0; q < n_pre; ++q) {
+                    const float fq = fast_exp2(ml[2 * q] - Ms);
+                    W += ml[2 * q + 1] * fq;
+                    const float *wa = p.ws_acc + ((size_t)q * p.ws_rows + row) * D + lane * EPL;
+#pragma unroll
+                    for (int j = 0; j < EPL; j += 4) {
+                        const float4 a = *(const float4 *)(wa + j);
+                        o[j] += a.x * fq;
+                        o[j + 1] += a.y * fq;
+                        o[j + 2] += a.z * fq;
+                        o[j + 3] += a.w * fq;
+                    }
+                }
+                const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+#pragma unroll
+                for (int j = 0; j < EPL; j += 8) {
+                    uint4 ov;
+                    ov.x = pack2<BF>(o[j] * inv, o[j + 1] * inv);
+                    ov.y = pack2<BF>(o[j + 2] * inv, o[j + 3] * inv);
+                    ov.z = pack2<BF>(o[j + 4] * inv, o[j + 5] * inv);
+                    ov.w = pack2<BF>(o[j + 6] * inv, o[j + 7] * inv);
+                    *(uint4 *)(p.out + row * D + lane * EPL + j) = ov;
+                }
+            } else if (p.split) {
                 const size_t slot = row * p.ws_slots + p.slot_base + part;
                 float *wa = p.ws_acc + ((size_t)(p.slot_base + part) * p.ws_rows + row) * D +
                             lane * EPL;
@@ -879,8 +922,8 @@ decode_prefix_mfma_kernel(DecodeParams p)
     const int prefix = min(max(p.seq_starts[first], 0), L0);
     if (q * p.pre_slot_tokens >= prefix)
         return;  // uniform: the slot holds no prefix tokens
-    const int t0 = min(prefix, (q * kMfmaWaves + w) * p.part_tokens);
-    const int t1 = min(prefix, t0 + p.part_tokens);
+    const int t0 = min(prefix, (q * kMfmaWaves + w) * p.pre_part_tokens);
+    const int t1 = min(prefix, t0 + p.pre_part_tokens);
     const int v = vsub * kCols + (threadIdx.x & 15);
     const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
     f32x4 o[D / 16];
@@ -1008,7 +1051,7 @@ hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hi
     e = gk == kCols ? launch_units<BF, F8, D, kCols>(p, stream)
         : gk == 2   ? launch_units<BF, F8, D, 2>(p, stream)
                     : launch_units<BF, F8, D, 1>(p, stream);
-    if (e != hipSuccess || !p.split)
+    if (e != hipSuccess || !p.split || p.fused_finish)
         return e;
     const int rows = p.num_seqs * p.num_q_heads;
     hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
@@ -1090,6 +1133,13 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (p.part_tokens < kBlock)
         p.part_tokens = kBlock;
     p.max_parts = p.split ? d.max_parts : 1;
+    // Shared prefixes on the vector-ALU kernel whose own ranges all fit 1024 tokens: one own part
+    // per row, as long as the longest own range, so that each own unit can finish its row (below)
+    const bool own_one_part = cascade && gk != kCols && d.max_own_len > 0 && d.max_own_len <= 1024;
+    if (own_one_part) {
+        p.part_tokens = (d.max_own_len + kBlock - 1) / kBlock * kBlock;
+        p.max_parts = 1;
+    }
     // split MFMA decode: kMfmaWaves consecutive parts per workgroup, merged into one slot
     p.wg_parts = gk == kCols && p.split ? kMfmaWaves : 1;
     p.slot_tokens = p.part_tokens * p.wg_parts;
@@ -1108,10 +1158,14 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     p.ws_acc = (float *)d.workspace;
     p.ws_ml = p.split ? p.ws_acc + (size_t)p.ws_rows * p.ws_slots * d.c.head_dim : nullptr;
 
+    // own ranges that all fit one part on the vector-ALU kernel finish their rows themselves
+    p.fused_finish = own_one_part ? 1 : 0;
+
     DecodeParams pre;
     if (cascade) {
         p.seq_starts = d.seq_starts;
         p.pre_slots = pre_slots;
+        p.pre_part_tokens = d.partition_size;
         p.pre_slot_tokens = d.partition_size * kMfmaWaves;
         p.slot_base = pre_slots;
         pre = p;

@@ -352,7 +352,8 @@ pa_status_t shared_prefix_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num
                                const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
                                const int32_t *group_starts, const int32_t *prefix_lens,
                                int32_t num_groups, int32_t max_group_size,
-                               int32_t max_prefix_len, int32_t num_q_heads, float scale,
+                               int32_t max_prefix_len, int32_t max_own_len,
+                               int32_t num_q_heads, float scale,
                                int32_t partition_size, void *workspace, size_t workspace_bytes,
                                void *stream, bool fp8, float k_scale, float v_scale)
 {
@@ -400,7 +401,10 @@ pa_status_t shared_prefix_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num
     if (workspace == nullptr || workspace_bytes < need)
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
     REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
-    const int32_t own = max_seq_len > 0 ? (max_seq_len + partition_size - 1) / partition_size : 1;
+    // own parts per sequence: enough for the longest own range (positions after the shared prefix)
+    const int32_t own_len =
+        max_own_len > 0 && max_own_len < max_seq_len ? max_own_len : max_seq_len;
+    const int32_t own = own_len > 0 ? (own_len + partition_size - 1) / partition_size : 1;
     pa::DecodeLaunch d;
     d.c = c;
     d.out = out;
@@ -421,6 +425,7 @@ pa_status_t shared_prefix_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num
     d.num_groups = num_groups;
     d.max_group_size = max_group_size;
     d.max_prefix_len = max_prefix_len;
+    d.max_own_len = own_len;
     if (d.group_starts == nullptr) {
         // no groups: a plain split decode (every prefix length must then be 0)
         d.seq_starts = nullptr;
@@ -447,14 +452,15 @@ pa_status_t pa_decode_shared_prefix(pa_dtype_t dtype, int32_t num_blocks, int32_
                                     int32_t max_seq_len, const int32_t *group_starts,
                                     const int32_t *prefix_lens, int32_t num_groups,
                                     int32_t max_group_size, int32_t max_prefix_len,
-                                    int32_t num_q_heads, float scale, int32_t partition_size,
-                                    void *workspace, size_t workspace_bytes, void *stream)
+                                    int32_t max_own_len, int32_t num_q_heads, float scale,
+                                    int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream)
 {
     return shared_prefix_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache,
                               v_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                               max_seq_len, group_starts, prefix_lens, num_groups, max_group_size,
-                              max_prefix_len, num_q_heads, scale, partition_size, workspace,
-                              workspace_bytes, stream, false, 1.0f, 1.0f);
+                              max_prefix_len, max_own_len, num_q_heads, scale, partition_size,
+                              workspace, workspace_bytes, stream, false, 1.0f, 1.0f);
 }
 
 pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
@@ -465,15 +471,16 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
                                         int32_t num_seqs, int32_t max_seq_len,
                                         const int32_t *group_starts, const int32_t *prefix_lens,
                                         int32_t num_groups, int32_t max_group_size,
-                                        int32_t max_prefix_len, int32_t num_q_heads, float scale,
-                                        float k_scale, float v_scale, int32_t partition_size,
-                                        void *workspace, size_t workspace_bytes, void *stream)
+                                        int32_t max_prefix_len, int32_t max_own_len,
+                                        int32_t num_q_heads, float scale, float k_scale,
+                                        float v_scale, int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream)
 {
     return shared_prefix_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache,
                               v_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                               max_seq_len, group_starts, prefix_lens, num_groups, max_group_size,
-                              max_prefix_len, num_q_heads, scale, partition_size, workspace,
-                              workspace_bytes, stream, true, k_scale, v_scale);
+                              max_prefix_len, max_own_len, num_q_heads, scale, partition_size,
+                              workspace, workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 }  // extern "C"

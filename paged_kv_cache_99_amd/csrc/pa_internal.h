@@ -61,6 +61,7 @@ struct DecodeLaunch {
     int32_t num_groups;
     int32_t max_group_size;
     int32_t max_prefix_len;
+    int32_t max_own_len = 0;      // bound on seq_lens - prefix lens (shared-prefix decode); 0: none
     // E4M3 caches (c.fp8): element = code value * k_scale / v_scale
     bool fp8 = false;
     float k_scale = 1.0f;

@@ -131,6 +131,8 @@ class GpuStep:
             self.prefix_lens = ints_to_device(pl, dev)
             self.max_group_size = int(np.max(np.diff(gs))) if len(gs) > 1 else 1
             self.max_prefix_len = int(pl.max()) if len(pl) else 0
+            # the longest own range (positions after the shared prefix) sizes the own units
+            self.max_own_len = int((np.asarray(w.seq_lens[:nd], np.int64) - pl).max())
             if self.partition_size == 0:
                 self.partition_size = 512
             self.workspace = torch.empty(max(16, binding.decode_shared_prefix_workspace_size(
@@ -176,7 +178,8 @@ class GpuStep:
                 self.dec_out, self.dec_query, self.k_cache, self.v_cache, self.dec_tables,
                 self.dec_lens, self.max_seq_len, self.group_starts, self.prefix_lens,
                 self.max_group_size, self.max_prefix_len, self.w.scale, self.k_scale,
-                self.v_scale, self.partition_size, self.workspace, stream)
+                self.v_scale, self.partition_size, self.workspace, stream,
+                max_own_len=self.max_own_len)
         elif self.n_decode and self.fp8:
             binding.decode_fp8(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
                                self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,
@@ -187,7 +190,8 @@ class GpuStep:
                                          self.dec_tables, self.dec_lens, self.max_seq_len,
                                          self.group_starts, self.prefix_lens,
                                          self.max_group_size, self.max_prefix_len, self.w.scale,
-                                         self.partition_size, self.workspace, stream)
+                                         self.partition_size, self.workspace, stream,
+                                         max_own_len=self.max_own_len)
         elif self.n_decode:
             binding.decode(self.dec_out, self.dec_query, self.k_cache, self.v_cache,
                            self.dec_tables, self.dec_lens, self.max_seq_len, self.w.scale,

@@ -356,3 +356,47 @@ def test_shared_prefix_decode_contract_breach_stays_in_bounds():
     torch.cuda.synchronize()
     assert_attention_close(words_from_device(g.dec_out), ref, w.dtype,
                            "shared-prefix decode after a contract breach")
+
+
+@pytest.mark.parametrize("kv", ["auto", "fp8"])
+def test_shared_prefix_own_range_bound(kv):
+    """max_own_len sizes the own-range units. With the exact bound (every own range of the
+    2040-token workload fits one part) each own unit folds in its row's prefix partials and writes
+    the output; with 0 (no bound) the own ranges run in 512-token parts and a merge pass combines
+    them. Both match the oracle. A bound below the longest own range is a contract breach: no error,
+    no access outside the arguments, and a valid call afterwards is exact."""
+    w = workload("prefix_sharing_2040")
+    ks, vs = 0.03, 0.02
+    if kv == "auto":
+        g = run_on_gpu(w, stages=("copy", "scatter"), shared_prefix=True)
+        kc, vc = oracle_pool_after_step(w)
+        ref = oracle_decode(w, kc, vc)
+        call = binding.decode_shared_prefix
+        extra = ()
+    else:
+        k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, ks)
+        v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, vs)
+        g = GpuStep(w, shared_prefix=True, kv_cache="fp8", k_scale=ks, v_scale=vs,
+                    fp8_pool=(k8, v8))
+        g.copy()
+        g.scatter()
+        torch.cuda.synchronize()
+        k8, v8 = oracle.copy_blocks_fp8(k8, v8, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+        k8, v8 = oracle.reshape_and_cache_fp8(w.new_key, w.new_value, k8, v8, w.slot_mapping,
+                                              w.num_blocks, w.H_kv, w.D, w.dtype, ks, vs)
+        nd = w.n_decode
+        ref = oracle.decode_fp8(w.query_decode, k8, v8, w.block_tables[:nd], w.seq_lens[:nd],
+                                w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+        call = binding.decode_shared_prefix_fp8
+        extra = (ks, vs)
+    assert g.shared_prefix and 0 < g.max_own_len <= 520
+    for bound in (g.max_own_len, 0, 16, g.max_own_len):
+        print(f"[parity] shared prefix ({kv}), max_own_len={bound}", flush=True)
+        out = torch.empty_like(g.dec_out)
+        call(out, g.dec_query, g.k_cache, g.v_cache, g.dec_tables, g.dec_lens, g.max_seq_len,
+             g.group_starts, g.prefix_lens, g.max_group_size, g.max_prefix_len, w.scale, *extra,
+             partition_size=512, workspace=g.workspace, max_own_len=bound)
+        torch.cuda.synchronize()
+        if bound != 16:  # 16 < the longest own range: a breach, unspecified output
+            assert_attention_close(words_from_device(out), ref, w.dtype,
+                                   f"shared prefix ({kv}), max_own_len={bound}", absolute=True)
