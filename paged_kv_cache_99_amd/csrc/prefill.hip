@@ -327,10 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     if (one_part && n_tiles > 0) {
         // ---------------------------------------------------------------- pipelined loop
         // Step t computes PV(t-1), QK(t+1) and the softmax of tile t. Tiles are loaded in pairs:
-        // odd steps t = 2u+1 wait for the loads of step t-2, pass a barrier and issue K tiles
-        // 2u+4, 2u+5 (into the slots of K tiles 2u, 2u+1, which QK read in steps 2u-1 and 2u)
-        // and V tiles 2u+2, 2u+3 (into the slots of V tiles 2u-2, 2u-1, read by PV in steps
-        // 2u-1 and 2u): every load gets two steps to land.
+        // odd steps t = 2u+1 wait for the loads of the two steps before, pass a barrier and issue
+        // K tiles 2u+4, 2u+5 (into the slots of K tiles 2u, 2u+1, which QK read in steps 2u-1 and
+        // 2u); the even step after it issues V tiles 2u+2, 2u+3 (into the slots of V tiles 2u-2,
+        // 2u-1, read by PV in steps 2u-1 and 2u, before that barrier). Spreading the two pairs
+        // over both steps keeps the load issue off one step; the K pair has two steps to land,
+        // the V pair one (both are waited for at step 2u+3, which first reads them).
         auto kslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (j & 3) * TILEB; };
         auto vslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (4 + (j & 3)) * TILEB; };
         using P0 = std::integral_constant<int, 0>;
@@ -553,9 +555,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                     __syncthreads();   // for every wave; every wave is done with step t-1
                     if (2 * u + 4 < n_tiles)
                         (void)issue_span(Two{}, p.k_cache, kslot(2 * u + 4), u + 2);
-                    if (2 * u + 2 < n_tiles)
-                        (void)issue_span(Two{}, p.v_cache, vslot(2 * u + 2), u + 1);
                 }
+            } else if constexpr (!F8) {
+                const int u = (t >> 1) - 1;  // t = 2u + 2: V tiles 2u+2, 2u+3
+                if (u >= 0 && 2 * u + 2 < n_tiles)
+                    (void)issue_span(Two{}, p.v_cache, vslot(2 * u + 2), u + 1);
             }
             if (rescale) {
 #pragma unroll
