@@ -837,9 +837,9 @@ __device__ __forceinline__ void mfma_workgroup_merge(const DecodeParams &p, int 
 // (at most 168 registers): each unit holds one step of K and V operands in flight, so the number
 // of resident waves sets the bytes in flight per CU.
 //  * Split (p.wg_parts == kMfmaWaves): workgroup (sequence, slot q, subgroup of 16 query heads,
-//    kv head); wave w computes part kMfmaWaves*q + w on its own, then the workgroup merges its
-//    parts through LDS by rescaling to their common maximum (the same log-sum-exp merge as the
-//    merge kernel's) and writes one partial result per row to slot q. Every part's partial would
+//    kv head); wave w computes the w-th quarter of slot q's tokens on its own, then the
+//    workgroup merges its parts through LDS by rescaling to their common maximum (the same
+//    log-sum-exp merge as the merge kernel's) and writes one partial result per row to slot q. Every part's partial would
 //    otherwise be an fp32 write of D floats per query head, and at G = 8 those writes cost several
 //    times their share of the HBM traffic.
 //  * Otherwise (p.wg_parts == 1): the waves are independent units (sequence, part, subgroup, kv
@@ -869,8 +869,19 @@ decode_mfma_kernel(DecodeParams p)
     const int part = merged ? q * kMfmaWaves + w : q;
     if (p.split && start + q * p.slot_tokens >= L)
         return;  // the slot holds no tokens (uniform over the workgroup in the merged mode)
-    const int t0 = min(L, start + part * p.part_tokens);
-    const int t1 = min(L, t0 + p.part_tokens);
+    int t0, t1;
+    if (merged) {
+        // The slot's tokens split evenly over the waves in 32-token steps. A sequence's last slot
+        // is usually partial, and fixed parts would leave waves idle beside one full part (the
+        // mixed step's decode, G = 4: 541 -> 537 us; over E4M3 caches 300 -> 293-296 us).
+        const int s0 = start + q * p.slot_tokens, s1 = min(L, s0 + p.slot_tokens);
+        const int chunk = ((s1 - s0 + kMfmaWaves - 1) / kMfmaWaves + 31) & ~31;
+        t0 = min(s1, s0 + w * chunk);
+        t1 = min(s1, t0 + chunk);
+    } else {
+        t0 = min(L, start + part * p.part_tokens);
+        t1 = min(L, t0 + p.part_tokens);
+    }
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h = sub * kCols + (lane & 15);
     const int qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
