@@ -75,8 +75,7 @@ struct DecodeParams {
     int32_t ws_rows;      // (sequence, head) rows: num_seqs * num_q_heads
     int32_t wg_parts;     // MFMA kernel: parts merged per workgroup (1 or kMfmaWaves)
     int32_t slot_tokens;  // tokens of a row's own workspace slot: part_tokens * wg_parts
-    int32_t pre_part_tokens;  // tokens per wave of a shared-prefix workgroup (partition_size)
-    int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: pre_part_tokens * kMfmaWaves
+    int32_t pre_slot_tokens;  // tokens of a shared-prefix slot: partition_size * kMfmaWaves
     int32_t slot_base;    // first slot these units write
     int32_t pre_slots;    // slots [0, pre_slots) hold shared-prefix results (merge)
     int32_t n_vsub;       // prefix units: groups of GK (member, head) pairs per kv head
@@ -833,6 +832,17 @@ __device__ __forceinline__ void mfma_workgroup_merge(const DecodeParams &p, int 
         *(float2 *)(p.ws_ml + ((size_t)qrow * p.ws_slots + slot) * 2) = make_float2(M, lm);
 }
 
+// Wave w's share [t0, t1) of a slot's tokens [s0, s1): the slot split evenly over the kMfmaWaves
+// waves in 32-token steps. A sequence's last slot is usually partial, and fixed parts would leave
+// waves idle beside one full part (the mixed step's decode, G = 4: 541 -> 537 us; over E4M3
+// caches 300 -> 293-296 us).
+__device__ __forceinline__ void wave_share(int s0, int s1, int w, int &t0, int &t1)
+{
+    const int chunk = ((s1 - s0 + kMfmaWaves - 1) / kMfmaWaves + 31) & ~31;
+    t0 = min(s1, s0 + w * chunk);
+    t1 = min(s1, t0 + chunk);
+}
+
 // Plain decode of head groups of 3 or more. A workgroup is kMfmaWaves waves, at most three per SIMD
 // (at most 168 registers): each unit holds one step of K and V operands in flight, so the number
 // of resident waves sets the bytes in flight per CU.
@@ -871,13 +881,8 @@ decode_mfma_kernel(DecodeParams p)
         return;  // the slot holds no tokens (uniform over the workgroup in the merged mode)
     int t0, t1;
     if (merged) {
-        // The slot's tokens split evenly over the waves in 32-token steps. A sequence's last slot
-        // is usually partial, and fixed parts would leave waves idle beside one full part (the
-        // mixed step's decode, G = 4: 541 -> 537 us; over E4M3 caches 300 -> 293-296 us).
-        const int s0 = start + q * p.slot_tokens, s1 = min(L, s0 + p.slot_tokens);
-        const int chunk = ((s1 - s0 + kMfmaWaves - 1) / kMfmaWaves + 31) & ~31;
-        t0 = min(s1, s0 + w * chunk);
-        t1 = min(s1, t0 + chunk);
+        const int s0 = start + q * p.slot_tokens;
+        wave_share(s0, min(L, s0 + p.slot_tokens), w, t0, t1);
     } else {
         t0 = min(L, start + part * p.part_tokens);
         t1 = min(L, t0 + p.part_tokens);
@@ -902,8 +907,8 @@ decode_mfma_kernel(DecodeParams p)
 }
 
 // Shared-prefix units: workgroup (prefix group g, kv head, subgroup of 16 (member, query head)
-// pairs, prefix slot q); wave w takes part kMfmaWaves*q + w of the prefix and the workgroup merges
-// its parts into slot q as decode_mfma_kernel does. The members of group g are sequences
+// pairs, prefix slot q); wave w takes its share of slot q's prefix tokens (wave_share) and the
+// workgroup merges its parts into slot q as decode_mfma_kernel does. The members of group g are sequences
 // group_starts[g] .. group_starts[g+1]-1; they share the blocks of positions
 // [0, seq_starts[first member]), read here once through the first member's table for all of them
 // (openeuler.csdn.net "高并发 AI 服务的内存瓶颈", 机制 2: shared blocks are stored once). Pair v of
@@ -933,8 +938,8 @@ decode_prefix_mfma_kernel(DecodeParams p)
     const int prefix = min(max(p.seq_starts[first], 0), L0);
     if (q * p.pre_slot_tokens >= prefix)
         return;  // uniform: the slot holds no prefix tokens
-    const int t0 = min(prefix, (q * kMfmaWaves + w) * p.pre_part_tokens);
-    const int t1 = min(prefix, t0 + p.pre_part_tokens);
+    int t0, t1;
+    wave_share(q * p.pre_slot_tokens, min(prefix, (q + 1) * p.pre_slot_tokens), w, t0, t1);
     const int v = vsub * kCols + (threadIdx.x & 15);
     const int qrow = v < n_mem * G ? (first + v / G) * p.num_q_heads + kvh * G + v % G : -1;
     f32x4 o[D / 16];
@@ -1176,7 +1181,6 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (cascade) {
         p.seq_starts = d.seq_starts;
         p.pre_slots = pre_slots;
-        p.pre_part_tokens = d.partition_size;
         p.pre_slot_tokens = d.partition_size * kMfmaWaves;
         p.slot_base = pre_slots;
         pre = p;
