@@ -467,12 +467,15 @@ __device__ __forceinline__ int qk_dim(int c, int g)
     return F8 ? 16 * (g + 4 * (c >> 1)) + 8 * (c & 1) : 32 * c + 8 * g;
 }
 
-// XOR swizzle of the 16-byte pieces of V row r in LDS (rows of D 16-bit elements): the 16 rows
-// one transposed read touches start on distinct pieces.
+// XOR swizzle of the 16-byte pieces of V row r in LDS (rows of D 16-bit elements). A transposed
+// read serves 32 lanes a cycle: 8 consecutive rows at 2 adjacent pieces, which must fall on
+// distinct 16-byte bank groups (64 four-byte banks, one 256-byte line per D = 128 row; two rows per
+// line for D = 64). For D = 128, 2 (r & 7) + (r >> 3 & 1) does that; r & 15 sent rows r and r + 1
+// to the same pieces (2-way conflicts; measured neutral in time, the kernel waits on HBM).
 template <int D>
 __device__ __forceinline__ int vswz(int r)
 {
-    return D == 128 ? (r & 15) : (r & 7);
+    return D == 128 ? ((r & 7) << 1) | ((r >> 3) & 1) : (r & 7);
 }
 
 // Bytes of LDS one MFMA unit stages V through: two blocks of 16 rows of D 16-bit elements.

@@ -98,16 +98,23 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// XOR swizzle of the 16-byte pieces of LDS row r (D = 128: 16 pieces; D = 64: 8 pieces). Chosen so
-// that 16 consecutive rows read at one column (the K operand) and 4 consecutive rows read at 2
-// adjacent pieces (the transposed V operand) fall on distinct banks.
+// XOR swizzle of the 16-byte pieces of LDS row r (D = 128: 16 pieces; D = 64: 8 pieces, two rows
+// per 256-byte line of the 64 four-byte banks). Chosen so that both operand reads are free of bank
+// conflicts:
+//   - K: 16 consecutive rows read at one column (ds_read_b128, 16 lanes a cycle) -- swz over each
+//     aligned 16 rows (each row parity, for D = 64) is a permutation;
+//   - V: 4 consecutive rows read at 4 adjacent pieces (ds_read_b64_tr_b16, 32 lanes a cycle) --
+//     rows r and r + 1 (D = 128), r and r + 2 (D = 64) take different groups of 4 pieces.
+// (An earlier swizzle, 2 (r & 7) + (r >> 3 & 1), sent rows r and r + 1 of V to the same pieces:
+// 2 conflict cycles per V read, 64 per wave-step; removing them took the 1856-row chunk from
+// 249-252 to 246 us, bit-identical.) swz(r + 8) = swz(r) ^ 2 for both.
 template <int D>
 __device__ __forceinline__ int swz(int r)
 {
     if constexpr (D == 128)
-        return 2 * (r & 7) + ((r >> 3) & 1);
+        return ((r & 3) << 2) | ((r >> 2) & 3);
     else
-        return (r >> 1) & 7;
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 template <bool BF, int D, int GK, bool TREE, bool F8>
@@ -357,14 +364,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         // registers). K operand of k-step c, rows kt*32 + n: piece (2c + hh) ^ swz(n) of the row,
         // i.e. byte (32 c) ^ 16 (hh ^ swz(n)). V operand of 32-dim tile dt, key rows r1 = 16 c4 +
         // 4 v_half + v_k and r2 = r1 + 8: piece (dim / 8) ^ swz(r), i.e. byte (64 dt) ^ 16 w for a
-        // lane constant w, and swz(r2) differs from swz(r1) in one bit (X2). Slot bases are
+        // lane constant w, and swz(r2) = swz(r1) ^ 2, i.e. byte X2 = 32. Slot bases are
         // multiples of 8 KiB and the lane bases stay below 8 KiB, so the XORs and the slot offset
         // never interact.
         const uint32_t lds0 = lds_address(lds);
         const int k_lane = n * ROWB + 16 * (hh ^ k_sw);
         const int r1b = 4 * v_half + v_k;
         const int v_lane = r1b * ROWB + 16 * ((v_dim >> 3) ^ swz<D>(r1b)) + (v_dim & 7) * 2;
-        constexpr int X2 = D == 128 ? 16 : 64;
+        constexpr int X2 = 32;
 
         // S^T = K Q^T of one tile into s, k-steps [C0, C1) (k-step 0 starts from zero); ka is the
         // lane's K base in the tile's slot
