@@ -125,8 +125,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   seq_lens      [num_seqs] int32, counting the token being decoded.
  *   max_seq_len   a host-side upper bound on seq_lens (sizes the launch); <= 16 * max_blocks_per_seq.
  *   partition_size  0: one pass per (sequence, kv head). Otherwise a multiple of 16 (at most 1024):
- *                 each sequence is cut into parts of that many tokens, processed in parallel, and
- *                 merged by rescaling with the parts' maxima and sums of exponentials ([OV] §9 (4)).
+ *                 each sequence is cut into parts of that many tokens (head groups of 3 or more:
+ *                 slots of 4 * partition_size tokens, each split evenly over four waves in 32-token
+ *                 steps), processed in parallel, and merged by rescaling with the parts' maxima and
+ *                 sums of exponentials ([OV] §9 (4)). It changes only the fp32 rounding.
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL when
  *                 that is 0); its contents are overwritten.
  * `out` must not alias any input.
