@@ -228,9 +228,26 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
                              int32_t num_q_heads, float scale, void *stream);
 
 /*
+ * Bytes of the optional pa_prefill_chunk_fp8 workspace: a 16-bit copy of num_seqs *
+ * max_blocks_per_seq blocks of both caches (2 * 16 * num_kv_heads * head_dim bytes per block and
+ * cache, each cache's region rounded up to 256 bytes); 0 for non-positive arguments.
+ */
+size_t pa_prefill_chunk_fp8_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq,
+                                           int32_t num_kv_heads, int32_t head_dim);
+
+/*
  * pa_prefill_chunk_fp8 -- pa_prefill_chunk over E4M3 caches ([V1] §4.4 with [PD] §5.4): keys and
  * values are read as code value times k_scale / v_scale; query and out are of `dtype` (F16 or
  * BF16); layouts, the other arguments and errors as in pa_prefill_chunk.
+ *   workspace     NULL, or device memory of at least pa_prefill_chunk_fp8_workspace_size(num_seqs,
+ *                 max_blocks_per_seq, num_kv_heads, head_dim) bytes, 256-byte aligned (else
+ *                 PA_ERR_WORKSPACE / PA_ERR_INVALID_ARG before anything is enqueued; its contents
+ *                 are overwritten). With a workspace, every block of the context of each sequence
+ *                 is first widened exactly to the 16-bit type (one pass over the E4M3 codes) and
+ *                 the 16-bit kernel then reads it by direct-to-LDS loads, which is faster for a
+ *                 chunk that is compute-bound; results are bit-identical to the path without one,
+ *                 which converts the codes inside the tile loop. num_seqs * max_blocks_per_seq
+ *                 must not exceed 2^31 - 1.
  */
 pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
                                  int32_t head_dim, void *out, const void *query,
@@ -239,7 +256,7 @@ pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t n
                                  const int32_t *seq_lens, const int32_t *cu_q_lens,
                                  int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                  int32_t num_q_heads, float scale, float k_scale, float v_scale,
-                                 void *stream);
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_prefill_chunk_tree -- pa_prefill_chunk for chunks that hold a tree of drafted tokens.

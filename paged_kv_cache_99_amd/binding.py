@@ -78,9 +78,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_fp8.restype = _i
         L.pa_decode_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _f, _f,
                                     _f, _i, _p, _sz, _p]
+        L.pa_prefill_chunk_fp8_workspace_size.restype = _sz
+        L.pa_prefill_chunk_fp8_workspace_size.argtypes = [_i, _i, _i, _i]
         L.pa_prefill_chunk_fp8.restype = _i
         L.pa_prefill_chunk_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i,
-                                           _i, _i, _f, _f, _f, _p]
+                                           _i, _i, _f, _f, _f, _p, _sz, _p]
         L.pa_prefill_chunk_tree.restype = _i
         L.pa_prefill_chunk_tree.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p,
                                             _i, _i, _i, _i, _f, _p]
@@ -337,11 +339,28 @@ def prefill_chunk(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_len
                                   _stream(stream)))
 
 
+def prefill_fp8_workspace_size(num_seqs: int, max_blocks_per_seq: int, num_kv_heads: int,
+                               head_dim: int) -> int:
+    """pa_prefill_chunk_fp8_workspace_size: bytes of the widened 16-bit copy of the context."""
+    return int(lib().pa_prefill_chunk_fp8_workspace_size(num_seqs, max_blocks_per_seq,
+                                                         num_kv_heads, head_dim))
+
+
+def alloc_prefill_fp8_workspace(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim,
+                                device=None) -> Optional[torch.Tensor]:
+    n = prefill_fp8_workspace_size(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def prefill_chunk_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens,
                       max_q_len: int, scale: float, k_scale: float, v_scale: float,
-                      stream=None) -> None:
+                      stream=None, workspace: Optional[torch.Tensor] = None) -> None:
     """pa_prefill_chunk_fp8: pa_prefill_chunk over E4M3 caches (uint8 or float8_e4m3fn;
-    elements = code value * k_scale / v_scale); query/out float16 or bfloat16."""
+    elements = code value * k_scale / v_scale); query/out float16 or bfloat16. With a workspace
+    (alloc_prefill_fp8_workspace) the context is first widened to 16 bits and read by the 16-bit
+    kernel; the results are the same bits."""
     _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=True)
     dt = _act_dtype(query, "query")
     tq, hq = int(query.shape[0]), int(query.shape[1])
@@ -354,12 +373,15 @@ def prefill_chunk_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q
     S = int(seq_lens.shape[0])
     if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q_lens.shape != (S + 1,):
         raise ValueError("block_tables must be [S, max_blocks] and cu_q_lens [S + 1]")
+    if workspace is not None:
+        _gpu(workspace, "workspace", torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_prefill_chunk_fp8(dt, nb, hkv, d, out.data_ptr(), query.data_ptr(),
                                       k_cache.data_ptr(), v_cache.data_ptr(),
                                       block_tables.data_ptr(), int(block_tables.shape[1]),
                                       seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, tq,
                                       int(max_q_len), hq, float(scale), float(k_scale),
-                                      float(v_scale), _stream(stream)))
+                                      float(v_scale), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------------- E4M3 caches

@@ -494,7 +494,8 @@ pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_he
                          const int32_t *cu_q_lens, const uint64_t *tree_mask, bool tree,
                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                          int32_t num_q_heads, float scale, void *stream, bool fp8 = false,
-                         float k_scale = 1.0f, float v_scale = 1.0f)
+                         float k_scale = 1.0f, float v_scale = 1.0f, void *workspace = nullptr,
+                         size_t workspace_bytes = 0)
 {
     pa::CacheDims c;
     pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
@@ -549,6 +550,21 @@ pa_status_t prefill_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_he
     p.c.fp8 = fp8;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
+    if (fp8 && workspace != nullptr) {
+        REQUIRE(max_blocks_per_seq > 0, "max_blocks_per_seq %d: nothing to widen",
+                max_blocks_per_seq);
+        REQUIRE((int64_t)num_seqs * max_blocks_per_seq <= 0x7fffffff,
+                "num_seqs * max_blocks_per_seq %lld exceeds the widened pool's block ids",
+                (long long)num_seqs * max_blocks_per_seq);
+        REQUIRE(((uintptr_t)workspace & 255) == 0, "workspace is not 256-byte aligned");
+        const size_t need = pa::prefill_widen_bytes(num_seqs, max_blocks_per_seq, num_kv_heads,
+                                                    head_dim);
+        if (workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                        need);
+        p.widen_k16 = workspace;
+        p.widen_v16 = (char *)workspace + need / 2;
+    }
     return launched(pa::launch_prefill(p, (hipStream_t)stream),
                     tree ? "prefill_chunk_tree" : fp8 ? "prefill_chunk_fp8" : "prefill_chunk");
 }
@@ -570,6 +586,12 @@ pa_status_t pa_prefill_chunk(pa_dtype_t dtype, int32_t num_blocks, int32_t num_k
                         num_seqs, total_q, max_q_len, num_q_heads, scale, stream);
 }
 
+size_t pa_prefill_chunk_fp8_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq,
+                                           int32_t num_kv_heads, int32_t head_dim)
+{
+    return pa::prefill_widen_bytes(num_seqs, max_blocks_per_seq, num_kv_heads, head_dim);
+}
+
 pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
                                  int32_t head_dim, void *out, const void *query,
                                  const void *k_cache, const void *v_cache,
@@ -577,12 +599,12 @@ pa_status_t pa_prefill_chunk_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t n
                                  const int32_t *seq_lens, const int32_t *cu_q_lens,
                                  int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                  int32_t num_q_heads, float scale, float k_scale, float v_scale,
-                                 void *stream)
+                                 void *workspace, size_t workspace_bytes, void *stream)
 {
     return prefill_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
                         block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, nullptr, false,
                         num_seqs, total_q, max_q_len, num_q_heads, scale, stream, true, k_scale,
-                        v_scale);
+                        v_scale, workspace, workspace_bytes);
 }
 
 pa_status_t pa_prefill_chunk_tree(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,

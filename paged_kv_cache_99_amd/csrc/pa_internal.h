@@ -103,7 +103,13 @@ struct PrefillLaunch {
     // E4M3 caches (c.fp8): element = code value * k_scale / v_scale; query/out of dtype c.bf16
     float k_scale = 1.0f;
     float v_scale = 1.0f;
+    // E4M3 caches with a workspace: the sequences' blocks are first widened to 16 bits into these
+    // two regions (num_seqs * max_blocks blocks each), and the 16-bit kernel runs on them
+    void *widen_k16 = nullptr;
+    void *widen_v16 = nullptr;
 };
+size_t prefill_widen_bytes(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
+                           int32_t head_dim);  // pa_shapes.cpp: both regions
 bool prefill_supported(int32_t head_dim, int32_t group);  // pa_shapes.cpp
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 

@@ -29,4 +29,14 @@ size_t decode_workspace_used(int32_t num_seqs, int32_t num_q_heads, int32_t num_
     return (size_t)num_seqs * num_q_heads * slots * (head_dim + 2) * sizeof(float);
 }
 
+size_t prefill_widen_bytes(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
+                           int32_t head_dim)
+{
+    if (num_seqs <= 0 || max_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return 0;
+    // K and V, 16-bit elements, blocks of 16 rows: one region per cache, 256-byte aligned
+    const size_t region = (size_t)num_seqs * max_blocks * num_kv_heads * 16 * head_dim * 2;
+    return 2 * ((region + 255) & ~(size_t)255);
+}
+
 }  // namespace pa

@@ -82,7 +82,9 @@ struct PrefillParams {
     int32_t n_items;
     int32_t total_q;
     float scale_log2;
-    float v_scale;  // E4M3 caches: value scale, applied to the output (k_scale is in scale_log2)
+    float v_scale;  // value scale (E4M3 caches, also widened), applied to the output; k_scale is
+                    // in scale_log2
+    int32_t identity_blocks;  // block i of sequence s is block s * max_blocks + i (a widened copy)
 };
 
 constexpr int kWaves = 8;                // waves per workgroup
@@ -254,7 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         const int key0 = t * KEYS + wave * kBlock;  // first key of this wave's block
         if (wave >= NBLK || key0 >= L)
             return 0;
-        const int blk = table[key0 / kBlock];
+        const int blk =
+            p.identity_blocks ? seq * p.max_blocks + key0 / kBlock : table[key0 / kBlock];
         if ((unsigned)blk >= (unsigned)p.num_blocks)
             return PER_BLK;
         const char *sbase = (const char *)cache + kvh_bytes + (size_t)blk * blk_bytes;
@@ -782,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     l_run = pair_sum(l_run);
     if (!row_ok)
         return;
-    const float inv = l_run > 0.0f ? (F8 ? p.v_scale : 1.0f) / l_run : 0.0f;
+    const float inv = l_run > 0.0f ? p.v_scale / l_run : 0.0f;
     uint16_t *dst = p.out + ((size_t)(q0 + row) * p.num_q_heads + head) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -793,6 +796,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             w.y = pack2<BF>(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
             *(uint2 *)(dst + dt * 32 + 8 * j + 4 * hh) = w;
         }
+}
+
+// E4M3 context widened for the 16-bit kernel: block i < ceil(L_s / 16) of sequence s, both caches,
+// every kv head, converted exactly to the query's 16-bit type (the conversion of the register-
+// staged E4M3 path) into block s * max_blocks + i of a 16-bit pool of the cache layout
+// [block][kv head][16][D]. A block id outside the pool gives zeros. Rows past a sequence's end
+// are converted too, but the prefill never loads them.
+struct WidenParams {
+    const uint8_t *__restrict__ k8;
+    const uint8_t *__restrict__ v8;
+    uint16_t *__restrict__ k16;
+    uint16_t *__restrict__ v16;
+    const int32_t *__restrict__ block_tables;
+    const int32_t *__restrict__ seq_lens;
+    int32_t num_seqs;
+    int32_t max_blocks;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+};
+
+constexpr int kWidenThreads = 256;
+
+template <bool BF, int D>
+__global__ __launch_bounds__(kWidenThreads) void widen_e4m3_kernel(WidenParams w)
+{
+    const int sb = blockIdx.x;  // s * max_blocks + i
+    const int s = sb / w.max_blocks, i = sb % w.max_blocks;
+    if (s >= w.num_seqs)
+        return;
+    const int L = min(max(w.seq_lens[s], 0), w.max_blocks * kBlock);
+    if (i * kBlock >= L)
+        return;
+    const int blk = w.block_tables[(size_t)s * w.max_blocks + i];
+    const bool ok = (unsigned)blk < (unsigned)w.num_blocks;
+    const size_t per_blk = (size_t)w.num_kv_heads * kBlock * D;  // elements of a block, all heads
+    const int pieces = (int)(per_blk / 16);                        // 16-code pieces per cache
+    for (int j = threadIdx.x; j < 2 * pieces; j += kWidenThreads) {
+        const bool v = j >= pieces;
+        const int jj = v ? j - pieces : j;
+        const uint8_t *src = (v ? w.v8 : w.k8) + (size_t)blk * per_blk + (size_t)jj * 16;
+        uint16_t *dst = (v ? w.v16 : w.k16) + (size_t)sb * per_blk + (size_t)jj * 16;
+        const uint4 c = ok ? *(const uint4 *)src : make_uint4(0, 0, 0, 0);
+        ((uint4 *)dst)[0] = make_uint4(e4m3x2_to_pk16<BF, false>(c.x), e4m3x2_to_pk16<BF, true>(c.x),
+                                       e4m3x2_to_pk16<BF, false>(c.y), e4m3x2_to_pk16<BF, true>(c.y));
+        ((uint4 *)dst)[1] = make_uint4(e4m3x2_to_pk16<BF, false>(c.z), e4m3x2_to_pk16<BF, true>(c.z),
+                                       e4m3x2_to_pk16<BF, false>(c.w), e4m3x2_to_pk16<BF, true>(c.w));
+    }
 }
 
 template <bool BF, int D, int GK>
@@ -851,11 +901,45 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
     if (items > 0x7ffffff0)
         return hipErrorInvalidValue;
     p.n_items = (int32_t)items;
-    const bool fp8 = d.c.fp8;
+    bool fp8 = d.c.fp8;
     if (fp8 && d.tree_mask)
         return hipErrorInvalidValue;  // no tree mask over E4M3 caches
     p.scale_log2 = (float)((double)d.scale * (fp8 ? (double)d.k_scale : 1.0) * 1.4426950408889634);
     p.v_scale = fp8 ? d.v_scale : 1.0f;
+    p.identity_blocks = 0;
+    if (fp8 && d.widen_k16) {
+        // widen the sequences' E4M3 blocks into the workspace, then run the 16-bit kernel on it
+        WidenParams w;
+        w.k8 = (const uint8_t *)d.k_cache;
+        w.v8 = (const uint8_t *)d.v_cache;
+        w.k16 = (uint16_t *)d.widen_k16;
+        w.v16 = (uint16_t *)d.widen_v16;
+        w.block_tables = d.block_tables;
+        w.seq_lens = d.seq_lens;
+        w.num_seqs = d.num_seqs;
+        w.max_blocks = d.max_blocks;
+        w.num_blocks = d.c.num_blocks;
+        w.num_kv_heads = d.c.num_kv_heads;
+        const int64_t n_sb = (int64_t)d.num_seqs * d.max_blocks;
+        if (n_sb > 0x7fffffff)
+            return hipErrorInvalidValue;
+        if (d.c.bf16)
+            hipLaunchKernelGGL((d.c.head_dim == 64 ? widen_e4m3_kernel<true, 64>
+                                                   : widen_e4m3_kernel<true, 128>),
+                               dim3((unsigned)n_sb), dim3(kWidenThreads), 0, stream, w);
+        else
+            hipLaunchKernelGGL((d.c.head_dim == 64 ? widen_e4m3_kernel<false, 64>
+                                                   : widen_e4m3_kernel<false, 128>),
+                               dim3((unsigned)n_sb), dim3(kWidenThreads), 0, stream, w);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        p.k_cache = (const uint16_t *)d.widen_k16;
+        p.v_cache = (const uint16_t *)d.widen_v16;
+        p.num_blocks = (int32_t)n_sb;
+        p.identity_blocks = 1;
+        fp8 = false;  // the 16-bit kernel, with k_scale in scale_log2 and v_scale on the output
+    }
     if (d.c.bf16)
         return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, fp8, stream)
                                   : launch_gk<true, 128>(gk, p, fp8, stream);

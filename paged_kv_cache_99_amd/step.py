@@ -75,12 +75,14 @@ class GpuStep:
     kv_cache="fp8" keeps the caches as E4M3 codes (lecture 34 §4.4) with scales k_scale, v_scale:
     fp8_pool gives their initial bytes (numpy uint8, the pool layout); without it the 16-bit pool is
     quantized on the device by the library's own FP8 scatter, each slot being one token. Such a
-    step runs every stage over the E4M3 caches (the *_fp8 entry points).
+    step runs every stage over the E4M3 caches (the *_fp8 entry points). Its chunks are prefilled
+    over a widened 16-bit copy of their context (pa_prefill_chunk_fp8 with a workspace) when that
+    copy takes at most widen_limit bytes, else with the codes converted inside the tile loop.
     """
 
     def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
                  shared_prefix: bool = False, kv_cache: str = "auto", k_scale: float = 1.0,
-                 v_scale: float = 1.0, fp8_pool=None):
+                 v_scale: float = 1.0, fp8_pool=None, widen_limit: int = 1 << 30):
         self.w = w
         self.device = torch.device(device)
         dt, dev = w.dtype, self.device
@@ -145,6 +147,12 @@ class GpuStep:
         self.pre_out = torch.empty_like(self.pre_query)
         cu = np.asarray(w.cu_q_lens)
         self.max_q_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
+        self.pre_workspace = None
+        if self.fp8 and self.pre_query.shape[0]:
+            n = binding.prefill_fp8_workspace_size(int(self.pre_tables.shape[0]),
+                                                   int(self.pre_tables.shape[1]), w.H_kv, w.D)
+            if 0 < n <= widen_limit:
+                self.pre_workspace = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def quantize_pool_on_device(self, w):
         """E4M3 caches holding the codes of the workload's 16-bit pool: every slot of the pool is
@@ -201,7 +209,8 @@ class GpuStep:
         if self.pre_query.shape[0] and self.fp8:
             binding.prefill_chunk_fp8(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
                                       self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
-                                      self.w.scale, self.k_scale, self.v_scale, stream)
+                                      self.w.scale, self.k_scale, self.v_scale, stream,
+                                      workspace=self.pre_workspace)
         elif self.pre_query.shape[0]:
             binding.prefill_chunk(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
                                   self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,

@@ -164,6 +164,28 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.pa_decode_fp8(*small) == WORKSPACE
 
 
+def test_fp8_prefill_workspace_checks_on_the_host():
+    """pa_prefill_chunk_fp8's optional workspace (the context widened to 16 bits): its size, and a
+    too-small or misaligned one refused before anything is enqueued (no device is touched)."""
+    lib = binding.lib()
+    f = ctypes.c_float
+    size = lib.pa_prefill_chunk_fp8_workspace_size
+    assert size(1, 512, 8, 128) == 2 * 512 * 8 * 16 * 128 * 2
+    assert size(3, 5, 1, 64) == 2 * ((3 * 5 * 16 * 64 * 2 + 255) // 256 * 256)
+    assert size(0, 5, 1, 64) == 0 and size(1, 0, 1, 64) == 0
+    need = size(1, 4, 2, 128)
+    args = [BF16, 10, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 8, 8, 8, f(0.1),
+            f(0.5), f(0.5)]
+    assert lib.pa_prefill_chunk_fp8(*args, FAKE, need - 1, None) == WORKSPACE
+    assert lib.pa_prefill_chunk_fp8(*args, FAKE + 16, need, None) == INVALID
+    no_blocks = list(args)
+    no_blocks[9] = 0
+    assert lib.pa_prefill_chunk_fp8(*no_blocks, FAKE, need, None) == INVALID
+    bad_scale = list(args)
+    bad_scale[17] = f(0.0)
+    assert lib.pa_prefill_chunk_fp8(*bad_scale, FAKE, need, None) == INVALID
+
+
 def test_noalloc_decode_checks_its_scratch_limit_on_the_host():
     """pa_decode_noalloc has pa_decode's checks, and refuses sizes whose partial results exceed its
     static scratch before anything is enqueued (no device is touched here)."""

@@ -257,6 +257,26 @@ def test_prefill_chunks(H_q, H_kv, D, dtype):
                            f"fp8 prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}")
 
 
+@pytest.mark.parametrize("H_q,H_kv,D,dtype", [(8, 2, 128, "bf16"), (4, 4, 64, "f16"),
+                                            (12, 4, 128, "f16"), (16, 16, 64, "bf16")])
+def test_prefill_widened_equals_staged(H_q, H_kv, D, dtype):
+    """The step prefills over a 16-bit widened copy of the context (pa_prefill_chunk_fp8 with a
+    workspace); without one the codes are converted in the tile loop. Same conversion, same LDS
+    contents, same MFMAs: the outputs must be the same bits, and both within the gate."""
+    lens = [40, 700, 1300, 97, 16, 2049, 777]
+    q_lens = [40, 129, 300, 1, 16, 64, 700]
+    w = W.build([300] + lens, H_q, H_kv, D, dtype, seed=880 + H_q + D, n_decode=1, q_lens=q_lens)
+    g, ref = run_fp8_prefill(w, 0.04, 0.025)
+    assert g.pre_workspace is not None
+    staged = torch.empty_like(g.pre_out)
+    binding.prefill_chunk_fp8(staged, g.pre_query, g.k_cache, g.v_cache, g.pre_tables, g.pre_lens,
+                              g.pre_cu, g.max_q_len, w.scale, 0.04, 0.025)
+    torch.cuda.synchronize()
+    widened = words_from_device(g.pre_out)
+    assert np.array_equal(widened, words_from_device(staged))
+    assert_attention_close(widened, ref, dtype, f"fp8 widened prefill H_q={H_q} D={D} {dtype}")
+
+
 def test_prefill_mixed_step_full():
     """The 2048-token mixed step over E4M3 caches: every decode row and every row of the 1856-row
     chunk (all 32 heads) against the oracle."""
@@ -280,6 +300,13 @@ def test_prefill_mixed_step_full():
     print(f"[fp8] oracle prefill of the whole chunk: {time.time() - t:.1f}s", flush=True)
     assert_attention_close(words_from_device(g.pre_out), ref_p, w.dtype, "fp8 mixed prefill",
                            absolute=True)
+    # the step prefilled over the widened copy; the in-loop conversion gives the same bits
+    assert g.pre_workspace is not None
+    staged = torch.empty_like(g.pre_out)
+    binding.prefill_chunk_fp8(staged, g.pre_query, g.k_cache, g.v_cache, g.pre_tables, g.pre_lens,
+                              g.pre_cu, g.max_q_len, w.scale, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_from_device(g.pre_out), words_from_device(staged))
 
 
 def test_prefill_is_deterministic():
