@@ -28,6 +28,9 @@ Prints ONE JSON line:
                far larger than the 256 MB Infinity Cache, so each step reads them from HBM;
                --evict-mb 512 also displaces every cache level before each timed decode, to show
                that.
+  graph        (--graph) the same step recorded once as a HIP graph and replayed: time per step
+               and the rates above over it, for steps whose kernels are short enough that host
+               launches show.
 
 Algorithmic bytes (what the method must move, per stage; E = 2 bytes per cache element, 1 with
 --kv-cache fp8, whose caches hold E4M3 codes):
@@ -340,6 +343,9 @@ def main():
                     help="read an MB-megabyte buffer before each timed decode (outside the decode "
                          "events, inside the step time) so that no cache level holds K/V rows from "
                          "the previous step; 512 exceeds the 256 MB Infinity Cache twice over")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step recorded once as a HIP graph and replayed (reported "
+                         "under \"graph\"; the line's value stays the eager step's)")
     args = ap.parse_args()
     if args.print_decode_src_hash:
         print(src_hash(DECODE_SRCS), src_hash(PREFILL_SRCS))
@@ -405,6 +411,19 @@ def main():
     dec_ms = float(np.mean(dec_t))
     pre_ms = float(np.mean(pre_t))
 
+    graph_ms = None
+    if args.graph:
+        graph = g.capture()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / K
+        del graph
+
     if args.copy_calibration:
         calibration_copy(g, args.copy_calibration)
 
@@ -469,6 +488,13 @@ def main():
             "algorithmic_bytes_per_launch": int(u_bytes),
         },
     }
+    if graph_ms is not None:
+        out["graph"] = {
+            "ms_per_step": round(graph_ms, 5),
+            "value": round(step_bytes / (graph_ms * 1e-3) / 1e9, 2),
+            "step_tokens_per_s": round(step_tokens / (graph_ms * 1e-3), 1),
+            "decode_tokens_per_s": round(w.n_decode / (graph_ms * 1e-3), 1),
+        }
     if g.shared_prefix or u_bytes != d_bytes:
         out["decode_logical_bytes"] = int(d_bytes)
         out["decode_GBps_logical"] = round(d_bytes / (dec_ms * 1e-3) / 1e9, 2)

@@ -221,3 +221,17 @@ class GpuStep:
         self.scatter(stream)
         self.decode(stream)
         self.prefill(stream)
+
+    def capture(self):
+        """The whole step recorded once as a HIP graph (torch.cuda.CUDAGraph) and returned; each
+        graph.replay() then launches the same kernels on the same buffers with one call. The
+        library's entry points allocate nothing and issue no memset, so every node is a kernel.
+        Replays read the buffers as they are at replay time: new tokens, queries, slots and
+        seq_lens written in place are picked up, as long as each seq_lens[s] stays within the
+        max_seq_len (and the shared-prefix bounds) the launch was sized for."""
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(self.device)
+        with torch.cuda.graph(graph):
+            self.run()
+        torch.cuda.synchronize(self.device)
+        return graph
