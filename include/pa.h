@@ -328,6 +328,61 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
                                         float v_scale, int32_t partition_size, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
+/*
+ * pa_decode_multi -- a few query rows per sequence (multi-token decode), read like a decode.
+ * [PD] §5.4: the k drafts of a speculative step are verified by one pass of the target model;
+ * [V1] §5.3: a draft tree (EAGLE) is verified the same way. The rows of sequence s are
+ * cu_q_lens[s] .. cu_q_lens[s+1]-1 of query and out, at positions first_s .. seq_lens[s]-1
+ * (first_s = seq_lens[s] - q_len_s). Row i attends positions 0..first_s-1 and the rows' own
+ * positions first_s + j for j <= i; with tree_mask, only those j whose bit j of
+ * tree_mask[cu_q_lens[s] + i] is set. out equals pa_prefill_chunk's (pa_prefill_chunk_tree's with
+ * a mask) for the same rows; a row that attends no position is written as zeros.
+ * Each kv head's context is read once per 16 (row, query head) pairs, on MFMA, split into parts of
+ * partition_size tokens merged by rescaling with their maxima and sums of exponentials, as in
+ * pa_decode ([OV] §9 (4)). The chunk kernel of pa_prefill_chunk instead reads it once per
+ * workgroup of 256 pairs, which few rows leave mostly empty: this call is the faster one up to
+ * about 32 pairs per kv head (max_q_len * num_q_heads / num_kv_heads), the chunk kernel beyond.
+ *   query, out    [total_q][num_q_heads][head_dim] of `dtype` (F16 or BF16); out must not alias
+ *                 an input.
+ *   cu_q_lens     [num_seqs + 1] int32, cu_q_lens[0] = 0, non-decreasing, cu_q_lens[num_seqs] =
+ *                 total_q; q_len_s <= max_q_len and q_len_s <= seq_lens[s] are the caller's
+ *                 contract (rows past max_q_len are not written).
+ *   tree_mask     NULL (causal rows) or [total_q] uint64, device memory, 8-byte aligned; bits
+ *                 j > i are ignored.
+ *   max_q_len     1..16 (PA_ERR_INVALID_ARG otherwise).
+ *   max_seq_len   an upper bound on seq_lens (sizes the launch); <= 16 * max_blocks_per_seq.
+ *   partition_size, workspace: as in pa_decode, with a workspace of at least
+ *                 pa_decode_multi_workspace_size(...) bytes (0 when unsplit).
+ * The other arguments, layouts and errors are those of pa_decode.
+ */
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_seq_len,
+                                      int32_t partition_size);
+
+pa_status_t pa_decode_multi(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                            int32_t head_dim, void *out, const void *query, const void *k_cache,
+                            const void *v_cache, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *cu_q_lens, const uint64_t *tree_mask, int32_t num_seqs,
+                            int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                            int32_t num_q_heads, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_multi_fp8 -- pa_decode_multi over E4M3 caches ([V1] §4.4): keys and values are read
+ * as code value times k_scale / v_scale (finite, positive); everything else as in pa_decode_multi.
+ */
+pa_status_t pa_decode_multi_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, void *out, const void *query,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                const uint64_t *tree_mask, int32_t num_seqs, int32_t total_q,
+                                int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                                float scale, float k_scale, float v_scale,
+                                int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static text for a status code. */
 const char *pa_status_string(pa_status_t status);
 

@@ -89,6 +89,14 @@ def lib() -> ctypes.CDLL:
         L.pa_prefill_chunk.restype = _i
         L.pa_prefill_chunk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _i,
                                        _i, _f, _p]
+        L.pa_decode_multi_workspace_size.restype = _sz
+        L.pa_decode_multi_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.pa_decode_multi.restype = _i
+        L.pa_decode_multi.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i,
+                                      _i, _i, _i, _f, _i, _p, _sz, _p]
+        L.pa_decode_multi_fp8.restype = _i
+        L.pa_decode_multi_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i,
+                                          _i, _i, _i, _i, _f, _f, _f, _i, _p, _sz, _p]
         _lib = L
     return _lib
 
@@ -382,6 +390,72 @@ def prefill_chunk_fp8(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q
                                       seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, tq,
                                       int(max_q_len), hq, float(scale), float(k_scale),
                                       float(v_scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------------- multi-token decode
+MULTI_MAX_ROWS = 16  # rows per sequence pa_decode_multi takes
+
+
+def decode_multi_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim, max_seq_len,
+                                partition_size) -> int:
+    return int(lib().pa_decode_multi_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
+                                                    max_seq_len, partition_size))
+
+
+def alloc_decode_multi_workspace(num_seqs, max_q_len, num_q_heads, head_dim, max_seq_len,
+                                 partition_size, device=None) -> Optional[torch.Tensor]:
+    n = decode_multi_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim, max_seq_len,
+                                    partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def decode_multi(out, query, k_cache, v_cache, block_tables, seq_lens, cu_q_lens, max_q_len: int,
+                 max_seq_len: int, scale: float, partition_size: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None, tree_mask=None,
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> None:
+    """pa_decode_multi (pa_decode_multi_fp8 when k_scale and v_scale are given, over E4M3 caches):
+    up to 16 query rows per sequence, out/query [total_q, H_q, D] by cu_q_lens [S+1]; seq_lens [S];
+    tables [S, max_blocks]; tree_mask None or int64/uint64 [total_q]. The result is
+    prefill_chunk's for the same rows."""
+    fp8 = k_scale is not None or v_scale is not None
+    _, nb, hkv, d = _cache_dims(k_cache, v_cache, fp8=fp8)
+    dt = _act_dtype(query, "query")
+    tq, hq = int(query.shape[0]), int(query.shape[1])
+    for t, n in ((query, "query"), (out, "out")):
+        _gpu(t, n, query.dtype)
+        if tuple(t.shape) != (tq, hq, d):
+            raise ValueError(f"{n} must be [{tq}, {hq}, {d}]")
+    if not fp8 and query.dtype != k_cache.dtype:
+        raise ValueError("query and the 16-bit caches differ in dtype")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (cu_q_lens, "cu_q_lens")):
+        _gpu(t, n, torch.int32)
+    S = int(seq_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q_lens.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and cu_q_lens [S + 1]")
+    if tree_mask is not None:
+        if not (tree_mask.is_cuda and tree_mask.is_contiguous()) or \
+                tree_mask.dtype not in (torch.int64, torch.uint64) or tuple(tree_mask.shape) != (tq,):
+            raise ValueError(f"tree_mask must be a contiguous int64/uint64 GPU tensor [{tq}]")
+    if partition_size is None:
+        partition_size = default_partition_size(max_seq_len, 3)
+    need = decode_multi_workspace_size(S, max_q_len, hq, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = alloc_decode_multi_workspace(S, max_q_len, hq, d, max_seq_len, partition_size,
+                                                 query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [dt, nb, hkv, d, out.data_ptr(), query.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
+            seq_lens.data_ptr(), cu_q_lens.data_ptr(), _ptr(tree_mask), S, tq, int(max_q_len),
+            int(max_seq_len), hq, float(scale)]
+    if fp8:
+        _check(lib().pa_decode_multi_fp8(*args, float(k_scale), float(v_scale),
+                                         int(partition_size), _ptr(workspace), ws_bytes,
+                                         _stream(stream)))
+    else:
+        _check(lib().pa_decode_multi(*args, int(partition_size), _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
 
 
 # ------------------------------------------------------------------------- E4M3 caches

@@ -82,6 +82,15 @@ struct DecodeParams {
     // shared-prefix decode whose own ranges all fit one part (vector-ALU units): each own unit
     // folds its row's shared-prefix partials in and writes the output, and no merge kernel runs
     int32_t fused_finish;
+    // Multi-token decode (mt_rows > 0, MFMA kernel): sequence s has q_len = cu_q[s+1] - cu_q[s]
+    // (at most mt_rows) query rows, rows cu_q[s] .. of the [total_q][num_q_heads][D] query and
+    // output; row r sits at position L - q_len + r and sees the positions before the rows, and row
+    // j <= r of them when bit j of tree_mask[cu_q[s] + r] is set (every such j without a mask).
+    // Workspace rows are (sequence, row, head): (s * mt_rows + r) * num_q_heads + head.
+    const int32_t *__restrict__ cu_q;
+    const uint64_t *__restrict__ tree_mask;
+    int32_t mt_rows;
+    int32_t total_q;
 };
 
 // Position range of unit `part` of a sequence: [start + part*P, min(L, start + (part+1)*P)).
@@ -496,10 +505,13 @@ __device__ __forceinline__ void wave_lds_fence()
 // tile t), m the running maximum of column j (log2 domain) and l this lane's share of column j's
 // running sum (the four row groups g add up to it). v_lds is the wave's own staging area
 // (kUnitLds<D> bytes). An empty range leaves o = 0, m = -inf, l = 0.
-template <bool BF, bool F8, int D>
+// MT (multi-token rows): positions from c0 on are the query rows' own; column j sees position
+// c0 + i only when bit i of its vis is set (none from c0 + 32 on).
+template <bool BF, bool F8, int D, bool MT = false>
 __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const int32_t *table,
                                           int kvh, int t0, int t1, uint8_t *v_lds,
-                                          f32x4 (&o)[D / 16], float &m, float &l)
+                                          f32x4 (&o)[D / 16], float &m, float &l, int c0 = 0,
+                                          uint32_t vis = 0)
 {
     constexpr int NC = D / 32;              // QK k-chunks
     constexpr int NT = D / 16;              // PV output tiles
@@ -585,7 +597,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
         };
         auto whole_step = [&](int st) {
             bool w = 2 * st + 1 < nb && (bb + 2 * st) * kBlock >= t0 &&
-                     (bb + 2 * st + 2) * kBlock <= t1;
+                     (bb + 2 * st + 2) * kBlock <= (MT ? min(t1, c0) : t1);
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const int raw = __builtin_amdgcn_readlane(my_blk, w ? 2 * st + b : 0);
@@ -647,8 +659,16 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float x = acc[v] * p.scale_log2;
-                    if (!whole && !tok_ok(st, b, 4 * g + v))
-                        x = -INFINITY;
+                    if (!whole) {
+                        bool ok = tok_ok(st, b, 4 * g + v);
+                        if constexpr (MT) {
+                            const int tok = (bb + 2 * st + b) * kBlock + 4 * g + v;
+                            if (ok && tok >= c0)
+                                ok = tok - c0 < 32 && ((vis >> (tok - c0)) & 1u);
+                        }
+                        if (!ok)
+                            x = -INFINITY;
+                    }
                     sv[4 * b + v] = x;
                 }
             }
@@ -857,8 +877,12 @@ __device__ __forceinline__ void wave_share(int s0, int s1, int w, int &t0, int &
 //    times their share of the HBM traffic.
 //  * Otherwise (p.wg_parts == 1): the waves are independent units (sequence, part, subgroup, kv
 //    head) that write their own partial result, or the output when the decode is not split.
+// MT: multi-token decode (p.mt_rows > 0). The columns of a kv head are its (row, query head)
+// pairs, row-major: column v of the group is row v / G, query head kvh * G + v % G, and the
+// subgroups cover the mt_rows * G pairs. Each column carries its row's view of the rows' own
+// positions (mfma_unit's c0 and vis); workspace rows are (sequence, row, head).
 
-template <bool BF, bool F8, int D>
+template <bool BF, bool F8, int D, bool MT = false>
 __global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_mfma_kernel(DecodeParams p)
 {
@@ -870,13 +894,23 @@ decode_mfma_kernel(DecodeParams p)
     const int unit = merged ? wg : wg * kMfmaWaves + w;
     if (unit >= p.n_units)
         return;  // uniform over the workgroup in the merged mode
-    const int seq = unit % p.num_seqs;
-    int rest = unit / p.num_seqs;
+    // MT numbers the subgroups fastest: the subgroups of one (sequence, slot, kv head) read the
+    // same K/V and run side by side on one XCD, so all but the first find it in that XCD's L2
+    int rest = unit, sub = 0;
+    if constexpr (MT) {
+        sub = rest % p.n_sub;
+        rest /= p.n_sub;
+    }
+    const int seq = rest % p.num_seqs;
+    rest /= p.num_seqs;
     const int n_slot = merged ? p.ws_slots - p.slot_base : p.max_parts;  // slots (parts) per row
     const int q = unit_part(p, rest % n_slot, n_slot);
     rest /= n_slot;
-    const int sub = rest % p.n_sub;
-    const int kvh = rest / p.n_sub;
+    if constexpr (!MT) {
+        sub = rest % p.n_sub;
+        rest /= p.n_sub;
+    }
+    const int kvh = rest;
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int start = unit_start(p, seq, L);
     const int part = merged ? q * kMfmaWaves + w : q;
@@ -891,22 +925,43 @@ decode_mfma_kernel(DecodeParams p)
         t1 = min(L, t0 + p.part_tokens);
     }
     const int G = p.num_q_heads / p.num_kv_heads;
-    const int h = sub * kCols + (lane & 15);
-    const int qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
+    int qrow, wrow;  // query / output row and workspace row of this lane's column (-1: none)
+    int c0 = 0;
+    uint32_t vis = 0;
+    if constexpr (MT) {
+        // offsets are clamped to [0, total_q] so that no index contents reach outside the arrays
+        const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
+        const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
+        if (sub * kCols >= min(q_len, p.mt_rows) * G)
+            return;  // no row of this subgroup (uniform over the workgroup in the merged mode)
+        const int v = sub * kCols + (lane & 15), r = v / G;
+        const bool ok = r < min(q_len, p.mt_rows);
+        const int head = kvh * G + v % G;
+        qrow = ok ? (q0 + r) * p.num_q_heads + head : -1;
+        wrow = ok ? (seq * p.mt_rows + r) * p.num_q_heads + head : -1;
+        c0 = L - q_len;  // position of row 0
+        vis = ok ? (2u << r) - 1u : 0u;  // rows 0..r (r < mt_rows <= 16)
+        if (ok && p.tree_mask)
+            vis &= (uint32_t)p.tree_mask[q0 + r];
+    } else {
+        const int h = sub * kCols + (lane & 15);
+        qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
+        wrow = qrow;
+    }
     f32x4 o[NT];
     float m, l;
-    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
-                         sm.stage + w * kUnitLds<D>, o, m, l);
+    mfma_unit<BF, F8, D, MT>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
+                             sm.stage + w * kUnitLds<D>, o, m, l, c0, vis);
     const float lsum = column_sum(l);
     if (!p.split) {
         mfma_write_output<BF, F8, D>(p, qrow, o, lsum);
         return;
     }
     if (!merged) {
-        mfma_write_partial<F8, D>(p, qrow, p.slot_base + part, o, m, lsum);
+        mfma_write_partial<F8, D>(p, wrow, p.slot_base + part, o, m, lsum);
         return;
     }
-    mfma_workgroup_merge<F8, D>(p, qrow, p.slot_base + q, o, m, lsum, sm);
+    mfma_workgroup_merge<F8, D>(p, wrow, p.slot_base + q, o, m, lsum, sm);
 }
 
 // Shared-prefix units: workgroup (prefix group g, kv head, subgroup of 16 (member, query head)
@@ -965,10 +1020,23 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     constexpr int U = 8;                // load instructions in flight
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int grp = lane / LPP, sub = lane % LPP;
-    const int idx = blockIdx.x * 4 + wave;
-    if (idx >= p.num_seqs * p.num_q_heads)
+    const int idx = blockIdx.x * 4 + wave;  // workspace row
+    if (idx >= p.ws_rows)
         return;
-    const int seq = idx / p.num_q_heads;
+    int seq, orow;  // sequence and output row
+    if (p.mt_rows > 0) {  // workspace rows (sequence, row, head) of a multi-token decode
+        const int per_seq = p.mt_rows * p.num_q_heads;
+        seq = idx / per_seq;
+        const int r = idx % per_seq / p.num_q_heads;
+        const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
+        const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
+        if (r >= min(q_len, p.mt_rows))
+            return;
+        orow = (q0 + r) * p.num_q_heads + idx % p.num_q_heads;
+    } else {
+        seq = idx / p.num_q_heads;
+        orow = idx;
+    }
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int start = unit_start(p, seq, L);
     // parts of this row: shared-prefix parts in slots [0, n_pre), own parts after pre_slots.
@@ -988,6 +1056,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
     for (int jj = lane; jj < np; jj += kWave)
         M = fmaxf(M, ml[2 * slot_of(jj)]);
     M = wave_max(M);
+    // a row that sees no position (every part at -inf, possible under a multi-token tree mask)
+    // gets weights exp2(-inf) = 0 and is written as zeros
+    if (M == -INFINITY)
+        M = 0.0f;
     float W = 0.0f;
     for (int jj = lane; jj < np; jj += kWave)
         W += fast_exp2(ml[2 * slot_of(jj)] - M) * ml[2 * slot_of(jj) + 1];
@@ -1034,7 +1106,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
         uint2 w2;
         w2.x = pack2<BF>(o[0] * inv, o[1] * inv);
         w2.y = pack2<BF>(o[2] * inv, o[3] * inv);
-        *(uint2 *)(p.out + (size_t)idx * D + sub * 4) = w2;
+        *(uint2 *)(p.out + (size_t)orow * D + sub * 4) = w2;
     }
 }
 
@@ -1072,8 +1144,26 @@ hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hi
                     : launch_units<BF, F8, D, 1>(p, stream);
     if (e != hipSuccess || !p.split || p.fused_finish)
         return e;
-    const int rows = p.num_seqs * p.num_q_heads;
-    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((p.ws_rows + 3) / 4), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+// Multi-token decode: the MFMA kernel with per-column views of the rows' own positions, then the
+// merge of the split parts
+template <bool BF, bool F8, int D>
+hipError_t run_decode_multi(const DecodeParams &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D, true>),
+                       dim3(round_up8(p.wg_parts == kMfmaWaves
+                                          ? p.n_units
+                                          : (p.n_units + kMfmaWaves - 1) / kMfmaWaves)),
+                       dim3(kWave * kMfmaWaves), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.split)
+        return e;
+    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3((p.ws_rows + 3) / 4), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -1216,6 +1306,70 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
                                   : run_decode<true, false, 128>(gk, p, pp, stream);
     return d.c.head_dim == 64 ? run_decode<false, false, 64>(gk, p, pp, stream)
                               : run_decode<false, false, 128>(gk, p, pp, stream);
+}
+
+}  // namespace pa
+
+namespace pa {
+
+hipError_t launch_decode_multi(const DecodeLaunch &d, hipStream_t stream)
+{
+    if (d.num_seqs == 0 || d.total_q == 0 || d.max_q_len == 0)
+        return hipSuccess;
+    const int group = d.num_q_heads / d.c.num_kv_heads;
+    DecodeParams p = {};
+    p.query = (const uint16_t *)d.query;
+    p.k_cache = (const uint16_t *)d.k_cache;
+    p.v_cache = (const uint16_t *)d.v_cache;
+    p.block_tables = d.block_tables;
+    p.seq_lens = d.seq_lens;
+    p.out = (uint16_t *)d.out;
+    p.max_blocks = d.max_blocks;
+    p.num_seqs = d.num_seqs;
+    p.num_kv_heads = d.c.num_kv_heads;
+    p.num_q_heads = d.num_q_heads;
+    p.num_blocks = d.c.num_blocks;
+    p.max_seq_len = d.max_seq_len;
+    p.scale_log2 = (float)((double)d.scale * (d.fp8 ? (double)d.k_scale : 1.0) * 1.4426950408889634);
+    p.v_scale = d.fp8 ? d.v_scale : 1.0f;
+    p.cu_q = d.cu_q_lens;
+    p.tree_mask = d.tree_mask;
+    p.mt_rows = d.max_q_len;
+    p.total_q = d.total_q;
+    // the (row, query head) pairs of a kv head, kCols per subgroup
+    p.n_sub = (d.max_q_len * group + kCols - 1) / kCols;
+    p.split = d.max_parts > 0 ? 1 : 0;
+    p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
+    if (p.part_tokens < kBlock)
+        p.part_tokens = kBlock;
+    p.max_parts = p.split ? d.max_parts : 1;
+    p.wg_parts = p.split ? kMfmaWaves : 1;
+    p.slot_tokens = p.part_tokens * p.wg_parts;
+    p.ws_slots = (p.max_parts + p.wg_parts - 1) / p.wg_parts;
+    const int64_t rows = (int64_t)d.num_seqs * d.max_q_len * d.num_q_heads;
+    if (rows > 0x7fffffff)
+        return hipErrorInvalidValue;
+    p.ws_rows = (int32_t)rows;
+    // workspace: acc [slots][rows][D], then (m, l) [rows][slots][2]
+    p.ws_acc = (float *)d.workspace;
+    p.ws_ml = p.split ? p.ws_acc + (size_t)p.ws_rows * p.ws_slots * d.c.head_dim : nullptr;
+    const int64_t units = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub *
+                          (p.wg_parts == kMfmaWaves ? p.ws_slots : p.max_parts);
+    if (units > 0x7ffffff0)
+        return hipErrorInvalidValue;
+    p.n_units = (int32_t)units;
+    if (d.fp8) {
+        if (d.c.bf16)
+            return d.c.head_dim == 64 ? run_decode_multi<true, true, 64>(p, stream)
+                                      : run_decode_multi<true, true, 128>(p, stream);
+        return d.c.head_dim == 64 ? run_decode_multi<false, true, 64>(p, stream)
+                                  : run_decode_multi<false, true, 128>(p, stream);
+    }
+    if (d.c.bf16)
+        return d.c.head_dim == 64 ? run_decode_multi<true, false, 64>(p, stream)
+                                  : run_decode_multi<true, false, 128>(p, stream);
+    return d.c.head_dim == 64 ? run_decode_multi<false, false, 64>(p, stream)
+                              : run_decode_multi<false, false, 128>(p, stream);
 }
 
 }  // namespace pa

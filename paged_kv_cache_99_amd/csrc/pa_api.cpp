@@ -622,3 +622,148 @@ pa_status_t pa_prefill_chunk_tree(pa_dtype_t dtype, int32_t num_blocks, int32_t 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_seq_len,
+                                      int32_t partition_size)
+{
+    if (parts_of(max_seq_len, partition_size) == 0)
+        return 0;
+    return pa::decode_multi_workspace_used(num_seqs, max_q_len, num_q_heads, head_dim,
+                                           max_seq_len, partition_size);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status_t multi_call(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, void *out, const void *query, const void *k_cache,
+                       const void *v_cache, const int32_t *block_tables,
+                       int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                       const int32_t *cu_q_lens, const uint64_t *tree_mask, int32_t num_seqs,
+                       int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                       int32_t num_q_heads, float scale, int32_t partition_size, void *workspace,
+                       size_t workspace_bytes, void *stream, bool fp8, float k_scale,
+                       float v_scale)
+{
+    pa::CacheDims c;
+    pa_status_t s = check_cache(dtype, num_blocks, num_kv_heads, head_dim, &c);
+    if (s != PA_OK)
+        return s;
+    REQUIRE(num_seqs >= 0, "num_seqs %d < 0", num_seqs);
+    REQUIRE(total_q >= 0, "total_q %d < 0", total_q);
+    REQUIRE(max_q_len >= 1 && max_q_len <= pa::kMultiMaxRows, "max_q_len %d is outside [1, %d]",
+            max_q_len, pa::kMultiMaxRows);
+    REQUIRE(num_q_heads > 0 && num_q_heads % num_kv_heads == 0,
+            "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+            num_kv_heads);
+    REQUIRE(max_blocks_per_seq >= 0, "max_blocks_per_seq %d < 0", max_blocks_per_seq);
+    REQUIRE(max_seq_len >= 0 && (int64_t)max_seq_len <= (int64_t)PA_BLOCK_SIZE * max_blocks_per_seq,
+            "max_seq_len %d is outside [0, 16 * max_blocks_per_seq = %lld]", max_seq_len,
+            (long long)PA_BLOCK_SIZE * max_blocks_per_seq);
+    REQUIRE(partition_size >= 0 && partition_size % PA_BLOCK_SIZE == 0 && partition_size <= 1024,
+            "partition_size %d is not 0 or a multiple of 16 up to 1024", partition_size);
+    REQUIRE(scale > 0.0f && scale < 3.0e38f, "scale %g is not a finite positive number", (double)scale);
+    if (fp8)
+        REQUIRE(good_scale(k_scale) && good_scale(v_scale),
+                "k_scale %g / v_scale %g is not a finite positive number", (double)k_scale,
+                (double)v_scale);
+    // row indices (total_q rows, or sequence x max_q_len rows, times the heads) stay in int32
+    REQUIRE((int64_t)total_q * num_q_heads <= 0x7fffffff &&
+                (int64_t)num_seqs * max_q_len * num_q_heads <= 0x7fffffff,
+            "%d query rows x %d heads exceed the row index range", total_q, num_q_heads);
+    if (!pa::decode_supported(head_dim, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "no decode kernel for head_dim %d, group %d", head_dim,
+                    num_q_heads / num_kv_heads);
+    if (num_seqs == 0 || total_q == 0)
+        return ok();
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(query, "query");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    REQUIRE(block_tables != nullptr, "block_tables is NULL");
+    REQUIRE(seq_lens != nullptr, "seq_lens is NULL");
+    REQUIRE(cu_q_lens != nullptr, "cu_q_lens is NULL");
+    if (tree_mask != nullptr)
+        REQUIRE(((uintptr_t)tree_mask & 7) == 0, "tree_mask is not 8-byte aligned");
+    const size_t need = pa_decode_multi_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
+                                                       max_seq_len, partition_size);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                        need);
+        REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    }
+    pa::DecodeLaunch d;
+    d.c = c;
+    d.out = out;
+    d.query = query;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.max_blocks = max_blocks_per_seq;
+    d.seq_lens = seq_lens;
+    d.num_seqs = num_seqs;
+    d.max_seq_len = max_seq_len;
+    d.num_q_heads = num_q_heads;
+    d.scale = scale;
+    d.partition_size = partition_size;
+    d.max_parts = parts_of(max_seq_len, partition_size);
+    d.seq_starts = nullptr;
+    d.group_starts = nullptr;
+    d.num_groups = 0;
+    d.max_group_size = 0;
+    d.max_prefix_len = 0;
+    d.workspace = need > 0 ? workspace : nullptr;
+    d.fp8 = fp8;
+    d.c.fp8 = fp8;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    d.cu_q_lens = cu_q_lens;
+    d.tree_mask = tree_mask;
+    d.max_q_len = max_q_len;
+    d.total_q = total_q;
+    return launched(pa::launch_decode_multi(d, (hipStream_t)stream),
+                    fp8 ? "decode_multi_fp8" : "decode_multi");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_multi(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                            int32_t head_dim, void *out, const void *query, const void *k_cache,
+                            const void *v_cache, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *cu_q_lens, const uint64_t *tree_mask, int32_t num_seqs,
+                            int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                            int32_t num_q_heads, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    return multi_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                      block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, tree_mask, num_seqs,
+                      total_q, max_q_len, max_seq_len, num_q_heads, scale, partition_size,
+                      workspace, workspace_bytes, stream, false, 1.0f, 1.0f);
+}
+
+pa_status_t pa_decode_multi_fp8(pa_dtype_t dtype, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, void *out, const void *query,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *seq_lens, const int32_t *cu_q_lens,
+                                const uint64_t *tree_mask, int32_t num_seqs, int32_t total_q,
+                                int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                                float scale, float k_scale, float v_scale,
+                                int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                void *stream)
+{
+    return multi_call(dtype, num_blocks, num_kv_heads, head_dim, out, query, k_cache, v_cache,
+                      block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, tree_mask, num_seqs,
+                      total_q, max_q_len, max_seq_len, num_q_heads, scale, partition_size,
+                      workspace, workspace_bytes, stream, true, k_scale, v_scale);
+}
+
+}  // extern "C"

@@ -66,6 +66,12 @@ struct DecodeLaunch {
     bool fp8 = false;
     float k_scale = 1.0f;
     float v_scale = 1.0f;
+    // multi-token decode (launch_decode_multi): up to max_q_len query rows per sequence, laid out
+    // [total_q][num_q_heads][head_dim] by cu_q_lens [num_seqs + 1]; tree_mask [total_q] or null
+    const int32_t *cu_q_lens = nullptr;
+    const uint64_t *tree_mask = nullptr;
+    int32_t max_q_len = 0;
+    int32_t total_q = 0;
 };
 // Host-side shape logic (pa_shapes.cpp) ------------------------------------------------------
 // The MFMA decode (head groups of 3 or more) runs workgroups of this many waves, and in a split
@@ -74,6 +80,14 @@ constexpr int kDecodeMfmaWaves = 4;
 // Group sizes with a dedicated kernel; any other group size runs as several of these.
 bool decode_supported(int32_t head_dim, int32_t group);
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+// Multi-token decode: the MFMA decode kernel over (row, query head) columns, rows of up to
+// kMultiMaxRows per sequence; the workspace holds (sequence, row, head) partial rows.
+constexpr int kMultiMaxRows = 16;
+hipError_t launch_decode_multi(const DecodeLaunch &d, hipStream_t stream);
+// Bytes of workspace a split multi-token decode writes and reads: one fp32 partial (head_dim + 2
+// floats) per (sequence, row < max_q_len, query head) and slot of kDecodeMfmaWaves parts.
+size_t decode_multi_workspace_used(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_size);
 // Bytes of workspace a plain (unshared) decode of these sizes writes and reads: one fp32 partial
 // (head_dim + 2 floats) per (sequence, query head, slot). At most pa_decode_workspace_size.
 size_t decode_workspace_used(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

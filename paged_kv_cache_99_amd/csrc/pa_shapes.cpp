@@ -29,6 +29,17 @@ size_t decode_workspace_used(int32_t num_seqs, int32_t num_q_heads, int32_t num_
     return (size_t)num_seqs * num_q_heads * slots * (head_dim + 2) * sizeof(float);
 }
 
+size_t decode_multi_workspace_used(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_size)
+{
+    if (num_seqs <= 0 || max_q_len <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
+        partition_size <= 0 || max_seq_len <= 0)
+        return 0;  // unsplit: no partial results
+    const int parts = (max_seq_len + partition_size - 1) / partition_size;
+    const size_t slots = (size_t)(parts + kDecodeMfmaWaves - 1) / kDecodeMfmaWaves;
+    return (size_t)num_seqs * max_q_len * num_q_heads * slots * (head_dim + 2) * sizeof(float);
+}
+
 size_t prefill_widen_bytes(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
                            int32_t head_dim)
 {

@@ -22,6 +22,12 @@ from . import binding
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 
+# (row, query head) pairs per kv head up to which GpuStep sends short chunks to pa_decode_multi by
+# default: two of its 16-pair subgroups. Measured on 64 sequences of U{1024..4096} tokens (bf16):
+# 16 pairs 144-151 us and 32 pairs 229-231 us against 230-248 us for the chunk kernel; 64 pairs
+# 373 us against 250 us.
+MULTI_AUTO_PAIRS = 32
+
 
 def words_to_device(words: np.ndarray, dtype: str, device) -> torch.Tensor:
     """Upload 16-bit words (numpy uint16) as a float16/bfloat16 tensor of the same shape."""
@@ -78,11 +84,17 @@ class GpuStep:
     step runs every stage over the E4M3 caches (the *_fp8 entry points). Its chunks are prefilled
     over a widened 16-bit copy of their context (pa_prefill_chunk_fp8 with a workspace) when that
     copy takes at most widen_limit bytes, else with the codes converted inside the tile loop.
+
+    multi_token: chunks of at most 16 rows each (drafted tokens to verify, lecture 32 §5.4) go
+    through pa_decode_multi, which reads each context like a decode, instead of the chunk kernel of
+    pa_prefill_chunk; None picks it when every chunk is that short and a kv head's rows times its
+    query heads come to at most MULTI_AUTO_PAIRS (more pairs re-read the context per 16 of them).
     """
 
     def __init__(self, w, device="cuda", partition_size: Optional[int] = None,
                  shared_prefix: bool = False, kv_cache: str = "auto", k_scale: float = 1.0,
-                 v_scale: float = 1.0, fp8_pool=None, widen_limit: int = 1 << 30):
+                 v_scale: float = 1.0, fp8_pool=None, widen_limit: int = 1 << 30,
+                 multi_token: Optional[bool] = None):
         self.w = w
         self.device = torch.device(device)
         dt, dev = w.dtype, self.device
@@ -147,8 +159,20 @@ class GpuStep:
         self.pre_out = torch.empty_like(self.pre_query)
         cu = np.asarray(w.cu_q_lens)
         self.max_q_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
+        self.pre_max_seq_len = int(np.max(w.seq_lens[nd:])) if len(w.seq_lens) > nd else 0
+        short = 0 < self.max_q_len <= binding.MULTI_MAX_ROWS
+        if multi_token is None:
+            multi_token = short and self.max_q_len * (w.H_q // w.H_kv) <= MULTI_AUTO_PAIRS
+        self.multi_token = bool(multi_token)
+        if self.multi_token and not short:
+            raise ValueError(f"chunks of up to {self.max_q_len} rows: pa_decode_multi takes "
+                             f"{binding.MULTI_MAX_ROWS}")
+        self.multi_partition = binding.default_partition_size(self.pre_max_seq_len, 3)
+        self.multi_workspace = binding.alloc_decode_multi_workspace(
+            int(self.pre_tables.shape[0]), self.max_q_len, w.H_q, w.D, self.pre_max_seq_len,
+            self.multi_partition, dev) if self.multi_token else None
         self.pre_workspace = None
-        if self.fp8 and self.pre_query.shape[0]:
+        if self.fp8 and self.pre_query.shape[0] and not self.multi_token:
             n = binding.prefill_fp8_workspace_size(int(self.pre_tables.shape[0]),
                                                    int(self.pre_tables.shape[1]), w.H_kv, w.D)
             if 0 < n <= widen_limit:
@@ -206,7 +230,14 @@ class GpuStep:
                            self.partition_size, self.workspace, stream)
 
     def prefill(self, stream=None):
-        if self.pre_query.shape[0] and self.fp8:
+        if self.pre_query.shape[0] and self.multi_token:
+            binding.decode_multi(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
+                                 self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
+                                 self.pre_max_seq_len, self.w.scale, self.multi_partition,
+                                 self.multi_workspace, stream,
+                                 k_scale=self.k_scale if self.fp8 else None,
+                                 v_scale=self.v_scale if self.fp8 else None)
+        elif self.pre_query.shape[0] and self.fp8:
             binding.prefill_chunk_fp8(self.pre_out, self.pre_query, self.k_cache, self.v_cache,
                                       self.pre_tables, self.pre_lens, self.pre_cu, self.max_q_len,
                                       self.w.scale, self.k_scale, self.v_scale, stream,

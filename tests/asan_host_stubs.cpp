@@ -28,6 +28,8 @@ hipError_t launch_copy_blocks(const CacheDims &, void *, void *, const int32_t *
 
 hipError_t launch_decode(const DecodeLaunch &, hipStream_t) { return hipErrorNoDevice; }
 
+hipError_t launch_decode_multi(const DecodeLaunch &, hipStream_t) { return hipErrorNoDevice; }
+
 hipError_t decode_scratch(hipStream_t, void **) { return hipErrorNoDevice; }
 
 hipError_t launch_prefill(const PrefillLaunch &, hipStream_t) { return hipErrorNoDevice; }

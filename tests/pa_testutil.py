@@ -34,6 +34,25 @@ def oracle_pool_after_step(w, poison=False):
     return kc, vc
 
 
+def oracle_fp8_pool(w, k_scale, v_scale, poison=True):
+    """The workload's pool as E4M3 codes (the oracle's quantization), free slots poisoned with the
+    NaN code unless poison is False."""
+    kc = oracle.quantize_e4m3(w.k_cache, w.dtype, k_scale)
+    vc = oracle.quantize_e4m3(w.v_cache, w.dtype, v_scale)
+    if poison:
+        kc, vc = oracle.poison_free_slots_fp8(kc, vc, w.block_tables, w.seq_lens, w.num_blocks,
+                                              w.H_kv, w.D)
+    return kc, vc
+
+
+def oracle_fp8_after_step(w, kc, vc, k_scale, v_scale):
+    """The E4M3 pool a step's attention reads: copy_blocks, then the quantizing scatter."""
+    if len(w.copy_pairs):
+        kc, vc = oracle.copy_blocks_fp8(kc, vc, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
+    return oracle.reshape_and_cache_fp8(w.new_key, w.new_value, kc, vc, w.slot_mapping,
+                                        w.num_blocks, w.H_kv, w.D, w.dtype, k_scale, v_scale)
+
+
 def oracle_decode(w, kc, vc, pairs=None, nthreads=0):
     nd = w.n_decode
     return oracle.decode(w.query_decode, kc, vc, w.block_tables[:nd], w.seq_lens[:nd], w.H_q,

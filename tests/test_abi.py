@@ -209,3 +209,46 @@ def test_noalloc_decode_checks_its_scratch_limit_on_the_host():
     assert call(512, 64, 8, 32768, 512, out=None) == INVALID
     assert call(512, 8, 8, 32768, 512, dtype=FP8) == INVALID
     assert call(0, 8, 8, 32768, 512) == OK          # no sequences: a no-op
+
+
+def test_multi_token_decode_checks_on_the_host():
+    """pa_decode_multi / _fp8: the workspace size (one fp32 partial per (sequence, row, head) and
+    slot of four parts), and the host checks that refuse bad arguments before anything is
+    enqueued (no device is touched here)."""
+    lib = binding.lib()
+    f = ctypes.c_float
+    size = lib.pa_decode_multi_workspace_size
+    # 3 sequences x 4 rows x 32 heads, 4096 tokens in 512-token parts: 8 parts -> 2 slots
+    assert size(3, 4, 32, 128, 4096, 512) == 3 * 4 * 32 * 2 * 130 * 4
+    assert size(3, 4, 32, 128, 4096, 0) == 0      # unsplit
+    assert size(3, 4, 32, 128, 512, 512) == 0     # one part: unsplit
+    assert size(0, 4, 32, 128, 4096, 512) == 0
+
+    def call(**kw):
+        a = dict(dtype=BF16, num_kv_heads=8, out=FAKE, cu=FAKE, tree=None, num_seqs=3, total_q=12,
+                 max_q_len=4, max_seq_len=4096, num_q_heads=32, part=512, ws=FAKE,
+                 ws_bytes=size(3, 4, 32, 128, 4096, 512), fp8=False, k_scale=0.5)
+        a.update(kw)
+        head = [a["dtype"], 1000, a["num_kv_heads"], 128, a["out"], FAKE, FAKE, FAKE, FAKE, 256,
+                FAKE, a["cu"], a["tree"], a["num_seqs"], a["total_q"], a["max_q_len"],
+                a["max_seq_len"], a["num_q_heads"], f(0.088)]
+        tail = [a["part"], a["ws"], a["ws_bytes"], None]
+        if a["fp8"]:
+            return lib.pa_decode_multi_fp8(*head, f(a["k_scale"]), f(0.5), *tail)
+        return lib.pa_decode_multi(*head, *tail)
+
+    assert call(max_q_len=0) == INVALID
+    assert call(max_q_len=17) == INVALID
+    assert b"max_q_len" in lib.pa_last_error()
+    assert call(part=24) == INVALID
+    assert call(max_seq_len=256 * 16 + 1) == INVALID
+    assert call(num_q_heads=12) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(tree=FAKE + 4) == INVALID           # tree_mask not 8-byte aligned
+    assert call(ws_bytes=size(3, 4, 32, 128, 4096, 512) - 1) == WORKSPACE
+    assert call(ws=FAKE + 8) == INVALID             # workspace not 16-byte aligned
+    assert call(fp8=True, k_scale=0.0) == INVALID
+    assert call(dtype=FP8) == INVALID               # the 16-bit entry takes 16-bit caches
+    assert call(num_seqs=0) == OK                   # nothing to do: no-ops
+    assert call(total_q=0) == OK

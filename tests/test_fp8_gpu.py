@@ -17,27 +17,11 @@ import oracle
 import pa_workloads as W
 from paged_kv_cache_99_amd import binding
 from paged_kv_cache_99_amd.step import GpuStep, words_from_device, words_to_device
-from pa_testutil import assert_attention_close
+from pa_testutil import assert_attention_close, oracle_fp8_after_step, oracle_fp8_pool
 
 pytestmark = pytest.mark.gpu
 
 TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
-
-
-def oracle_fp8_pool(w, k_scale, v_scale, poison=True):
-    kc = oracle.quantize_e4m3(w.k_cache, w.dtype, k_scale)
-    vc = oracle.quantize_e4m3(w.v_cache, w.dtype, v_scale)
-    if poison:
-        kc, vc = oracle.poison_free_slots_fp8(kc, vc, w.block_tables, w.seq_lens, w.num_blocks,
-                                              w.H_kv, w.D)
-    return kc, vc
-
-
-def oracle_fp8_after_step(w, kc, vc, k_scale, v_scale):
-    if len(w.copy_pairs):
-        kc, vc = oracle.copy_blocks_fp8(kc, vc, w.copy_pairs, w.num_blocks, w.H_kv, w.D)
-    return oracle.reshape_and_cache_fp8(w.new_key, w.new_value, kc, vc, w.slot_mapping,
-                                        w.num_blocks, w.H_kv, w.D, w.dtype, k_scale, v_scale)
 
 
 def bytes_of(t):

@@ -49,7 +49,8 @@ def test_multi_token_rows_equal_per_row_decode(H_q, H_kv, D, dtype):
                 q_lens=k.tolist())
     print(f"[multi-token] {n} sequences, k in [{k.min()}, {k.max()}], {int(k.sum())} rows, "
           f"H_q={H_q} H_kv={H_kv} D={D} {dtype}", flush=True)
-    g = GpuStep(w)
+    g = GpuStep(w, multi_token=False)   # the chunk kernel (pa_decode_multi has its own tests)
+    assert not g.multi_token
     g.scatter()
     g.prefill()
     torch.cuda.synchronize()
