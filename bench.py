@@ -17,7 +17,10 @@ Prints ONE JSON line:
                on the current decode sources, else null;
   roofline_prefill  (steps with a prefill chunk) the chunk's causal FLOPs / its event time against
                the 2.5 PFLOP/s dense bf16 MFMA peak, with the MFMA-busy share of SIMD cycles from
-               the committed counter record of the current prefill sources, else null;
+               the committed counter record of the current prefill sources, else null. Steps
+               whose chunks are all short (drafted tokens, GpuStep.multi_token) read them with
+               pa_decode_multi instead: its roofline is HBM, algorithmic bytes as for prefill; in
+               a step with no one-token decodes it is also the line's roofline and cpu_baseline;
   step_tokens_per_s  query tokens the step attends for (decode sequences + prefill rows) / step
                time: the mixed step's 2048-token budget per step;
   cpu_baseline the CPU oracle (float64) timed on this host over the workload's decode (a bounded
@@ -191,6 +194,52 @@ def cpu_baseline(w, max_seconds, fp8=None):
             "cpu_model": cpu_model(),
             "single_thread": {"value": round(b1 / e1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"{n1} of {nd} sequences in {e1:.2f} s"}}
+
+
+def cpu_baseline_multi(w, max_seconds, fp8=None):
+    """The float64 oracle over the workload's short chunks (multi-token rows: every row and query
+    head of each sampled sequence), sequences taken in order until the sample passes max_seconds,
+    on every host thread; rate in GB/s of each sampled sequence's K/V read once (the algorithmic
+    bytes of pa_decode_multi)."""
+    import oracle
+    nd = w.n_decode
+    cu = np.asarray(w.cu_q_lens, np.int64)
+    S = len(cu) - 1
+    threads = oracle.max_threads()
+    esize = 2
+    if fp8 is not None:
+        esize = 1
+        k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, fp8[0])
+        v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, fp8[1])
+    lens = w.seq_lens[nd:].astype(np.int64)
+    n_seq, elapsed, t0 = 0, 0.0, time.perf_counter()
+    step = max(1, S // 8)
+    while n_seq < S:
+        take = np.arange(n_seq, min(S, n_seq + step))
+        pairs = np.array([(r, h) for s in take for r in range(cu[s], cu[s + 1])
+                          for h in range(w.H_q)], np.int32)
+        if len(pairs):
+            if fp8 is None:
+                oracle.prefill(w.query_prefill, w.k_cache, w.v_cache, w.block_tables[nd:],
+                               w.seq_lens[nd:], w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks,
+                               w.dtype, w.scale, rows=pairs, nthreads=threads)
+            else:
+                oracle.prefill_fp8(w.query_prefill, k8, v8, w.block_tables[nd:], w.seq_lens[nd:],
+                                   w.cu_q_lens, w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype,
+                                   w.scale, fp8[0], fp8[1], rows=pairs, nthreads=threads)
+        n_seq += len(take)
+        elapsed = time.perf_counter() - t0
+        if elapsed > max_seconds:
+            break
+    rows = int(cu[n_seq] - cu[0])
+    nbytes = int(np.sum(lens[:n_seq])) * 2 * w.H_kv * w.D * esize + 2 * rows * w.H_q * w.D * 2
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 oracle of the multi-token rows of {n_seq} of {S} sequences "
+                      f"({rows} rows x {w.H_q} query heads, {nbytes / 1e9:.3f} GB of K/V read "
+                      f"once per sequence) in {elapsed:.2f} s, pool before the step's scatter",
+            "seconds": round(elapsed, 3),
+            "cpu_model": cpu_model()}
 
 
 def cpu_baseline_prefill(w, max_seconds, fp8=None):
@@ -498,7 +547,26 @@ def main():
     if g.shared_prefix or u_bytes != d_bytes:
         out["decode_logical_bytes"] = int(d_bytes)
         out["decode_GBps_logical"] = round(d_bytes / (dec_ms * 1e-3) / 1e9, 2)
-    if has_prefill:
+    multi = has_prefill and g.multi_token
+    if multi:
+        # short chunks through pa_decode_multi: HBM-bound like a decode
+        m_gbs = p_bytes / (pre_ms * 1e-3) / 1e9
+        out["prefill_ms"] = round(pre_ms, 5)
+        out["prefill_ms_p10_p50_p90"] = [round(float(x), 5)
+                                         for x in np.percentile(pre_t, [10, 50, 90])]
+        out["multi_token_rows_per_s"] = round(int(g.pre_query.shape[0]) / (ms_per_step * 1e-3), 1)
+        mrec = committed_record(tag, "traffic", DECODE_SRCS)
+        out["roofline_prefill"] = {
+            "bound": "hbm",
+            "kernel": "pa_decode_multi" + ("_fp8" if fp8 else "") + " (multi-token + merge kernels)",
+            "achieved": round(m_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(m_gbs / HBM_PEAK_GBS, 4),
+            "traffic": mrec.get("hbm_bytes_per_launch") if mrec and not g.n_decode else None,
+            "algorithmic_bytes_per_launch": int(p_bytes), "flops_per_launch": int(p_flops)}
+        if not g.n_decode:  # the multi-token kernel is the step's dominant kernel
+            out["roofline"] = dict(out["roofline_prefill"])
+            out["pct_of_hbm_peak"] = round(100.0 * m_gbs / HBM_PEAK_GBS, 2)
+    elif has_prefill:
         out["prefill_ms"] = round(pre_ms, 5)
         out["prefill_ms_p10_p50_p90"] = [round(float(x), 5)
                                          for x in np.percentile(pre_t, [10, 50, 90])]
@@ -511,7 +579,10 @@ def main():
             "frac": out["prefill_mfma_frac"], "flops_per_launch": int(p_flops),
             # MFMA-busy share of SIMD cycles from the committed counter record of these sources
             "mfma_busy_counter": crec.get("mfma_busy_frac") if crec else None}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and multi and not g.n_decode:
+        out["cpu_baseline"] = cpu_baseline_multi(w, args.cpu_seconds,
+                                                 (args.k_scale, args.v_scale) if fp8 else None)
+    elif not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
                                            (args.k_scale, args.v_scale) if fp8 else None)
         if has_prefill:

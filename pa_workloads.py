@@ -341,6 +341,16 @@ def llama2_7b_decode(seed: int = 2, batch: int = 64) -> Workload:
     return build(lens, 32, 32, 128, "f16", seed + 1000, name="llama2_7b_decode")
 
 
+def llama2_7b_spec_decode(seed: int = 2, batch: int = 64, drafts: int = 4) -> Workload:
+    """The LLaMA-2-7B-shaped layer of llama2_7b_decode (same seeded U{512..4096} contexts, 32 q =
+    32 kv heads of 128, fp16) in a speculative step: every sequence appends `drafts` drafted tokens
+    (its last positions), verified together as one short chunk of that many rows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(512, 4096, size=batch, endpoint=True) + (drafts - 1)
+    return build(lens, 32, 32, 128, "f16", seed + 1000, n_decode=0, q_lens=[drafts] * batch,
+                 name=f"llama2_7b_spec{drafts}")
+
+
 def llama70b_gqa_decode(seed: int = 3, batch: int = 32) -> Workload:
     """70B-GQA-shaped long-context decode: 32 sequences of U{8192..32768} tokens, 64 q / 8 kv heads
     of 128, bf16, split into partitions of 512 tokens."""
@@ -375,6 +385,7 @@ NAMED = {
     "tiny_decode": tiny_decode,
     "llama2_7b_decode": llama2_7b_decode,
     "llama70b_gqa_decode": llama70b_gqa_decode,
+    "llama2_7b_spec4": llama2_7b_spec_decode,
     "prefix_sharing_2040": lambda seed=4: prefix_sharing_sampling(2040, seed),
     "prefix_sharing_2048": lambda seed=4: prefix_sharing_sampling(2048, seed),
     "chunked_prefill_mixed": chunked_prefill_mixed,
