@@ -337,11 +337,11 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
  * positions first_s + j for j <= i; with tree_mask, only those j whose bit j of
  * tree_mask[cu_q_lens[s] + i] is set. out equals pa_prefill_chunk's (pa_prefill_chunk_tree's with
  * a mask) for the same rows; a row that attends no position is written as zeros.
- * Each kv head's context is read once per 16 (row, query head) pairs, on MFMA, split into parts of
+ * Each kv head's context is read once per 32 (row, query head) pairs, on MFMA, split into parts of
  * partition_size tokens merged by rescaling with their maxima and sums of exponentials, as in
  * pa_decode ([OV] §9 (4)). The chunk kernel of pa_prefill_chunk instead reads it once per
  * workgroup of 256 pairs, which few rows leave mostly empty: this call is the faster one up to
- * about 32 pairs per kv head (max_q_len * num_q_heads / num_kv_heads), the chunk kernel beyond.
+ * 32 pairs per kv head (max_q_len * num_q_heads / num_kv_heads), the two are even at 64.
  *   query, out    [total_q][num_q_heads][head_dim] of `dtype` (F16 or BF16); out must not alias
  *                 an input.
  *   cu_q_lens     [num_seqs + 1] int32, cu_q_lens[0] = 0, non-decreasing, cu_q_lens[num_seqs] =

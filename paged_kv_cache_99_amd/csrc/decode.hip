@@ -505,13 +505,16 @@ __device__ __forceinline__ void wave_lds_fence()
 // tile t), m the running maximum of column j (log2 domain) and l this lane's share of column j's
 // running sum (the four row groups g add up to it). v_lds is the wave's own staging area
 // (kUnitLds<D> bytes). An empty range leaves o = 0, m = -inf, l = 0.
-// MT (multi-token rows): positions from c0 on are the query rows' own; column j sees position
-// c0 + i only when bit i of its vis is set (none from c0 + 32 on).
-template <bool BF, bool F8, int D, bool MT = false>
-__device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const int32_t *table,
-                                          int kvh, int t0, int t1, uint8_t *v_lds,
-                                          f32x4 (&o)[D / 16], float &m, float &l, int c0 = 0,
-                                          uint32_t vis = 0)
+// NCG column groups of 16 (query rows qrow[cg]) share every K operand and every transposed V
+// read: a unit of NCG groups reads the context once for 16 * NCG rows.
+// MT (multi-token rows): positions from c0 on are the query rows' own; column j of group cg sees
+// position c0 + i only when bit i of its vis[cg] is set (none from c0 + 32 on).
+template <bool BF, bool F8, int D, bool MT, int NCG>
+__device__ __forceinline__ void mfma_unit_cols(const DecodeParams &p, const int (&qrow)[NCG],
+                                               const int32_t *table, int kvh, int t0, int t1,
+                                               uint8_t *v_lds, f32x4 (&o)[NCG][D / 16],
+                                               float (&m)[NCG], float (&l)[NCG], int c0,
+                                               const uint32_t (&vis)[NCG])
 {
     constexpr int NC = D / 32;              // QK k-chunks
     constexpr int NT = D / 16;              // PV output tiles
@@ -524,17 +527,20 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
     const int lane = threadIdx.x & (kWave - 1);
     const int j = lane & 15, g = lane >> 4;
 
-    uint4 q[NC];
+    uint4 q[NCG][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-        q[c] = qrow >= 0 ? *(const uint4 *)(p.query + (size_t)qrow * D + qk_dim<F8>(c, g))
-                         : make_uint4(0, 0, 0, 0);
-
+    for (int cg = 0; cg < NCG; ++cg) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    m = -INFINITY;
-    l = 0.0f;
+        for (int c = 0; c < NC; ++c)
+            q[cg][c] = qrow[cg] >= 0
+                           ? *(const uint4 *)(p.query + (size_t)qrow[cg] * D + qk_dim<F8>(c, g))
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            o[cg][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        m[cg] = -INFINITY;
+        l[cg] = 0.0f;
+    }
 
     const uint8_t *kbase = (const uint8_t *)p.k_cache + (size_t)kvh * TILE;
     const uint8_t *vbase = (const uint8_t *)p.v_cache + (size_t)kvh * TILE;
@@ -638,10 +644,13 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
                 }
         };
 
-        auto scores = [&](int st, bool whole, const uint4(&kk)[2][KL], float(&sv)[8]) {
+        auto scores = [&](int st, bool whole, const uint4(&kk)[2][KL], float(&sv)[NCG][8]) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 acc[NCG];
+#pragma unroll
+                for (int cg = 0; cg < NCG; ++cg)
+                    acc[cg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     uint4 a;
@@ -654,62 +663,69 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
                     } else {
                         a = kk[b][c];
                     }
-                    acc = mfma16<BF>(a, q[c], acc);
+#pragma unroll
+                    for (int cg = 0; cg < NCG; ++cg)
+                        acc[cg] = mfma16<BF>(a, q[cg][c], acc[cg]);
                 }
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float x = acc[v] * p.scale_log2;
-                    if (!whole) {
-                        bool ok = tok_ok(st, b, 4 * g + v);
-                        if constexpr (MT) {
-                            const int tok = (bb + 2 * st + b) * kBlock + 4 * g + v;
-                            if (ok && tok >= c0)
-                                ok = tok - c0 < 32 && ((vis >> (tok - c0)) & 1u);
+                for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = acc[cg][v] * p.scale_log2;
+                        if (!whole) {
+                            bool ok = tok_ok(st, b, 4 * g + v);
+                            if constexpr (MT) {
+                                const int tok = (bb + 2 * st + b) * kBlock + 4 * g + v;
+                                if (ok && tok >= c0)
+                                    ok = tok - c0 < 32 && ((vis[cg] >> (tok - c0)) & 1u);
+                            }
+                            if (!ok)
+                                x = -INFINITY;
                         }
-                        if (!ok)
-                            x = -INFINITY;
+                        sv[cg][4 * b + v] = x;
                     }
-                    sv[4 * b + v] = x;
-                }
             }
         };
 
-        auto accumulate = [&](const float(&sv)[8]) {
-            float over = sv[0] - m;
+        auto accumulate = [&](const float(&sv)[NCG][8]) {
+            uint4 pb[NCG], pl[NCG];
 #pragma unroll
-            for (int e = 1; e < 8; ++e)
-                over = fmaxf(over, sv[e] - m);
-            if (!__all(!(over > kLazy))) {
-                float mx = sv[0];
+            for (int cg = 0; cg < NCG; ++cg) {
+                float over = sv[cg][0] - m[cg];
 #pragma unroll
                 for (int e = 1; e < 8; ++e)
-                    mx = fmaxf(mx, sv[e]);
-                mx = fmaxf(mx, xor_shfl(mx, 16));
-                mx = fmaxf(mx, xor_shfl(mx, 32));  // column max over the 4 row groups
-                if (mx > m) {
-                    const float alpha = fast_exp2(m - mx);  // 0 while m = -inf
-                    l *= alpha;
+                    over = fmaxf(over, sv[cg][e] - m[cg]);
+                if (!__all(!(over > kLazy))) {
+                    float mx = sv[cg][0];
 #pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        o[t] *= alpha;
-                    m = mx;
+                    for (int e = 1; e < 8; ++e)
+                        mx = fmaxf(mx, sv[cg][e]);
+                    mx = fmaxf(mx, xor_shfl(mx, 16));
+                    mx = fmaxf(mx, xor_shfl(mx, 32));  // column max over the 4 row groups
+                    if (mx > m[cg]) {
+                        const float alpha = fast_exp2(m[cg] - mx);  // 0 while m = -inf
+                        l[cg] *= alpha;
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            o[cg][t] *= alpha;
+                        m[cg] = mx;
+                    }
                 }
-            }
-            const float ms = m == -INFINITY ? 0.0f : m;
-            float pr[8];
+                const float ms = m[cg] == -INFINITY ? 0.0f : m[cg];
+                float pr[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pr[e] = fast_exp2(sv[e] - ms);  // masked: exp2(-inf) = 0
-                l += pr[e];
-            }
-            uint4 pb, pl;
-            uint32_t *hw = &pb.x, *lw = &pl.x;
+                for (int e = 0; e < 8; ++e) {
+                    pr[e] = fast_exp2(sv[cg][e] - ms);  // masked: exp2(-inf) = 0
+                    l[cg] += pr[e];
+                }
+                uint32_t *hw = &pb[cg].x, *lw = &pl[cg].x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hw[e] = pack2<BF>(pr[2 * e], pr[2 * e + 1]);
-                if constexpr (BF)
-                    lw[e] = pack2<BF>(pr[2 * e] - lo_f32<BF>(hw[e]),
-                                      pr[2 * e + 1] - hi_f32<BF>(hw[e]));
+                for (int e = 0; e < 4; ++e) {
+                    hw[e] = pack2<BF>(pr[2 * e], pr[2 * e + 1]);
+                    if constexpr (BF)
+                        lw[e] = pack2<BF>(pr[2 * e] - lo_f32<BF>(hw[e]),
+                                          pr[2 * e + 1] - hi_f32<BF>(hw[e]));
+                }
             }
 
 #pragma unroll
@@ -724,9 +740,12 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
                                            __builtin_bit_cast(uint2, lo4).y,
                                            __builtin_bit_cast(uint2, hi4).x,
                                            __builtin_bit_cast(uint2, hi4).y);
-                o[t] = mfma16<BF>(a, pb, o[t]);
-                if constexpr (BF)
-                    o[t] = mfma16<BF>(a, pl, o[t]);
+#pragma unroll
+                for (int cg = 0; cg < NCG; ++cg) {
+                    o[cg][t] = mfma16<BF>(a, pb[cg], o[cg][t]);
+                    if constexpr (BF)
+                        o[cg][t] = mfma16<BF>(a, pl[cg], o[cg][t]);
+                }
             }
         };
 
@@ -743,7 +762,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
             if (st + 1 < nsteps)
                 load_v(st + 1, va);
             wave_lds_fence();
-            float sv[8];
+            float sv[NCG][8];
             scores(st, whole, ka, sv);
             if (st + 1 < nsteps)
                 load_k(st + 1, ka);
@@ -751,6 +770,24 @@ __device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const
         }
     }
 
+}
+
+// One column group of query rows, no multi-token view: the plain and shared-prefix decodes.
+template <bool BF, bool F8, int D>
+__device__ __forceinline__ void mfma_unit(const DecodeParams &p, int qrow, const int32_t *table,
+                                          int kvh, int t0, int t1, uint8_t *v_lds,
+                                          f32x4 (&o)[D / 16], float &m, float &l)
+{
+    const int qr[1] = {qrow};
+    const uint32_t vis[1] = {0u};
+    f32x4 oo[1][D / 16];
+    float mm[1], ll[1];
+    mfma_unit_cols<BF, F8, D, false, 1>(p, qr, table, kvh, t0, t1, v_lds, oo, mm, ll, 0, vis);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+        o[t] = oo[0][t];
+    m = mm[0];
+    l = ll[0];
 }
 
 // Column sums of the four row groups' running sums (every lane of column j gets column j's).
@@ -877,12 +914,8 @@ __device__ __forceinline__ void wave_share(int s0, int s1, int w, int &t0, int &
 //    times their share of the HBM traffic.
 //  * Otherwise (p.wg_parts == 1): the waves are independent units (sequence, part, subgroup, kv
 //    head) that write their own partial result, or the output when the decode is not split.
-// MT: multi-token decode (p.mt_rows > 0). The columns of a kv head are its (row, query head)
-// pairs, row-major: column v of the group is row v / G, query head kvh * G + v % G, and the
-// subgroups cover the mt_rows * G pairs. Each column carries its row's view of the rows' own
-// positions (mfma_unit's c0 and vis); workspace rows are (sequence, row, head).
 
-template <bool BF, bool F8, int D, bool MT = false>
+template <bool BF, bool F8, int D>
 __global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_mfma_kernel(DecodeParams p)
 {
@@ -894,23 +927,13 @@ decode_mfma_kernel(DecodeParams p)
     const int unit = merged ? wg : wg * kMfmaWaves + w;
     if (unit >= p.n_units)
         return;  // uniform over the workgroup in the merged mode
-    // MT numbers the subgroups fastest: the subgroups of one (sequence, slot, kv head) read the
-    // same K/V and run side by side on one XCD, so all but the first find it in that XCD's L2
-    int rest = unit, sub = 0;
-    if constexpr (MT) {
-        sub = rest % p.n_sub;
-        rest /= p.n_sub;
-    }
-    const int seq = rest % p.num_seqs;
-    rest /= p.num_seqs;
+    const int seq = unit % p.num_seqs;
+    int rest = unit / p.num_seqs;
     const int n_slot = merged ? p.ws_slots - p.slot_base : p.max_parts;  // slots (parts) per row
     const int q = unit_part(p, rest % n_slot, n_slot);
     rest /= n_slot;
-    if constexpr (!MT) {
-        sub = rest % p.n_sub;
-        rest /= p.n_sub;
-    }
-    const int kvh = rest;
+    const int sub = rest % p.n_sub;
+    const int kvh = rest / p.n_sub;
     const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
     const int start = unit_start(p, seq, L);
     const int part = merged ? q * kMfmaWaves + w : q;
@@ -925,43 +948,98 @@ decode_mfma_kernel(DecodeParams p)
         t1 = min(L, t0 + p.part_tokens);
     }
     const int G = p.num_q_heads / p.num_kv_heads;
-    int qrow, wrow;  // query / output row and workspace row of this lane's column (-1: none)
-    int c0 = 0;
-    uint32_t vis = 0;
-    if constexpr (MT) {
-        // offsets are clamped to [0, total_q] so that no index contents reach outside the arrays
-        const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
-        const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
-        if (sub * kCols >= min(q_len, p.mt_rows) * G)
-            return;  // no row of this subgroup (uniform over the workgroup in the merged mode)
-        const int v = sub * kCols + (lane & 15), r = v / G;
-        const bool ok = r < min(q_len, p.mt_rows);
-        const int head = kvh * G + v % G;
-        qrow = ok ? (q0 + r) * p.num_q_heads + head : -1;
-        wrow = ok ? (seq * p.mt_rows + r) * p.num_q_heads + head : -1;
-        c0 = L - q_len;  // position of row 0
-        vis = ok ? (2u << r) - 1u : 0u;  // rows 0..r (r < mt_rows <= 16)
-        if (ok && p.tree_mask)
-            vis &= (uint32_t)p.tree_mask[q0 + r];
-    } else {
-        const int h = sub * kCols + (lane & 15);
-        qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
-        wrow = qrow;
-    }
+    const int h = sub * kCols + (lane & 15);
+    const int qrow = h < G ? seq * p.num_q_heads + kvh * G + h : -1;
     f32x4 o[NT];
     float m, l;
-    mfma_unit<BF, F8, D, MT>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
-                             sm.stage + w * kUnitLds<D>, o, m, l, c0, vis);
+    mfma_unit<BF, F8, D>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh, t0, t1,
+                         sm.stage + w * kUnitLds<D>, o, m, l);
     const float lsum = column_sum(l);
     if (!p.split) {
         mfma_write_output<BF, F8, D>(p, qrow, o, lsum);
         return;
     }
     if (!merged) {
-        mfma_write_partial<F8, D>(p, wrow, p.slot_base + part, o, m, lsum);
+        mfma_write_partial<F8, D>(p, qrow, p.slot_base + part, o, m, lsum);
         return;
     }
-    mfma_workgroup_merge<F8, D>(p, wrow, p.slot_base + q, o, m, lsum, sm);
+    mfma_workgroup_merge<F8, D>(p, qrow, p.slot_base + q, o, m, lsum, sm);
+}
+
+// Multi-token decode (p.mt_rows > 0): the MFMA units of decode_mfma_kernel, whose columns are the
+// (row, query head) pairs of a kv head, row-major (pair v: row v / G, query head kvh * G + v % G),
+// in NCG groups of 16 per wave that share the wave's K and V reads. Workgroups are numbered with
+// the subgroups of 16 * NCG pairs fastest, so that the subgroups reading one (sequence, slot,
+// kv head) run side by side on one XCD and all but the first find the context in its L2. Each
+// column carries its row's view of the rows' own positions (mfma_unit_cols' c0 and vis);
+// workspace rows are (sequence, row, head). Two groups take up to 232 registers: two waves per
+// SIMD instead of three.
+template <bool BF, bool F8, int D, int NCG>
+__global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4 - NCG))) void
+decode_multi_kernel(DecodeParams p)
+{
+    constexpr int NT = D / 16;
+    __shared__ __align__(16) MfmaLds<D> sm;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
+    const bool merged = p.wg_parts == kMfmaWaves;
+    const int unit = merged ? wg : wg * kMfmaWaves + w;
+    if (unit >= p.n_units)
+        return;  // uniform over the workgroup in the merged mode
+    int rest = unit;
+    const int sub = rest % p.n_sub;
+    rest /= p.n_sub;
+    const int seq = rest % p.num_seqs;
+    rest /= p.num_seqs;
+    const int n_slot = merged ? p.ws_slots : p.max_parts;  // slots (parts) per row
+    const int q = unit_part(p, rest % n_slot, n_slot);
+    const int kvh = rest / n_slot;
+    const int L = min(max(p.seq_lens[seq], 0), p.max_seq_len);
+    const int part = merged ? q * kMfmaWaves + w : q;
+    if (p.split && q * p.slot_tokens >= L)
+        return;  // the slot holds no tokens (uniform over the workgroup in the merged mode)
+    int t0, t1;
+    if (merged) {
+        wave_share(q * p.slot_tokens, min(L, (q + 1) * p.slot_tokens), w, t0, t1);
+    } else {
+        t0 = min(L, part * p.part_tokens);
+        t1 = min(L, t0 + p.part_tokens);
+    }
+    const int G = p.num_q_heads / p.num_kv_heads;
+    // offsets are clamped to [0, total_q] so that no index contents reach outside the arrays
+    const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
+    const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
+    const int rows = min(q_len, p.mt_rows);
+    if (sub * kCols * NCG >= rows * G)
+        return;  // no row of this subgroup (uniform over the workgroup in the merged mode)
+    const int c0 = L - q_len;  // position of row 0
+    int qrow[NCG], wrow[NCG];  // query / output row and workspace row of each column (-1: none)
+    uint32_t vis[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+        const int v = (sub * NCG + cg) * kCols + (lane & 15), r = v / G;
+        const bool ok = r < rows;
+        const int head = kvh * G + v % G;
+        qrow[cg] = ok ? (q0 + r) * p.num_q_heads + head : -1;
+        wrow[cg] = ok ? (seq * p.mt_rows + r) * p.num_q_heads + head : -1;
+        vis[cg] = ok ? (2u << r) - 1u : 0u;  // rows 0..r (r < mt_rows <= 16)
+        if (ok && p.tree_mask)
+            vis[cg] &= (uint32_t)p.tree_mask[q0 + r];
+    }
+    f32x4 o[NCG][NT];
+    float m[NCG], l[NCG];
+    mfma_unit_cols<BF, F8, D, true, NCG>(p, qrow, p.block_tables + (size_t)seq * p.max_blocks, kvh,
+                                         t0, t1, sm.stage + w * kUnitLds<D>, o, m, l, c0, vis);
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+        const float lsum = column_sum(l[cg]);
+        if (!p.split)
+            mfma_write_output<BF, F8, D>(p, qrow[cg], o[cg], lsum);
+        else if (!merged)
+            mfma_write_partial<F8, D>(p, wrow[cg], part, o[cg], m[cg], lsum);
+        else
+            mfma_workgroup_merge<F8, D>(p, wrow[cg], q, o[cg], m[cg], lsum, sm);  // every wave
+    }
 }
 
 // Shared-prefix units: workgroup (prefix group g, kv head, subgroup of 16 (member, query head)
@@ -1152,13 +1230,16 @@ hipError_t run_decode(int gk, const DecodeParams &p, const DecodeParams *pre, hi
 // Multi-token decode: the MFMA kernel with per-column views of the rows' own positions, then the
 // merge of the split parts
 template <bool BF, bool F8, int D>
-hipError_t run_decode_multi(const DecodeParams &p, hipStream_t stream)
+hipError_t run_decode_multi(int ncg, const DecodeParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_mfma_kernel<BF, F8, D, true>),
-                       dim3(round_up8(p.wg_parts == kMfmaWaves
-                                          ? p.n_units
-                                          : (p.n_units + kMfmaWaves - 1) / kMfmaWaves)),
-                       dim3(kWave * kMfmaWaves), 0, stream, p);
+    const dim3 grid(round_up8(p.wg_parts == kMfmaWaves ? p.n_units
+                                                       : (p.n_units + kMfmaWaves - 1) / kMfmaWaves));
+    if (ncg == 2)
+        hipLaunchKernelGGL((decode_multi_kernel<BF, F8, D, 2>), grid, dim3(kWave * kMfmaWaves), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<BF, F8, D, 1>), grid, dim3(kWave * kMfmaWaves), 0,
+                           stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.split)
         return e;
@@ -1336,8 +1417,11 @@ hipError_t launch_decode_multi(const DecodeLaunch &d, hipStream_t stream)
     p.tree_mask = d.tree_mask;
     p.mt_rows = d.max_q_len;
     p.total_q = d.total_q;
-    // the (row, query head) pairs of a kv head, kCols per subgroup
-    p.n_sub = (d.max_q_len * group + kCols - 1) / kCols;
+    // the (row, query head) pairs of a kv head: one column group of kCols when they fit it, else
+    // subgroups of two column groups per wave
+    const int pairs = d.max_q_len * group;
+    const int ncg = pairs > kCols ? 2 : 1;
+    p.n_sub = (pairs + kCols * ncg - 1) / (kCols * ncg);
     p.split = d.max_parts > 0 ? 1 : 0;
     p.part_tokens = p.split ? d.partition_size : ((d.max_seq_len + kBlock - 1) / kBlock) * kBlock;
     if (p.part_tokens < kBlock)
@@ -1360,16 +1444,16 @@ hipError_t launch_decode_multi(const DecodeLaunch &d, hipStream_t stream)
     p.n_units = (int32_t)units;
     if (d.fp8) {
         if (d.c.bf16)
-            return d.c.head_dim == 64 ? run_decode_multi<true, true, 64>(p, stream)
-                                      : run_decode_multi<true, true, 128>(p, stream);
-        return d.c.head_dim == 64 ? run_decode_multi<false, true, 64>(p, stream)
-                                  : run_decode_multi<false, true, 128>(p, stream);
+            return d.c.head_dim == 64 ? run_decode_multi<true, true, 64>(ncg, p, stream)
+                                      : run_decode_multi<true, true, 128>(ncg, p, stream);
+        return d.c.head_dim == 64 ? run_decode_multi<false, true, 64>(ncg, p, stream)
+                                  : run_decode_multi<false, true, 128>(ncg, p, stream);
     }
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? run_decode_multi<true, false, 64>(p, stream)
-                                  : run_decode_multi<true, false, 128>(p, stream);
-    return d.c.head_dim == 64 ? run_decode_multi<false, false, 64>(p, stream)
-                              : run_decode_multi<false, false, 128>(p, stream);
+        return d.c.head_dim == 64 ? run_decode_multi<true, false, 64>(ncg, p, stream)
+                                  : run_decode_multi<true, false, 128>(ncg, p, stream);
+    return d.c.head_dim == 64 ? run_decode_multi<false, false, 64>(ncg, p, stream)
+                              : run_decode_multi<false, false, 128>(ncg, p, stream);
 }
 
 }  // namespace pa

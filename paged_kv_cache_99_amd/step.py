@@ -23,9 +23,9 @@ from . import binding
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 # (row, query head) pairs per kv head up to which GpuStep sends short chunks to pa_decode_multi by
-# default: two of its 16-pair subgroups. Measured on 64 sequences of U{1024..4096} tokens (bf16):
-# 16 pairs 144-151 us and 32 pairs 229-231 us against 230-248 us for the chunk kernel; 64 pairs
-# 373 us against 250 us.
+# default: one wave's two column groups. Measured on 64 sequences of U{1024..4096} tokens (bf16):
+# 16 pairs 146-153 us and 32 pairs 160 us against 236-248 us for the chunk kernel; 64 pairs (two
+# subgroups) 253 us against 245 us.
 MULTI_AUTO_PAIRS = 32
 
 
