@@ -360,6 +360,16 @@ def llama70b_gqa_decode(seed: int = 3, batch: int = 32) -> Workload:
                  name="llama70b_gqa_decode")
 
 
+def llama70b_gqa_spec_decode(seed: int = 3, batch: int = 32, drafts: int = 4) -> Workload:
+    """The 70B-GQA-shaped layer of llama70b_gqa_decode (same seeded U{8192..32768} contexts, 64 q /
+    8 kv heads of 128, bf16, 512-token parts) in a speculative step: every sequence appends `drafts`
+    drafted tokens, verified together as one short chunk (drafts x 8 query heads per kv head)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(8192, 32768, size=batch, endpoint=True) + (drafts - 1)
+    return build(lens, 64, 8, 128, "bf16", seed + 1000, n_decode=0, q_lens=[drafts] * batch,
+                 partition_size=512, name=f"llama70b_gqa_spec{drafts}")
+
+
 def prefix_sharing_sampling(prefix: int = 2040, seed: int = 4) -> Workload:
     """32 groups x 8 parallel samples sharing a prompt of `prefix` tokens (128 blocks, ref_cnt 8),
     private suffixes U{1..512}, 32 q = 32 kv heads of 128, fp16. With prefix 2040 the last shared
@@ -386,6 +396,7 @@ NAMED = {
     "llama2_7b_decode": llama2_7b_decode,
     "llama70b_gqa_decode": llama70b_gqa_decode,
     "llama2_7b_spec4": llama2_7b_spec_decode,
+    "llama70b_gqa_spec4": llama70b_gqa_spec_decode,
     "prefix_sharing_2040": lambda seed=4: prefix_sharing_sampling(2040, seed),
     "prefix_sharing_2048": lambda seed=4: prefix_sharing_sampling(2048, seed),
     "chunked_prefill_mixed": chunked_prefill_mixed,
