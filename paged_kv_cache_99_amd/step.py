@@ -127,6 +127,7 @@ class GpuStep:
         self.max_seq_len = int(np.max(w.seq_lens[:nd])) if nd else 0
         if partition_size is None:
             partition_size = getattr(w, "partition_size", None)
+        given_partition = partition_size  # the caller's or the workload's, else None
         meta = getattr(w, "meta", {}) or {}
         self.shared_prefix = bool(shared_prefix and "group_starts" in meta and nd)
         if partition_size is None:
@@ -167,7 +168,8 @@ class GpuStep:
         if self.multi_token and not short:
             raise ValueError(f"chunks of up to {self.max_q_len} rows: pa_decode_multi takes "
                              f"{binding.MULTI_MAX_ROWS}")
-        self.multi_partition = binding.default_partition_size(self.pre_max_seq_len, 3)
+        self.multi_partition = (int(given_partition) if given_partition is not None else
+                                binding.default_partition_size(self.pre_max_seq_len, 3))
         self.multi_workspace = binding.alloc_decode_multi_workspace(
             int(self.pre_tables.shape[0]), self.max_q_len, w.H_q, w.D, self.pre_max_seq_len,
             self.multi_partition, dev) if self.multi_token else None

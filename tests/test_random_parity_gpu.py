@@ -24,15 +24,19 @@ GROUPS = [(4, 4), (8, 8), (16, 8), (32, 8), (12, 4), (6, 2), (24, 8), (10, 2), (
 PARTS = [None, 0, 16, 256, 512, 1024]
 
 
-def draw_case(case, max_len=3000):
-    rng = np.random.default_rng(9100 + case)
+def draw_case(case, max_len=3000, short=False):
+    rng = np.random.default_rng((9300 if short else 9100) + case)
     H_q, H_kv = GROUPS[rng.integers(len(GROUPS))]
     D = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
     n_dec = int(rng.integers(1, 12))
     lens = rng.integers(1, int(rng.choice([64, 700, max_len])), size=n_dec).tolist()
     q_lens = []
-    if rng.random() < 0.6:
+    if short:  # 1-6 short chunks (drafted tokens) of 1-16 rows over 0-2999 cached tokens
+        n_pre = int(rng.integers(1, 7))
+        q_lens = rng.integers(1, 17, size=n_pre).tolist()
+        lens += (rng.integers(0, 3000, size=n_pre) + np.array(q_lens)).tolist()
+    elif rng.random() < 0.6:
         n_pre = int(rng.integers(1, 4))
         q_lens = rng.integers(1, 300, size=n_pre).tolist()
         lens += (rng.integers(0, 1500, size=n_pre) + np.array(q_lens)).tolist()
@@ -48,16 +52,26 @@ def test_random_step_matches_oracle(case):
     check_case(case)
 
 
-def check_case(case, max_len=3000):
-    """One seeded random step on the GPU, 16-bit and E4M3 caches, against the oracle."""
-    w, (ks, vs) = draw_case(case, max_len)
+@pytest.mark.parametrize("case", range(12))
+def test_random_short_chunk_step_matches_oracle(case):
+    """Steps whose chunks are 1-16 drafted rows, read by pa_decode_multi (any number of (row,
+    head) pairs per kv head: one or two column groups, one or more subgroups)."""
+    check_case(case, short=True)
+
+
+def check_case(case, max_len=3000, short=False):
+    """One seeded random step on the GPU, 16-bit and E4M3 caches, against the oracle. short: the
+    chunks are drafted rows, forced through pa_decode_multi."""
+    w, (ks, vs) = draw_case(case, max_len, short)
     nd = w.n_decode
     tag = (f"case {case}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} decodes={nd} "
            f"chunks={np.diff(w.cu_q_lens).tolist() if len(w.cu_q_lens) else []} "
            f"partition={w.partition_size}")
     print(f"[random] {tag}", flush=True)
 
-    g = GpuStep(w)
+    mt = True if short else None
+    g = GpuStep(w, multi_token=mt)
+    assert g.multi_token or not short
     g.run()
     torch.cuda.synchronize()
     kc, vc = oracle_pool_after_step(w)
@@ -73,7 +87,7 @@ def check_case(case, max_len=3000):
 
     k8 = oracle.quantize_e4m3(w.k_cache, w.dtype, ks)
     v8 = oracle.quantize_e4m3(w.v_cache, w.dtype, vs)
-    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(k8, v8))
+    g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(k8, v8), multi_token=mt)
     g.run()
     torch.cuda.synchronize()
     if len(w.copy_pairs):
