@@ -75,3 +75,25 @@ def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys)
             assert cp["kind"] == "oracle" and cp["unit"] == "GFLOP/s" and cp["value"] > 0
     else:
         assert "roofline_prefill" not in d and "cpu_baseline_prefill" not in d
+
+
+@pytest.mark.gpu
+def test_bench_line_of_a_speculative_step(monkeypatch, capsys):
+    """A step of drafted rows only (llama2_7b_spec4): its rows go through pa_decode_multi, whose
+    HBM roofline and CPU baseline become the line's."""
+    print("[bench contract] llama2_7b_spec4", file=sys.stderr, flush=True)
+    run_bench(monkeypatch, "--workload", "llama2_7b_spec4", "--steps", "3", "--warmup", "1",
+              "--cpu-seconds", "2")
+    lines = [l for l in capsys.readouterr().out.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for k in REQUIRED:
+        assert k in d, k
+    assert d["config"]["num_seqs"] == 0 and d["config"]["prefill_rows"] == 256
+    rf, rp = d["roofline"], d["roofline_prefill"]
+    assert rf["kernel"].startswith("pa_decode_multi") and rf == rp
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and 0 < rf["frac"] < 1
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert d["multi_token_rows_per_s"] > 0 and d["prefill_ms"] > 0
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["sample"]
