@@ -970,9 +970,9 @@ decode_mfma_kernel(DecodeParams p)
 // (row, query head) pairs of a kv head, row-major (pair v: row v / G, query head kvh * G + v % G),
 // in NCG groups of 16 per wave that share the wave's K and V reads. Workgroups are numbered with
 // the subgroups of 16 * NCG pairs fastest, so that the subgroups reading one (sequence, slot,
-// kv head) run side by side on one XCD and all but the first find the context in its L2. Each
-// column carries its row's view of the rows' own positions (mfma_unit_cols' c0 and vis);
-// workspace rows are (sequence, row, head). Two groups take up to 232 registers: two waves per
+// kv head) run side by side on one XCD, where the later ones find part of the context in its L2.
+// Each column carries its row's view of the rows' own positions (mfma_unit_cols' c0 and vis);
+// workspace rows are (sequence, row, head). Two groups take up to 252 registers: two waves per
 // SIMD instead of three.
 template <bool BF, bool F8, int D, int NCG>
 __global__ __launch_bounds__(kWave * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4 - NCG))) void
