@@ -1006,9 +1006,10 @@ decode_multi_kernel(DecodeParams p)
         t1 = min(L, t0 + p.part_tokens);
     }
     const int G = p.num_q_heads / p.num_kv_heads;
-    // offsets are clamped to [0, total_q] so that no index contents reach outside the arrays
-    const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
-    const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
+    // offsets are clamped to [0, total_q] so that no index contents reach outside the arrays; no
+    // cu_q: one row per sequence (a plain decode of a head group above kCols)
+    const int q0 = p.cu_q ? min(max(p.cu_q[seq], 0), p.total_q) : seq;
+    const int q_len = p.cu_q ? min(max(p.cu_q[seq + 1], q0), p.total_q) - q0 : 1;
     const int rows = min(q_len, p.mt_rows);
     if (sub * kCols * NCG >= rows * G)
         return;  // no row of this subgroup (uniform over the workgroup in the merged mode)
@@ -1106,8 +1107,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p)
         const int per_seq = p.mt_rows * p.num_q_heads;
         seq = idx / per_seq;
         const int r = idx % per_seq / p.num_q_heads;
-        const int q0 = min(max(p.cu_q[seq], 0), p.total_q);
-        const int q_len = min(max(p.cu_q[seq + 1], q0), p.total_q) - q0;
+        const int q0 = p.cu_q ? min(max(p.cu_q[seq], 0), p.total_q) : seq;
+        const int q_len = p.cu_q ? min(max(p.cu_q[seq + 1], q0), p.total_q) - q0 : 1;
         if (r >= min(q_len, p.mt_rows))
             return;
         orow = (q0 + r) * p.num_q_heads + idx % p.num_q_heads;
@@ -1298,6 +1299,17 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream)
     if (d.num_seqs == 0)
         return hipSuccess;
     const int group = d.num_q_heads / d.c.num_kv_heads;
+    if (group > kCols && !(d.group_starts != nullptr && d.num_groups > 0)) {
+        // head groups above one MFMA column group (MQA-like): the multi-token units with one row
+        // per sequence hold 32 query heads per wave, so each context is read once per 32 heads
+        // instead of once per 16 (the same workspace rows and slots as the MFMA decode)
+        DecodeLaunch m = d;
+        m.cu_q_lens = nullptr;
+        m.tree_mask = nullptr;
+        m.max_q_len = 1;
+        m.total_q = d.num_seqs;
+        return launch_decode_multi(m, stream);
+    }
     // groups of 1 and 2: one unit per query head pair on the vector ALU; larger groups: up to 16
     // query heads per unit on MFMA
     const int gk = group <= 2 ? group : kCols;

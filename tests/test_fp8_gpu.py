@@ -116,7 +116,8 @@ def test_decode_named_workload(name):
                            absolute=True)
 
 
-@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (32, 8), (64, 8), (6, 2), (12, 4)])
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (32, 8), (64, 8), (6, 2), (12, 4), (64, 2),
+                                      (48, 1)])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_decode_head_groups(H_q, H_kv, D, dtype):

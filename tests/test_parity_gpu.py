@@ -111,7 +111,8 @@ def test_decode_named_workload(name):
 
 
 # --------------------------------------------------------------------- decode: shapes and edges
-@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 4), (16, 4), (8, 1), (32, 2), (12, 4), (6, 2)])
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 4), (16, 4), (8, 1), (32, 2), (12, 4), (6, 2),
+                                      (64, 2), (40, 1)])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_decode_head_groups(H_q, H_kv, D, dtype):
