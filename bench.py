@@ -31,6 +31,8 @@ Prints ONE JSON line:
                far larger than the 256 MB Infinity Cache, so each step reads them from HBM;
                --evict-mb 512 also displaces every cache level before each timed decode, to show
                that.
+  stages       copy_blocks and reshape_and_cache (where the step has them): mean event time per
+               call, algorithmic bytes (below) and their rate against the 8 TB/s HBM peak;
   graph        (--graph) the same step recorded once as a HIP graph and replayed: time per step
                and the rates above over it, for steps whose kernels are short enough that host
                launches show.
@@ -432,6 +434,9 @@ def main():
     ev = TimingEvents(K)   # decode call of each step
     evp = TimingEvents(K)  # prefill call of each step
     has_prefill = g.pre_query.shape[0] > 0
+    has_copy, has_scatter = len(w.copy_pairs) > 0, len(w.slot_mapping) > 0
+    evc = TimingEvents(K) if has_copy else None     # copy_blocks call of each step
+    evs = TimingEvents(K) if has_scatter else None  # reshape_and_cache call of each step
     # eviction by reading: a write would leave dirty lines whose write-back competes with the
     # decode's reads
     evict = (torch.zeros(args.evict_mb << 18, dtype=torch.int32, device="cuda")
@@ -439,8 +444,16 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        if evc is not None:
+            evc.record(i, False, stream)
         g.copy()
+        if evc is not None:
+            evc.record(i, True, stream)
+        if evs is not None:
+            evs.record(i, False, stream)
         g.scatter()
+        if evs is not None:
+            evs.record(i, True, stream)
         if evict is not None:
             torch.amax(evict)
         ev.record(i, False, stream)
@@ -455,6 +468,11 @@ def main():
     ms_per_step = wall * 1e3 / K
     dec_t = [ev.elapsed_ms(i) for i in range(K)] if g.n_decode else [0.0]
     pre_t = [evp.elapsed_ms(i) for i in range(K)] if has_prefill else [0.0]
+    stage_us = {}
+    for name, e in (("copy_blocks", evc), ("reshape_and_cache", evs)):
+        if e is not None:
+            stage_us[name] = float(np.mean([e.elapsed_ms(i) for i in range(K)])) * 1e3
+            e.close()
     ev.close()
     evp.close()
     dec_ms = float(np.mean(dec_t))
@@ -537,6 +555,16 @@ def main():
             "algorithmic_bytes_per_launch": int(u_bytes),
         },
     }
+    # the copy and scatter stages: HBM-bound bit copies, algorithmic bytes per call / mean event time
+    stage_bytes = {"copy_blocks": copy_bytes(w, esize), "reshape_and_cache": scatter_bytes(w, esize)}
+    if stage_us:
+        out["stages"] = {}
+        for name, us in stage_us.items():
+            gbs = stage_bytes[name] / (us * 1e-6) / 1e9
+            out["stages"][name] = {
+                "us_per_call": round(us, 2), "algorithmic_bytes": int(stage_bytes[name]),
+                "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
     if graph_ms is not None:
         out["graph"] = {
             "ms_per_step": round(graph_ms, 5),

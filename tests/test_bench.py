@@ -32,6 +32,7 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("workload,cpu", [("tiny_decode", True), ("chunked_prefill_mixed", True),
+                                          ("prefix_sharing_2040", False),
                                           ("llama2_7b_decode", False)])
 def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys):
     args = ["--workload", workload, "--steps", "3", "--warmup", "1", "--cpu-seconds", "2"]
@@ -65,6 +66,14 @@ def test_bench_prints_one_complete_json_line(workload, cpu, monkeypatch, capsys)
         assert c["single_thread"]["value"] > 0
     else:
         assert "cpu_baseline" not in d
+    st = d.get("stages", {})
+    assert ("reshape_and_cache" in st) == (d["config"]["scatter_tokens"] > 0)
+    assert ("copy_blocks" in st) == (d["config"]["copy_pairs"] > 0)
+    for name, x in st.items():
+        assert x["us_per_call"] > 0 and x["algorithmic_bytes"] > 0 and x["unit"] == "GB/s"
+        assert abs(x["achieved"] - x["algorithmic_bytes"] / x["us_per_call"] / 1e3) \
+            <= 1e-2 * x["achieved"] + 0.01
+        assert abs(x["frac"] - x["achieved"] / 8000.0) < 1e-3
     if d["config"]["prefill_rows"]:
         assert d["step_tokens"] == 2048            # the mixed step's token budget
         assert d["prefill_ms"] > 0 and 0 < d["prefill_mfma_frac"] < 1
