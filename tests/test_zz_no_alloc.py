@@ -1,7 +1,7 @@
 """pa_decode_noalloc (no workspace, partial results in the library's static scratch) against
-pa_decode with a caller's workspace, through the C ABI: two calls in a row on one GPU, the second
-with a smaller input (so the scratch still holds the first call's partials beyond what the second
-writes). The two entry points run the same kernels on the same layout: outputs are compared bit
+pa_decode with a caller's workspace, through the C ABI: calls in a row on one GPU, the later ones
+with smaller inputs than the first (so the scratch still holds the first call's partials beyond
+what they write). The two entry points run the same kernels on the same layout: outputs are compared bit
 for bit, and both against the float64 oracle."""
 import numpy as np
 import pytest
@@ -32,7 +32,10 @@ def test_noalloc_decode_equals_decode_on_two_calls():
     calls = [
         # 70B-like head groups (MFMA kernel, four parts per scratch slot): 2.2 MB of partials
         W.build([3000, 17, 2500, 900, 1999, 4000, 1, 2048], 32, 4, 128, "bf16", seed=901),
-        # then a smaller input on the vector-ALU kernel (one part per slot): 0.4 MB of partials
+        # then smaller inputs: head groups of 32 (two MFMA column groups per wave, four parts per
+        # slot): 0.27 MB of partials
+        W.build([2000, 37, 1500, 800], 64, 2, 128, "bf16", seed=904),
+        # the vector-ALU kernel (one part per slot): 0.4 MB of partials
         W.build([600, 1100, 5, 700], 16, 16, 64, "f16", seed=902),
     ]
     for i, w in enumerate(calls):
