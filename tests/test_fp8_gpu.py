@@ -178,7 +178,7 @@ FP8_SHARED_GROUPS = [
 
 @pytest.mark.parametrize("H_q,H_kv,D,dtype", [(4, 4, 128, "f16"), (8, 2, 128, "bf16"),
                                               (16, 4, 64, "f16"), (6, 2, 128, "bf16"),
-                                              (2, 2, 64, "bf16")])
+                                              (2, 2, 64, "bf16"), (64, 2, 128, "bf16")])
 @pytest.mark.parametrize("part,ks,vs", [(16, 0.05, 0.015), (512, 2.0 ** -5, 0.3)])
 def test_shared_prefix_decode_groups(H_q, H_kv, D, dtype, part, ks, vs):
     w = W.build_shared_groups(FP8_SHARED_GROUPS, H_q, H_kv, D, dtype, seed=640 + H_q + D,

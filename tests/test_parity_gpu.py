@@ -317,7 +317,7 @@ SHARED_GROUPS = [
 
 @pytest.mark.parametrize("H_q,H_kv,D,dtype", [(4, 4, 128, "f16"), (8, 2, 128, "bf16"),
                                               (16, 4, 64, "f16"), (6, 2, 128, "bf16"),
-                                              (2, 2, 64, "bf16")])
+                                              (2, 2, 64, "bf16"), (64, 2, 128, "bf16")])
 @pytest.mark.parametrize("part", [16, 512])
 def test_shared_prefix_decode_groups(H_q, H_kv, D, dtype, part):
     w = poisoned(W.build_shared_groups(SHARED_GROUPS, H_q, H_kv, D, dtype, seed=130 + H_q + D,
