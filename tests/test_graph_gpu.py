@@ -10,7 +10,8 @@ replay and an eager step leave the same cache words and outputs.
   * A replay after new queries and new K/V rows were written in place, against an eager step on
     those inputs.
 The steps: the tiny decode, 16-bit and E4M3 mixed steps, a shared-prefix step with copy-on-write
-pairs, and drafted rows (pa_decode_multi) beside one-token decodes over E4M3 caches.
+pairs, a decode of head groups of 32, and drafted rows (pa_decode_multi) beside one-token decodes
+over E4M3 caches.
 A step with copy-on-write pairs is not idempotent on the cache words (a shared block's holder
 writes its new rows into the block the copies are taken from), hence the restored caches. The
 eager step itself is checked against the float64 oracle by the parity tests; these tests pin the
@@ -43,6 +44,9 @@ CASES = {
     "shared_prefix_f16": (lambda: W.build_shared_groups(SHARED_GROUPS, 4, 4, 128, "f16",
                                                         seed=712),
                           {"shared_prefix": True, "partition_size": 256}),
+    # head groups of 32 (MQA-like): the decode runs the two-column-group units
+    "groups_of_32": (lambda: W.build([3000, 700, 1500, 20, 4100], 64, 2, 128, "bf16", seed=715),
+                     {}),
     # drafted rows (pa_decode_multi) beside one-token decodes, E4M3 caches
     "drafts_e4m3": (lambda: W.build([700, 2500, 1300, 4100, 30], 16, 4, 128, "bf16", seed=714,
                                     n_decode=2, q_lens=[4, 7, 1]),
