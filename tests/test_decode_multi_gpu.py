@@ -170,3 +170,34 @@ def test_rows_that_see_no_position_are_zero(part):
     assert not np.any(ref[empty]), "the oracle's empty rows are zeros"
     assert not np.any(got.reshape(ref.shape)[empty]), "empty rows must be written as zeros"
     assert_attention_close(got, ref, "bf16", f"multi-token rows with empty views, part={part}")
+
+
+# ------------------------------------------------------------- the speculative benchmark workloads
+@pytest.mark.parametrize("name,kv", [("llama2_7b_spec4", "auto"), ("llama70b_gqa_spec4", "auto"),
+                                     ("llama70b_gqa_spec4", "fp8")])
+def test_speculative_workload_full(name, kv):
+    """The benchmark's speculative steps at full size, in the launch configuration bench.py times
+    (GpuStep picks pa_decode_multi and its partition itself): every drafted row, every head,
+    against the oracle's prefill rows on the pool after the step's scatter."""
+    w = W.named(name)
+    print(f"[multi] {name} {kv}: {len(w.seq_lens)} sequences, {int(w.cu_q_lens[-1])} rows",
+          flush=True)
+    if kv == "fp8":
+        ks, vs = 0.03, 0.02
+        kc, vc = oracle_fp8_pool(w, ks, vs, poison=False)
+        g = GpuStep(w, kv_cache="fp8", k_scale=ks, v_scale=vs, fp8_pool=(kc, vc))
+    else:
+        g = GpuStep(w)
+    assert g.multi_token and g.n_decode == 0
+    g.run()
+    torch.cuda.synchronize()
+    got = words_from_device(g.pre_out)
+    if kv == "fp8":
+        kc, vc = oracle_fp8_after_step(w, kc, vc, ks, vs)
+        ref = oracle.prefill_fp8(w.query_prefill, kc, vc, w.block_tables, w.seq_lens, w.cu_q_lens,
+                                 w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale, ks, vs)
+    else:
+        kc, vc = oracle_pool_after_step(w)
+        ref = oracle.prefill(w.query_prefill, kc, vc, w.block_tables, w.seq_lens, w.cu_q_lens,
+                             w.H_q, w.H_kv, w.D, w.num_blocks, w.dtype, w.scale)
+    assert_attention_close(got, ref, w.dtype, f"speculative step {name} {kv}", absolute=True)
