@@ -173,8 +173,8 @@ def test_rows_that_see_no_position_are_zero(part):
 
 
 # ------------------------------------------------------------- the speculative benchmark workloads
-@pytest.mark.parametrize("name,kv", [("llama2_7b_spec4", "auto"), ("llama70b_gqa_spec4", "auto"),
-                                     ("llama70b_gqa_spec4", "fp8")])
+@pytest.mark.parametrize("name,kv", [("llama2_7b_spec4", "auto"), ("llama2_7b_spec4", "fp8"),
+                                     ("llama70b_gqa_spec4", "auto"), ("llama70b_gqa_spec4", "fp8")])
 def test_speculative_workload_full(name, kv):
     """The benchmark's speculative steps at full size, in the launch configuration bench.py times
     (GpuStep picks pa_decode_multi and its partition itself): every drafted row, every head,
