@@ -10,7 +10,8 @@
 //
 // Tiling. A workgroup of 8 waves owns 256 (query row, query head) pairs of one kv-head group: the
 // GK heads that share the kv head, for 256/GK consecutive rows, so each K/V tile staged in LDS serves
-// every head of the group. Per 64-key tile (4 paged blocks):
+// every head of the group. (Short causal contexts use 4 waves and 128 pairs, so that two workgroups
+// share a CU; the arithmetic of every pair is the same.) Per 64-key tile (4 paged blocks):
 //   - 16-bit K and V rows go to LDS untouched, straight from HBM (global_load_lds_dwordx4: no
 //     staging registers), into buffers that are filled while others are computed. Rows are stored
 //     without padding; the 16-byte pieces of row r are XOR-swizzled (piece c at c ^ swz(r)) so that
@@ -87,9 +88,10 @@ struct PrefillParams {
     int32_t identity_blocks;  // block i of sequence s is block s * max_blocks + i (a widened copy)
 };
 
-constexpr int kWaves = 8;                // waves per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr int kPairs = kWaves * 32;      // (row, head) pairs per workgroup
+// Causal chunks whose block tables span at most this many tokens run four-wave workgroups (the
+// 16-bit and widened instances): measured on whole fresh prompts, 32 query / 8 kv heads of 128,
+// 3-12 % faster up to 1024 tokens, even at 2048, and 2-5 % slower at 4096.
+constexpr int kFourWaveKeys = 2048;
 constexpr int kKeys = 64;  // keys per tile
 // A workgroup whose first row attends at least this many keys rounds P to the 16-bit type in one
 // part: a bfloat16 probability keeps 8 significant bits, and over L keys of comparable weight the
@@ -119,10 +121,17 @@ __device__ __forceinline__ int swz(int r)
         return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <bool BF, int D, int GK, bool TREE, bool F8>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
+// W waves per workgroup: 8 (one workgroup per CU, 128 KiB of LDS: K and V four tiles each), or 4
+// for short causal work (64 KiB: two tiles each), so that two workgroups share a CU and one's set-up
+// and drain overlap the other's tile loop. Both compute every (row, head) pair the same way.
+template <bool BF, int D, int GK, bool TREE, bool F8, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void prefill_kernel(PrefillParams p)
 {
-    constexpr int R = kPairs / GK;                  // query rows per workgroup
+    static_assert(W == 8 || (W == 4 && !F8), "E4M3 staging needs eight waves");
+    constexpr int kWavesW = W;
+    constexpr int kThreadsW = W * 64;
+    constexpr int KS = W == 8 ? 4 : 2;              // LDS tile slots per cache
+    constexpr int R = kWavesW * 32 / GK;            // query rows per workgroup
     constexpr int DC = D / 16;                      // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;                      // 32-dim tiles of O^T
     constexpr int ROWB = D * 2;                     // bytes per LDS row (no padding)
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     // bytes [(j % 4) * TILEB, +TILEB), of the V cache from (4 + j % 4) * TILEB on. The direct-to-LDS loads are
     // issued so that the compiler does not track them (dma16_to_lds): reads of the tiles being
     // computed run while later tiles are in flight, and every wait for a load is explicit below.
-    __shared__ __align__(1024) uint8_t lds[8 * TILEB];
+    __shared__ __align__(1024) uint8_t lds[2 * KS * TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const size_t blk_stride = (size_t)p.num_kv_heads * kBlock * D;
 
     // LDS starts zeroed: slots of keys that are never loaded then hold finite values
-    for (int i = tid; i < 8 * TILEB / 16; i += kThreads)
+    for (int i = tid; i < 2 * KS * TILEB / 16; i += kThreadsW)
         ((uint4 *)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     const size_t kvh_bytes = (size_t)kvh * kBlock * D * 2;
     auto issue_span = [&](auto span, const uint16_t *cache, uint8_t *buf, int t) PA_INLINE -> int {
         constexpr int KEYS = kKeys * decltype(span)::value, NBLK = KEYS / kBlock;
-        static_assert(NBLK <= kWaves, "one block per wave");
+        static_assert(NBLK <= kWavesW, "one block per wave");
         const int key0 = t * KEYS + wave * kBlock;  // first key of this wave's block
         if (wave >= NBLK || key0 >= L)
             return 0;
@@ -343,8 +352,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         // 2u-1, read by PV in steps 2u-1 and 2u, before that barrier). Spreading the two pairs
         // over both steps keeps the load issue off one step; the K pair has two steps to land,
         // the V pair one (both are waited for at step 2u+3, which first reads them).
-        auto kslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (j & 3) * TILEB; };
-        auto vslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (4 + (j & 3)) * TILEB; };
+        auto kslot = [&](int j) PA_INLINE -> uint8_t * { return lds + (j & (KS - 1)) * TILEB; };
+        auto vslot = [&](int j) PA_INLINE -> uint8_t * {
+            return lds + (KS + (j & (KS - 1))) * TILEB;
+        };
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
         // wait until at most n of this wave's loads are in flight (and LDS/scalar reads are done)
@@ -539,6 +550,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                 put_codes(kslot(1), c);
             stage(0);
             __syncthreads();
+        } else if constexpr (W == 4) {
+            // K tiles 0 and 1; V tile t is issued at step t
+            (void)issue_span(One{}, p.k_cache, kslot(0), 0);
+            if (n_tiles > 1)
+                (void)issue_span(One{}, p.k_cache, kslot(1), 1);
+            wait_loads(0);
+            __syncthreads();
         } else {
             (void)issue_span(Two{}, p.k_cache, kslot(0), 0);
             const int c1 = n_tiles > 2 ? issue_span(Two{}, p.k_cache, kslot(2), 1) : 0;
@@ -554,7 +572,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
         // interleave the MFMAs of pv and qk with the vector work of the softmax.
         auto iter = [&](auto par, auto masked, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2],
                         const uint4 (&p_in)[4], uint4 (&p_out)[4]) PA_INLINE {
-            if constexpr (decltype(par)::value == 1) {
+            if constexpr (W == 4) {
+                // two slots per cache, one step of lead: the loads of step t-1 (K tile t+1, V
+                // tile t-1) land; every wave is done with step t-1, which last read the slots
+                // of K tile t and V tile t-2
+                wait_loads(0);
+                __syncthreads();
+                if (t + 2 < n_tiles)
+                    (void)issue_span(One{}, p.k_cache, kslot(t + 2), t + 2);
+                (void)issue_span(One{}, p.v_cache, vslot(t), t);
+            } else if constexpr (decltype(par)::value == 1) {
                 const int u = t >> 1;  // t = 2u + 1
                 if constexpr (F8) {
                     write_staged();    // K tiles 2u+2, 2u+3 and V tiles 2u, 2u+1
@@ -580,8 +607,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
             }
             // K tile t+1 (past the last tile: stale, finite) and V tile t-1 (before the first:
             // slot 3, still zero)
-            const uint32_t kb = lds0 + ((t + 1) & 3) * TILEB + k_lane;
-            const uint32_t vb = lds0 + (4 + ((t - 1) & 3)) * TILEB + v_lane;
+            const uint32_t kb = lds0 + ((t + 1) & (KS - 1)) * TILEB + k_lane;
+            const uint32_t vb = lds0 + (KS + ((t - 1) & (KS - 1))) * TILEB + v_lane;
             const float alpha = region(masked, t, s_in, s_out, p_in, p_out, kb, vb);
             rescale = !__all(alpha == 1.0f);
             alpha_prev = alpha;
@@ -628,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                 for (int v = 0; v < 16; ++v)
                     o[dt][v] *= alpha_prev;
         }
-        const uint32_t v_last = lds0 + (4 + ((n_tiles - 1) & 3)) * TILEB + v_lane;
+        const uint32_t v_last = lds0 + (KS + ((n_tiles - 1) & (KS - 1))) * TILEB + v_lane;
         pv(std::integral_constant<int, 0>{}, pb, v_last);
         pv(std::integral_constant<int, 1>{}, pb, v_last);
         pv(std::integral_constant<int, 2>{}, pb, v_last);
@@ -638,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     // ---------------------------------------------------------------- plain loop (split P)
     auto issue = [&](int t, int b) PA_INLINE {
         (void)issue_span(One{}, p.k_cache, lds + b * TILEB, t);
-        (void)issue_span(One{}, p.v_cache, lds + (4 + b) * TILEB, t);
+        (void)issue_span(One{}, p.v_cache, lds + (KS + b) * TILEB, t);
     };
     // E4M3 staging of the plain loop: this thread's K and V codes of the next tile
     uint4 k8 = make_uint4(0, 0, 0, 0), v8 = k8;
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
     auto store8 = [&](int b) PA_INLINE {
         if (have8) {
             put_codes(lds + b * TILEB, k8);
-            put_codes(lds + (4 + b) * TILEB, v8);
+            put_codes(lds + (KS + b) * TILEB, v8);
         }
     };
     // bfloat16 P in hi + lo parts: this loop runs only while some row of the group sees fewer
@@ -677,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p)
                 issue(t + 1, (t + 1) & 1);  // lands in the other buffer while tile t is computed
         }
         const uint8_t *kb = lds + (t & 1) * TILEB;
-        const uint8_t *vb = lds + (4 + (t & 1)) * TILEB;
+        const uint8_t *vb = lds + (KS + (t & 1)) * TILEB;
         // the two 32-key halves are independent accumulator chains: interleave them so that no
         // MFMA waits on the one issued just before it
         f32x16 s[2];
@@ -846,28 +873,32 @@ __global__ __launch_bounds__(kWidenThreads) void widen_e4m3_kernel(WidenParams w
 }
 
 template <bool BF, int D, int GK>
-hipError_t launch_typed(const PrefillParams &p, bool fp8, hipStream_t stream)
+hipError_t launch_typed(const PrefillParams &p, bool fp8, bool four, hipStream_t stream)
 {
+    const dim3 grid(round_up8(p.n_items));
     if (fp8)
-        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, true>), dim3(round_up8(p.n_items)),
-                           dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, true, 8>), grid, dim3(8 * 64), 0,
+                           stream, p);
     else if (p.tree_mask)
-        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, true, false>), dim3(round_up8(p.n_items)),
-                           dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, true, false, 8>), grid, dim3(8 * 64), 0,
+                           stream, p);
+    else if (four)
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, false, 4>), grid, dim3(4 * 64), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, false>), dim3(round_up8(p.n_items)),
-                           dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<BF, D, GK, false, false, 8>), grid, dim3(8 * 64), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
 template <bool BF, int D>
-hipError_t launch_gk(int gk, const PrefillParams &p, bool fp8, hipStream_t stream)
+hipError_t launch_gk(int gk, const PrefillParams &p, bool fp8, bool four, hipStream_t stream)
 {
     switch (gk) {
-    case 8: return launch_typed<BF, D, 8>(p, fp8, stream);
-    case 4: return launch_typed<BF, D, 4>(p, fp8, stream);
-    case 2: return launch_typed<BF, D, 2>(p, fp8, stream);
-    default: return launch_typed<BF, D, 1>(p, fp8, stream);
+    case 8: return launch_typed<BF, D, 8>(p, fp8, four, stream);
+    case 4: return launch_typed<BF, D, 4>(p, fp8, four, stream);
+    case 2: return launch_typed<BF, D, 2>(p, fp8, four, stream);
+    default: return launch_typed<BF, D, 1>(p, fp8, four, stream);
     }
 }
 
@@ -895,12 +926,6 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
     p.num_blocks = d.c.num_blocks;
     p.n_sub = group / gk;
     p.total_q = d.total_q;
-    const int rows_per_wg = kPairs / gk;
-    p.row_tiles = (d.max_q_len + rows_per_wg - 1) / rows_per_wg;
-    const int64_t items = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.row_tiles;
-    if (items > 0x7ffffff0)
-        return hipErrorInvalidValue;
-    p.n_items = (int32_t)items;
     bool fp8 = d.c.fp8;
     if (fp8 && d.tree_mask)
         return hipErrorInvalidValue;  // no tree mask over E4M3 caches
@@ -940,11 +965,20 @@ hipError_t launch_prefill(const PrefillLaunch &d, hipStream_t stream)
         p.identity_blocks = 1;
         fp8 = false;  // the 16-bit kernel, with k_scale in scale_log2 and v_scale on the output
     }
+    // short contexts (every sequence's table, so its context, at most kFourWaveKeys tokens): four-
+    // wave workgroups, two per CU
+    const bool four = !fp8 && !d.tree_mask && (int64_t)kBlock * d.max_blocks <= kFourWaveKeys;
+    const int rows_per_wg = (four ? 4 : 8) * 32 / gk;
+    p.row_tiles = (d.max_q_len + rows_per_wg - 1) / rows_per_wg;
+    const int64_t items = (int64_t)d.num_seqs * d.c.num_kv_heads * p.n_sub * p.row_tiles;
+    if (items > 0x7ffffff0)
+        return hipErrorInvalidValue;
+    p.n_items = (int32_t)items;
     if (d.c.bf16)
-        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, fp8, stream)
-                                  : launch_gk<true, 128>(gk, p, fp8, stream);
-    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, fp8, stream)
-                              : launch_gk<false, 128>(gk, p, fp8, stream);
+        return d.c.head_dim == 64 ? launch_gk<true, 64>(gk, p, fp8, four, stream)
+                                  : launch_gk<true, 128>(gk, p, fp8, four, stream);
+    return d.c.head_dim == 64 ? launch_gk<false, 64>(gk, p, fp8, four, stream)
+                              : launch_gk<false, 128>(gk, p, fp8, four, stream);
 }
 
 }  // namespace pa

@@ -208,6 +208,26 @@ def test_prefill_chunks_full(H_q, H_kv, D, dtype):
                            f"prefill H_q={H_q} H_kv={H_kv} D={D} {dtype}")
 
 
+def test_prefill_four_and_eight_wave_workgroups_agree():
+    """Chunks whose block tables span at most 2048 tokens run four-wave workgroups (two per CU),
+    wider tables eight-wave ones. The same chunk with its tables padded to 200 blocks takes the
+    eight-wave kernel: both give the same bits (every pair's arithmetic is the same) and meet the
+    oracle."""
+    lens, q_lens = [700, 1500, 33, 2000, 1024], [700, 300, 33, 64, 1]
+    for dtype in ("f16", "bf16"):
+        outs = []
+        for mb in (None, 200):
+            w = W.build(lens, 32, 8, 128, dtype, seed=777, n_decode=0, q_lens=q_lens,
+                        max_blocks=mb)
+            assert w.block_tables.shape[1] == (125 if mb is None else 200)
+            g = run_on_gpu(w, stages=("scatter", "prefill"))
+            outs.append(words_from_device(g.pre_out))
+        assert np.array_equal(outs[0], outs[1]), f"{dtype}: four- and eight-wave bits differ"
+        kc, vc = oracle_pool_after_step(w)
+        assert_attention_close(outs[0], oracle_prefill(w, kc, vc), dtype,
+                               f"prefill, four- and eight-wave workgroups, {dtype}")
+
+
 def test_prefill_long_chunk_gqa_full():
     """A 700-row chunk of a 2500-token sequence plus a whole 333-token prompt, 32 q / 8 kv heads:
     every row. The prompt's first rows see a handful of keys (outputs near 1), where a bf16
