@@ -31,8 +31,9 @@ Prints ONE JSON line:
                far larger than the 256 MB Infinity Cache, so each step reads them from HBM;
                --evict-mb 512 also displaces every cache level before each timed decode, to show
                that.
-  stages       copy_blocks and reshape_and_cache (where the step has them): mean event time per
-               call, algorithmic bytes (below) and their rate against the 8 TB/s HBM peak;
+  stages       copy_blocks and reshape_and_cache (where the step has them), each timed alone after
+               the steps: mean event time per call, algorithmic bytes (below) and their rate
+               against the 8 TB/s HBM peak;
   graph        (--graph) the same step recorded once as a HIP graph and replayed: time per step
                and the rates above over it, for steps whose kernels are short enough that host
                launches show.
@@ -434,9 +435,6 @@ def main():
     ev = TimingEvents(K)   # decode call of each step
     evp = TimingEvents(K)  # prefill call of each step
     has_prefill = g.pre_query.shape[0] > 0
-    has_copy, has_scatter = len(w.copy_pairs) > 0, len(w.slot_mapping) > 0
-    evc = TimingEvents(K) if has_copy else None     # copy_blocks call of each step
-    evs = TimingEvents(K) if has_scatter else None  # reshape_and_cache call of each step
     # eviction by reading: a write would leave dirty lines whose write-back competes with the
     # decode's reads
     evict = (torch.zeros(args.evict_mb << 18, dtype=torch.int32, device="cuda")
@@ -444,16 +442,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if evc is not None:
-            evc.record(i, False, stream)
         g.copy()
-        if evc is not None:
-            evc.record(i, True, stream)
-        if evs is not None:
-            evs.record(i, False, stream)
         g.scatter()
-        if evs is not None:
-            evs.record(i, True, stream)
         if evict is not None:
             torch.amax(evict)
         ev.record(i, False, stream)
@@ -468,13 +458,24 @@ def main():
     ms_per_step = wall * 1e3 / K
     dec_t = [ev.elapsed_ms(i) for i in range(K)] if g.n_decode else [0.0]
     pre_t = [evp.elapsed_ms(i) for i in range(K)] if has_prefill else [0.0]
-    stage_us = {}
-    for name, e in (("copy_blocks", evc), ("reshape_and_cache", evs)):
-        if e is not None:
-            stage_us[name] = float(np.mean([e.elapsed_ms(i) for i in range(K)])) * 1e3
-            e.close()
     ev.close()
     evp.close()
+
+    # the copy and scatter stages, each timed alone after the steps (K calls back to back, events
+    # around each): markers around them inside the timed steps stalled some steps' launches by
+    # hundreds of microseconds. Repeating a step's copies and slot writes leaves the pool as it is.
+    stage_us = {}
+    for name, fn, present in (("copy_blocks", g.copy, len(w.copy_pairs) > 0),
+                              ("reshape_and_cache", g.scatter, len(w.slot_mapping) > 0)):
+        if present:
+            e = TimingEvents(K)
+            for i in range(K):
+                e.record(i, False, stream)
+                fn()
+                e.record(i, True, stream)
+            torch.cuda.synchronize()
+            stage_us[name] = float(np.mean([e.elapsed_ms(i) for i in range(K)])) * 1e3
+            e.close()
     dec_ms = float(np.mean(dec_t))
     pre_ms = float(np.mean(pre_t))
 
