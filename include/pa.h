@@ -340,8 +340,9 @@ pa_status_t pa_decode_shared_prefix_fp8(pa_dtype_t dtype, int32_t num_blocks,
  * Each kv head's context is read once per 32 (row, query head) pairs, on MFMA, split into parts of
  * partition_size tokens merged by rescaling with their maxima and sums of exponentials, as in
  * pa_decode ([OV] §9 (4)). The chunk kernel of pa_prefill_chunk instead reads it once per
- * workgroup of 256 pairs, which few rows leave mostly empty: this call is the faster one up to
- * 32 pairs per kv head (max_q_len * num_q_heads / num_kv_heads), the two are even at 64.
+ * workgroup of 256 pairs (128 where the block tables span at most 2048 tokens), which few rows
+ * leave mostly empty: this call is the faster one up to 32 pairs per kv head (max_q_len *
+ * num_q_heads / num_kv_heads), the two are even at 64.
  *   query, out    [total_q][num_q_heads][head_dim] of `dtype` (F16 or BF16); out must not alias
  *                 an input.
  *   cu_q_lens     [num_seqs + 1] int32, cu_q_lens[0] = 0, non-decreasing, cu_q_lens[num_seqs] =
