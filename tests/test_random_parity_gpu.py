@@ -1,7 +1,7 @@
 """Random shapes against the oracle: decode and chunked prefill, 16-bit and E4M3 caches.
 
-Each case draws from its own seeded generator: a head group (MHA, GQA of 2 to 8, and groups that
-are not powers of two), head_dim 64 or 128, fp16 or bf16, 1-11 decode sequences of 1-3000 tokens,
+Each case draws from its own seeded generator: a head group (MHA, GQA of 2 to 8, groups that are
+not powers of two, and in their own cases groups of 17-64 query heads per kv head), head_dim 64 or 128, fp16 or bf16, 1-11 decode sequences of 1-3000 tokens,
 often 1-3 prefill chunks of 1-299 rows over 0-1499 cached tokens, a partition size (library
 default, unsplit, 16, 256, 512 or 1024), and E4M3 scales. The whole step runs on the GPU (copy,
 scatter, decode, prefill) and every output row is compared with the float64 oracle on the pool after
@@ -21,12 +21,15 @@ pytestmark = pytest.mark.gpu
 
 GROUPS = [(4, 4), (8, 8), (16, 8), (32, 8), (12, 4), (6, 2), (24, 8), (10, 2), (64, 8), (20, 4),
           (2, 2), (8, 2)]
+# head groups above 16 (MQA-like): decodes run the two-column-group units
+LARGE_GROUPS = [(64, 2), (40, 2), (48, 1), (34, 2), (128, 4), (96, 2), (32, 1), (17, 1)]
 PARTS = [None, 0, 16, 256, 512, 1024]
 
 
-def draw_case(case, max_len=3000, short=False):
-    rng = np.random.default_rng((9300 if short else 9100) + case)
-    H_q, H_kv = GROUPS[rng.integers(len(GROUPS))]
+def draw_case(case, max_len=3000, short=False, large=False):
+    rng = np.random.default_rng((9300 if short else 9100) + (400 if large else 0) + case)
+    groups = LARGE_GROUPS if large else GROUPS
+    H_q, H_kv = groups[rng.integers(len(groups))]
     D = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
     n_dec = int(rng.integers(1, 12))
@@ -59,10 +62,16 @@ def test_random_short_chunk_step_matches_oracle(case):
     check_case(case, short=True)
 
 
-def check_case(case, max_len=3000, short=False):
+@pytest.mark.parametrize("case", range(8))
+def test_random_large_group_step_matches_oracle(case):
+    """Head groups above 16 (17-64 query heads per kv head), regular and short-chunk steps."""
+    check_case(case, short=case >= 6, large=True)
+
+
+def check_case(case, max_len=3000, short=False, large=False):
     """One seeded random step on the GPU, 16-bit and E4M3 caches, against the oracle. short: the
-    chunks are drafted rows, forced through pa_decode_multi."""
-    w, (ks, vs) = draw_case(case, max_len, short)
+    chunks are drafted rows, forced through pa_decode_multi; large: head groups above 16."""
+    w, (ks, vs) = draw_case(case, max_len, short, large)
     nd = w.n_decode
     tag = (f"case {case}: H_q={w.H_q} H_kv={w.H_kv} D={w.D} {w.dtype} decodes={nd} "
            f"chunks={np.diff(w.cu_q_lens).tolist() if len(w.cu_q_lens) else []} "
