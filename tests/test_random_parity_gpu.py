@@ -1,9 +1,10 @@
 """Random shapes against the oracle: decode and chunked prefill, 16-bit and E4M3 caches.
 
 Each case draws from its own seeded generator: a head group (MHA, GQA of 2 to 8, groups that are
-not powers of two, and in their own cases groups of 17-64 query heads per kv head), head_dim 64 or 128, fp16 or bf16, 1-11 decode sequences of 1-3000 tokens,
-often 1-3 prefill chunks of 1-299 rows over 0-1499 cached tokens, a partition size (library
-default, unsplit, 16, 256, 512 or 1024), and E4M3 scales. The whole step runs on the GPU (copy,
+not powers of two, and in their own cases groups of 17-64 query heads per kv head), head_dim 64
+or 128, fp16 or bf16, 1-11 decode sequences of 1-3000 tokens, often 1-3 prefill chunks of 1-299
+rows over 0-1499 cached tokens, a partition size (library default, unsplit, 16, 256, 512 or
+1024), and E4M3 scales. The whole step runs on the GPU (copy,
 scatter, decode, prefill) and every output row is compared with the float64 oracle on the pool after
 the step's scatter, within the attention gate of the output type (short contexts give outputs near
 1, where a bf16 output's own rounding is up to 2^-8 |ref|).
